@@ -1,0 +1,7 @@
+"""CPU oracle for the MLA latent-KV hot path.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the package smoke check and the
+benchmark's CPU-baseline leg, never by the product path.
+"""
+from .mla_oracle import *  # noqa: F401,F403
+from .mla_oracle import OracleError  # noqa: F401
