@@ -1,0 +1,230 @@
+/*
+ * mla.h - C ABI of libmla.so: the hot path of GLM-5.2-style multi-head latent
+ * attention (MLA) over a compressed KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * Definitions follow the three "mlx-bun" diff pages on my.diffend.io:
+ *   [P1] "mlx-bun 0.0.11 -> 0.0.13", package/src/model/glm52-mla.ts
+ *   [P2] "mlx-bun 0.2.0 -> 0.4.0", glm52-mla.ts (left-padding mask) and
+ *        glm52-cache.ts (right-aligned rows, per-row lengths, left pad)
+ *
+ * A decode step is the chain
+ *   mla_rope_partial_interleaved (q rope part)  ->  mla_absorb_q  ->
+ *   mla_decode_latent_attn  ->  mla_decode_combine  ->  mla_absorb_v
+ * and a prefill block is one call of mla_prefill_reconstructed.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers unless the comment says [host].
+ *   - Ownership: the caller owns every buffer.  The library never allocates,
+ *     frees or keeps a pointer beyond the work it enqueues on `stream`; the
+ *     caller keeps buffers alive until that work completes (the pages' rule
+ *     that returned arrays are caller-owned, [P1] Glm52Mla.project).
+ *   - No entry point synchronises the device or the stream.  Work is enqueued
+ *     on `stream` (NULL = the default stream) and runs in stream order.
+ *   - Element strides are in elements, not bytes; the innermost (feature)
+ *     stride is always 1.
+ *   - dtype: MLA_DTYPE_F32 or MLA_DTYPE_BF16 names the storage type of the
+ *     activations, cache and weights an entry reads.  Accumulation is always
+ *     fp32; q_lat, partials, o_lat, lse and ctx are always fp32.
+ *   - Errors: arguments are checked on the host before anything is enqueued,
+ *     as the pages throw synchronously.  A failed check returns a negative
+ *     mla_status and enqueues nothing; mla_last_error() then returns a
+ *     message (thread-local, valid until the next call on that thread).  A
+ *     launch failure returns MLA_ERR_DEVICE.  Entry points are re-entrant.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_DTYPE_F32 = 0,
+  MLA_DTYPE_BF16 = 1
+} mla_dtype;
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_ARG = -1,        /* null pointer, bad dtype, non-positive geometry */
+  MLA_ERR_SHAPE = -2,      /* shapes that do not fit one another */
+  MLA_ERR_ROPE = -3,       /* RoPE argument rules of [P1] partialInterleavedRopeMlx */
+  MLA_ERR_SELECTION = -4,  /* DSA selection counts */
+  MLA_ERR_WORKSPACE = -5,  /* workspace missing or too small */
+  MLA_ERR_DEVICE = -6,     /* a HIP call or kernel launch failed */
+  MLA_ERR_UNSUPPORTED = -7 /* valid by the pages, outside this library's limits */
+} mla_status;
+
+/* Message of the last failed call on this thread ("" after success). */
+const char* mla_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int mla_version(void);
+
+/*
+ * Partial interleaved RoPE.  [P1] partialInterleavedRopeMlx.
+ *
+ * x and y are logical [batch, tokens, inner, feat] arrays of `dtype` with the
+ * same element strides (stride_b, stride_t, stride_i, 1); y may equal x (in
+ * place), otherwise they must not overlap.  For each row vector v = x[b,t,i,:]
+ * the first rotary_dims features hold pairs (a_p, b_p) = (v[2p], v[2p+1]),
+ * p < rotary_dims/2, and
+ *     y[p]          = a_p cos(ang) - b_p sin(ang)
+ *     y[R/2 + p]    = b_p cos(ang) + a_p sin(ang)
+ *     y[R .. feat)  = v[R .. feat)            (non-rotary tail kept)
+ * with position = offsets[b or 0] + t, inverse frequency
+ * f32(pow(f32(theta), f32(-2p/R))) and ang = f32(position * inverse frequency),
+ * all as on the page.  cos/sin and the rotation are evaluated in double and
+ * rounded once to `dtype`.
+ *
+ * offsets [host] int64: n_offsets == 1 (one offset for every row) or
+ * n_offsets == batch (one per row).  Rules of the page, MLA_ERR_ROPE when
+ * broken: offsets >= 0; rotary_dims > 0, even, <= feat; theta finite and > 0.
+ * Limits (MLA_ERR_UNSUPPORTED): rotary_dims <= 512; offset + tokens <= 2^53.
+ * Any of batch, tokens, inner may be 0 (nothing is enqueued).
+ */
+int mla_rope_partial_interleaved(int32_t dtype, const void* x, void* y,
+                                 int32_t batch, int32_t tokens, int32_t inner, int32_t feat,
+                                 int64_t stride_b, int64_t stride_t, int64_t stride_i,
+                                 int32_t rotary_dims, double theta,
+                                 const int64_t* offsets, int32_t n_offsets,
+                                 hipStream_t stream);
+
+/*
+ * Absorb the no-PE query into latent space.  [P1] Glm52Mla.attendAbsorbed:
+ * the key block of head h is W_UK[h] = w_kv_b rows [h(dn+dv), h(dn+dv)+dn),
+ * a [dn, r] matrix, and the latent-space query is q_nope . W_UK.
+ *
+ *   q_lat[b,h,c] = sum_d q_nope[b,h,d] * w_kv_b[h*(dn+dv) + d, c]
+ *
+ * q_nope: [batch, heads, qk_nope] of `dtype`, strides (q_stride_b, q_stride_h, 1).
+ * w_kv_b: [heads*(qk_nope+v_head), kv_lora_rank] of `dtype`, row-major, contiguous.
+ * q_lat:  [batch, heads, kv_lora_rank] fp32, contiguous.
+ */
+int mla_absorb_q(int32_t dtype, const void* q_nope, int64_t q_stride_b, int64_t q_stride_h,
+                 const void* w_kv_b, float* q_lat,
+                 int32_t batch, int32_t heads, int32_t qk_nope, int32_t v_head, int32_t kv_lora_rank,
+                 hipStream_t stream);
+
+/*
+ * Latent decode attention, split-T partials.  [P1] Glm52Mla.attendAbsorbed
+ * (scores = scale*(q_lat.latent^T + q_rope.rope^T), softmax, P.latent) with
+ * the DSA gather of the same function and the ragged rows of Glm52Mla.forward;
+ * [P2] glm52-cache.ts for the right-aligned cache.
+ *
+ * Cache: row b holds kv_len[b] valid tokens right-aligned in `width` slots,
+ * i.e. token j (0 <= j < kv_len[b]) of the row's valid slice is slot
+ * width - kv_len[b] + j.  latent [batch, width, kv_lora_rank] and
+ * rope [batch, width, rope_dim] are `dtype` arrays with element strides
+ * (latent_stride_b, latent_stride_t, 1) and (rope_stride_b, rope_stride_t, 1);
+ * a packed [batch, width, r+dr] cache passes rope = latent + r and equal
+ * strides.  Pad slots are never read.
+ *
+ * Attended list A_b of row b: all valid tokens in order when sel_count is
+ * NULL or sel_count[b] == -1; otherwise sel_count[b] >= 1 indices
+ * into the valid slice, read from sel_idx starting at the sum of the positive
+ * sel_count entries of the rows before b (rows concatenated), attended in list
+ * order, duplicates once per occurrence.  An index outside [0, kv_len[b]) is
+ * skipped (it contributes nothing) and, when dev_err is not NULL, *dev_err is
+ * set to a non-zero value on the device.  sel_count[b] == 0 is
+ * MLA_ERR_SELECTION (the page rejects an empty selection).
+ *
+ * A_b is cut in list order into n_b = ceil(|A_b| / chunk_len) splits of
+ * chunk_len tokens (the last may be shorter).  For split s of row b and head h
+ *   score_j  = softmax_scale * (q_lat[b,h,:] . latent_j + q_rope[b,h,:] . rope_j)
+ *   m        = max_j score_j,   l = sum_j exp(score_j - m)
+ *   part_o[b,h,s,:] = sum_j exp(score_j - m) latent_j / l
+ *   part_lse[b,h,s] = m + ln l
+ * A split whose indices were all skipped stores o = 0 and lse = -inf.
+ * Slots s >= n_b are left untouched.
+ *
+ * q_lat [batch, heads, kv_lora_rank] fp32 contiguous; q_rope [batch, heads,
+ * rope_dim] of `dtype`, strides (qr_stride_b, qr_stride_h, 1), already rotated.
+ * kv_len [host] int32[batch], each in [1, width] (MLA_ERR_SHAPE otherwise).
+ * sel_count [host] int32[batch] or NULL.  sel_idx device int32 (may be NULL
+ * only if no row is selected).  part_o [batch, heads, s_max, r] and
+ * part_lse [batch, heads, s_max] fp32; s_max >= max_b n_b (MLA_ERR_SHAPE).
+ * Limits (MLA_ERR_UNSUPPORTED): kv_lora_rank <= 1024, rope_dim <= 256.
+ */
+int mla_decode_latent_attn(int32_t dtype, const float* q_lat,
+                           const void* q_rope, int64_t qr_stride_b, int64_t qr_stride_h,
+                           const void* latent, int64_t latent_stride_b, int64_t latent_stride_t,
+                           const void* rope, int64_t rope_stride_b, int64_t rope_stride_t,
+                           int32_t batch, int32_t heads, int32_t kv_lora_rank, int32_t rope_dim,
+                           int32_t width, const int32_t* kv_len,
+                           const int32_t* sel_idx, const int32_t* sel_count,
+                           float softmax_scale, int32_t chunk_len,
+                           float* part_o, float* part_lse, int32_t s_max,
+                           int32_t* dev_err, hipStream_t stream);
+
+/*
+ * Combine split partials (flash-decoding merge).  The exact log-sum-exp
+ * decomposition of the page's softmax ([P1] attendAbsorbed):
+ *   LSE = ln sum_{s<n_b} exp(part_lse[b,h,s])
+ *   o_lat[b,h,:] = sum_{s<n_b} exp(part_lse[b,h,s] - LSE) part_o[b,h,s,:]
+ * Splits with lse = -inf contribute nothing; if every split of (b,h) is
+ * empty, o_lat = 0 and lse = -inf.
+ * n_splits [host] int32[batch], each in [1, s_max].  lse may be NULL.
+ * Layouts as in mla_decode_latent_attn; o_lat [batch, heads, r], lse [batch, heads].
+ */
+int mla_decode_combine(const float* part_o, const float* part_lse,
+                       int32_t batch, int32_t heads, int32_t kv_lora_rank, int32_t s_max,
+                       const int32_t* n_splits, float* o_lat, float* lse, hipStream_t stream);
+
+/*
+ * Project the latent context out through the value block.  [P1]
+ * attendAbsorbed: W_UV[h] = w_kv_b rows [h(dn+dv)+dn, (h+1)(dn+dv)), a
+ * [dv, r] matrix; the head output is o_lat . W_UV^T and heads are
+ * concatenated into [batch, heads*dv].
+ *   ctx[b, h*dv + v] = sum_c o_lat[b,h,c] * w_kv_b[h*(dn+dv) + dn + v, c]
+ * o_lat fp32 [batch, heads, r] contiguous; w_kv_b as in mla_absorb_q;
+ * ctx fp32 [batch, heads*v_head] contiguous.
+ */
+int mla_absorb_v(int32_t dtype, const float* o_lat, const void* w_kv_b, float* ctx,
+                 int32_t batch, int32_t heads, int32_t qk_nope, int32_t v_head, int32_t kv_lora_rank,
+                 hipStream_t stream);
+
+/*
+ * Reconstructed causal prefill.  [P1] Glm52Mla.project (q_b_proj of the
+ * normalised q-LoRA state, reshape [B,T,H,dn+dr], split no-PE / rope, RoPE of
+ * the rope part at q_offsets[b] + t) and Glm52Mla.attendReconstructed
+ * (kv_b_proj expansion to per-head K_nope / V, rope key broadcast over heads,
+ * scores scaled by softmax_scale, causal mask, softmax, P.V); [P2] left pad.
+ *
+ *   q[b,t,h,:]  = q_c[b,t,:] . w_q_b[h*(dn+dr) + (0..dn+dr), :]^T
+ *   key k is visible to query t of row b  iff  left_pad[b] <= k <= (keys - tokens) + t
+ *   ctx[b,t,h*dv + v] = sum_k softmax_k(score) * V[b,k,h,v]
+ *
+ * q_c [batch, tokens, q_lora_rank], w_q_b [heads*(qk_nope+qk_rope), q_lora_rank],
+ * latent [batch, keys, kv_lora_rank], rope [batch, keys, qk_rope] (already
+ * rotated, e.g. by mla_rope_partial_interleaved), w_kv_b as above; all
+ * `dtype`, contiguous.  q_offsets [host] int64[batch] >= 0.  left_pad [host]
+ * int32[batch] in [0, keys] or NULL (no padding).  keys >= tokens.  A query
+ * that sees no key (inside the pad) gets ctx = 0.  ctx fp32 [batch, tokens,
+ * heads*v_head].
+ *
+ * Workspace: with workspace == NULL the call stores the bytes it needs in
+ * *workspace_bytes and returns MLA_OK without enqueuing anything.  Otherwise
+ * *workspace_bytes must be at least that size (MLA_ERR_WORKSPACE) and the
+ * device buffer must be 256-byte aligned; its contents are scratch.
+ * Limits (MLA_ERR_UNSUPPORTED): qk_nope + qk_rope <= 256, v_head <= 256,
+ * qk_rope <= 512.
+ */
+int mla_prefill_reconstructed(int32_t dtype, int32_t batch, int32_t tokens, int32_t keys, int32_t heads,
+                              int32_t q_lora_rank, int32_t kv_lora_rank,
+                              int32_t qk_nope, int32_t qk_rope, int32_t v_head,
+                              const void* q_c, const void* w_q_b,
+                              const void* latent, const void* rope, const void* w_kv_b,
+                              const int64_t* q_offsets, double theta, const int32_t* left_pad,
+                              float softmax_scale,
+                              void* workspace, size_t* workspace_bytes,
+                              float* ctx, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

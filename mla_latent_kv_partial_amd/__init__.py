@@ -1,0 +1,227 @@
+"""Python binding of libmla.so: MLA latent-KV decode and reconstructed prefill on MI355X.
+
+Each function marshals torch tensors (device memory) and the current HIP
+stream into the C entry point of the same name in include/mla.h; all
+arithmetic runs in the library's HIP kernels.  Outputs not passed in are
+allocated with torch on the inputs' device.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import numbers
+
+import torch
+
+from ._lib import (EXPORTS, LIB_PATH, MLA_DTYPE_BF16, MLA_DTYPE_F32, MlaError, check, i32_array, i64_array,
+                   lib)
+
+__all__ = [
+    "MlaError", "LIB_PATH", "EXPORTS", "mla_rope_partial_interleaved", "mla_absorb_q", "mla_decode_latent_attn",
+    "mla_decode_combine", "mla_absorb_v", "mla_prefill_reconstructed", "mla_version", "split_count",
+]
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MLA_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return MLA_DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16 expected")
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _host_list(x):
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        return [int(v) for v in x.detach().cpu().reshape(-1).tolist()]
+    if isinstance(x, (int,)):
+        return [int(x)]
+    return [int(v) for v in x]
+
+
+def _collapse(shape, strides, lo, hi):
+    """(size, stride) of axes [lo, hi) viewed as one axis, or None if not viewable."""
+    size, stride = 1, 0
+    dims = [(shape[i], strides[i]) for i in range(lo, hi) if shape[i] != 1]
+    if not dims:
+        return 1, 0
+    size, stride = dims[-1]
+    for n, s in reversed(dims[:-1]):
+        if s != stride * size:
+            return None
+        size *= n
+    return size, stride
+
+
+def mla_version() -> int:
+    return int(lib.mla_version())
+
+
+def split_count(n_attended: int, chunk_len: int) -> int:
+    return -(-int(n_attended) // int(chunk_len))
+
+
+def mla_rope_partial_interleaved(x: torch.Tensor, position_offset, rotary_dims: int, theta: float,
+                                 token_axis: int = 1, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Partial interleaved RoPE of `x` (rank >= 2, feature axis last); `out=x` rotates in place."""
+    if x.dim() < 2:
+        raise ValueError("partial interleaved RoPE requires rank >= 2")
+    rank = x.dim()
+    axis = token_axis + rank if token_axis < 0 else token_axis
+    if not 0 <= axis < rank - 1:
+        raise ValueError("RoPE token axis must lie before the feature axis")
+    if out is None:
+        out = torch.empty_like(x)
+    if out.shape != x.shape or out.stride() != x.stride() or out.dtype != x.dtype:
+        raise ValueError("out must match x in shape, strides and dtype")
+    if x.stride(-1) != 1:
+        raise ValueError("the feature axis must have stride 1")
+    offsets = _host_list(position_offset)
+    per_row = not isinstance(position_offset, numbers.Integral)
+    shape, strides = list(x.shape), list(x.stride())
+    lead = _collapse(shape, strides, 0, axis)
+    inner = _collapse(shape, strides, axis + 1, rank - 1)
+    if lead is None or inner is None:
+        raise ValueError("x cannot be viewed as [batch, tokens, inner, feat]; make it contiguous")
+    batch, sb = lead
+    if per_row:
+        if axis == 0:
+            raise ValueError("per-row RoPE offsets require a separate token axis")
+        if len(offsets) != shape[0]:
+            raise ValueError(f"RoPE row offsets {len(offsets)} != batch {shape[0]}")
+        rep = batch // shape[0] if shape[0] else 1
+        offsets = [o for o in offsets for _ in range(rep)]
+    tokens, st = shape[axis], strides[axis]
+    n_inner, si = inner
+    offs = i64_array(offsets)
+    check(lib.mla_rope_partial_interleaved(
+        _dtype_code(x), _ptr(x), _ptr(out), batch, tokens, n_inner, shape[-1], sb, st, si, int(rotary_dims),
+        float(theta), offs, len(offsets), _stream(x)), "mla_rope_partial_interleaved")
+    return out
+
+
+def mla_absorb_q(q_nope: torch.Tensor, w_kv_b: torch.Tensor, v_head: int,
+                 q_lat: torch.Tensor | None = None) -> torch.Tensor:
+    """q_nope [B,H,dn] (strided, last stride 1), w_kv_b [H*(dn+dv), r] -> q_lat fp32 [B,H,r]."""
+    b, h, dn = q_nope.shape
+    r = w_kv_b.shape[1]
+    if q_nope.dtype != w_kv_b.dtype:
+        raise TypeError("q_nope and w_kv_b must share a dtype")
+    if q_nope.stride(2) != 1 or not w_kv_b.is_contiguous():
+        raise ValueError("q_nope needs feature stride 1 and w_kv_b must be contiguous")
+    if q_lat is None:
+        q_lat = torch.empty((b, h, r), dtype=torch.float32, device=q_nope.device)
+    check(lib.mla_absorb_q(_dtype_code(q_nope), _ptr(q_nope), q_nope.stride(0), q_nope.stride(1), _ptr(w_kv_b),
+                           _ptr(q_lat), b, h, dn, int(v_head), r, _stream(q_nope)), "mla_absorb_q")
+    return q_lat
+
+
+def mla_decode_latent_attn(q_lat: torch.Tensor, q_rope: torch.Tensor, latent: torch.Tensor, rope: torch.Tensor,
+                           kv_len, softmax_scale: float, chunk_len: int, sel_idx: torch.Tensor | None = None,
+                           sel_count=None, part_o: torch.Tensor | None = None,
+                           part_lse: torch.Tensor | None = None, s_max: int | None = None,
+                           dev_err: torch.Tensor | None = None):
+    """Split-T latent attention partials.  Returns (part_o, part_lse, n_splits list).
+
+    latent [B,W,r] and rope [B,W,dr] (strided views of a cache; feature stride 1);
+    kv_len and sel_count are host sequences; sel_idx an int32 device tensor.
+    """
+    b, h, r = q_lat.shape
+    w = latent.shape[1]
+    dr = rope.shape[2]
+    lens = _host_list(kv_len)
+    counts = _host_list(sel_count)
+    n_att = [c if counts is not None and c > 0 else n for n, c in zip(lens, counts or [-1] * b)]
+    n_splits = [split_count(n, chunk_len) for n in n_att]
+    if s_max is None:
+        s_max = max(n_splits) if n_splits else 1
+    dev = q_lat.device
+    if part_o is None:
+        part_o = torch.empty((b, h, s_max, r), dtype=torch.float32, device=dev)
+    if part_lse is None:
+        part_lse = torch.empty((b, h, s_max), dtype=torch.float32, device=dev)
+    if sel_idx is not None and sel_idx.dtype != torch.int32:
+        raise TypeError("sel_idx must be int32")
+    if latent.stride(2) != 1 or rope.stride(2) != 1 or q_rope.stride(2) != 1:
+        raise ValueError("feature axes must have stride 1")
+    check(lib.mla_decode_latent_attn(
+        _dtype_code(latent), _ptr(q_lat), _ptr(q_rope), q_rope.stride(0), q_rope.stride(1),
+        _ptr(latent), latent.stride(0), latent.stride(1), _ptr(rope), rope.stride(0), rope.stride(1),
+        b, h, r, dr, w, i32_array(lens), _ptr(sel_idx), None if counts is None else i32_array(counts),
+        float(softmax_scale), int(chunk_len), _ptr(part_o), _ptr(part_lse), int(s_max), _ptr(dev_err),
+        _stream(q_lat)), "mla_decode_latent_attn")
+    return part_o, part_lse, n_splits
+
+
+def mla_decode_combine(part_o: torch.Tensor, part_lse: torch.Tensor, n_splits, o_lat: torch.Tensor | None = None,
+                       lse: torch.Tensor | None = None, want_lse: bool = True):
+    """Merge partials into o_lat [B,H,r] (and lse [B,H])."""
+    b, h, s_max, r = part_o.shape
+    if o_lat is None:
+        o_lat = torch.empty((b, h, r), dtype=torch.float32, device=part_o.device)
+    if lse is None and want_lse:
+        lse = torch.empty((b, h), dtype=torch.float32, device=part_o.device)
+    check(lib.mla_decode_combine(_ptr(part_o), _ptr(part_lse), b, h, r, s_max, i32_array(_host_list(n_splits)),
+                                 _ptr(o_lat), _ptr(lse), _stream(part_o)), "mla_decode_combine")
+    return o_lat, lse
+
+
+def mla_absorb_v(o_lat: torch.Tensor, w_kv_b: torch.Tensor, qk_nope: int, v_head: int,
+                 ctx: torch.Tensor | None = None) -> torch.Tensor:
+    """o_lat fp32 [B,H,r] -> ctx fp32 [B,H*dv]."""
+    b, h, r = o_lat.shape
+    if ctx is None:
+        ctx = torch.empty((b, h * v_head), dtype=torch.float32, device=o_lat.device)
+    if not (o_lat.is_contiguous() and w_kv_b.is_contiguous()):
+        raise ValueError("o_lat and w_kv_b must be contiguous")
+    check(lib.mla_absorb_v(_dtype_code(w_kv_b), _ptr(o_lat), _ptr(w_kv_b), _ptr(ctx), b, h, int(qk_nope),
+                           int(v_head), r, _stream(o_lat)), "mla_absorb_v")
+    return ctx
+
+
+def prefill_workspace_bytes(dtype: torch.dtype, batch, tokens, keys, heads, q_lora_rank, kv_lora_rank, qk_nope,
+                            qk_rope, v_head) -> int:
+    need = ctypes.c_size_t(0)
+    code = MLA_DTYPE_BF16 if dtype == torch.bfloat16 else MLA_DTYPE_F32
+    offs = i64_array([0] * max(1, batch))
+    check(lib.mla_prefill_reconstructed(code, batch, tokens, keys, heads, q_lora_rank, kv_lora_rank, qk_nope, qk_rope,
+                                        v_head, None, None, None, None, None, offs, 10000.0, None, 1.0, None,
+                                        ctypes.byref(need), None, None), "mla_prefill_reconstructed")
+    return int(need.value)
+
+
+def mla_prefill_reconstructed(q_c: torch.Tensor, w_q_b: torch.Tensor, latent: torch.Tensor, rope: torch.Tensor,
+                              w_kv_b: torch.Tensor, heads: int, qk_nope: int, qk_rope: int, v_head: int, q_offsets,
+                              theta: float, softmax_scale: float | None = None, left_pad=None,
+                              workspace: torch.Tensor | None = None, ctx: torch.Tensor | None = None) -> torch.Tensor:
+    """Causal prefill: q_c [B,T,ql], latent [B,K,r], rope [B,K,dr] (rotated) -> ctx fp32 [B,T,H*dv]."""
+    b, t, ql = q_c.shape
+    k, r = latent.shape[1], latent.shape[2]
+    for name, ten in (("q_c", q_c), ("w_q_b", w_q_b), ("latent", latent), ("rope", rope), ("w_kv_b", w_kv_b)):
+        if not ten.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(qk_nope + qk_rope)
+    need = prefill_workspace_bytes(q_c.dtype, b, t, k, heads, ql, r, qk_nope, qk_rope, v_head)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_c.device)
+    if ctx is None:
+        ctx = torch.empty((b, t, heads * v_head), dtype=torch.float32, device=q_c.device)
+    size = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+    pads = _host_list(left_pad)
+    check(lib.mla_prefill_reconstructed(
+        _dtype_code(q_c), b, t, k, heads, ql, r, int(qk_nope), int(qk_rope), int(v_head), _ptr(q_c), _ptr(w_q_b),
+        _ptr(latent), _ptr(rope), _ptr(w_kv_b), i64_array(_host_list(q_offsets)), float(theta),
+        None if pads is None else i32_array(pads), float(softmax_scale), _ptr(workspace), ctypes.byref(size),
+        _ptr(ctx), _stream(q_c)), "mla_prefill_reconstructed")
+    return ctx

@@ -1,0 +1,114 @@
+// Internal launch interface between the C ABI layer (mla_abi.cpp) and the
+// kernel translation units.  Arguments here are already validated; every
+// launcher only enqueues work on `stream` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Per-launch row tables travel in the kernel argument block, so a launch
+// covers at most this many rows; the host splits larger batches.
+constexpr int kRopeRowsPerLaunch = 128;
+constexpr int kRopeMaxPairs = 256;           // rotary_dims <= 512
+constexpr int kDecodeRowsPerLaunch = 128;
+constexpr int kCombineRowsPerLaunch = 256;
+
+enum Dtype : int32_t { kF32 = 0, kBF16 = 1 };
+
+// ------------------------------------------------------------------ RoPE
+struct RopeParams {
+  const void* x;
+  void* y;
+  int32_t rows;          // batch rows in this launch
+  int32_t tokens, inner, feat;
+  int64_t sb, st, si;    // element strides (x and y)
+  int32_t rotary;        // rotary dims R
+  int32_t per_row;       // 1: off[b] per row, 0: off[0] for all rows
+  int32_t copy_tail;     // y != x
+  int64_t off[kRopeRowsPerLaunch];
+  float inv[kRopeMaxPairs];
+};
+hipError_t launch_rope(int32_t dtype, const RopeParams& p, hipStream_t stream);
+
+// ------------------------------------------------------------------ absorb
+struct AbsorbQParams {
+  const void* q;          // [B,H,dn] strided
+  int64_t q_sb, q_sh;
+  const void* w;          // [H*(dn+dv), r]
+  float* q_lat;           // [B,H,r]
+  int32_t batch, heads, dn, dv, r;
+};
+hipError_t launch_absorb_q(int32_t dtype, const AbsorbQParams& p, hipStream_t stream);
+
+struct AbsorbVParams {
+  const float* o_lat;     // [B,H,r]
+  const void* w;          // [H*(dn+dv), r]
+  float* ctx;             // [B,H*dv]
+  int32_t batch, heads, dn, dv, r;
+};
+hipError_t launch_absorb_v(int32_t dtype, const AbsorbVParams& p, hipStream_t stream);
+
+// ------------------------------------------------------------------ decode
+struct DecodeRows {
+  int32_t kv_len[kDecodeRowsPerLaunch];
+  int32_t n_att[kDecodeRowsPerLaunch];   // attended count
+  int32_t sel_off[kDecodeRowsPerLaunch]; // -1: dense row, else offset into sel
+};
+
+struct DecodeParams {
+  const float* q_lat;     // [rows,H,r] (already offset to the first row of the launch)
+  const void* q_rope;     // strided
+  int64_t qr_sb, qr_sh;
+  const void* latent;     // strided, first row of the launch
+  int64_t lat_sb, lat_st;
+  const void* rope;
+  int64_t rope_sb, rope_st;
+  const int32_t* sel;     // selection base (may be null)
+  float* part_o;          // [rows,H,s_max,r]
+  float* part_lse;        // [rows,H,s_max]
+  int32_t* dev_err;
+  int32_t rows, heads, r, dr, width;
+  int32_t chunk, s_max, s_launch;        // s_launch = max splits over the launch rows
+  float scale;
+  DecodeRows tab;
+};
+hipError_t launch_decode(int32_t dtype, const DecodeParams& p, hipStream_t stream);
+
+// ------------------------------------------------------------------ combine
+struct CombineParams {
+  const float* part_o;
+  const float* part_lse;
+  float* o_lat;
+  float* lse;             // may be null
+  int32_t rows, heads, r, s_max;
+  int32_t n_splits[kCombineRowsPerLaunch];
+};
+hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+
+// ------------------------------------------------------------------ prefill
+struct PrefillParams {
+  int32_t dtype;
+  int32_t batch, tokens, keys, heads, ql, r, dn, dr, dv;
+  const void* q_c;
+  const void* w_qb;
+  const void* latent;
+  const void* rope;
+  const void* w_kvb;
+  const int64_t* q_offsets;   // host
+  const int32_t* left_pad;    // host (nullable)
+  double theta;
+  float scale;
+  void* workspace;
+  float* ctx;
+};
+size_t prefill_workspace_bytes(const PrefillParams& p);
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+
+// Inverse-frequency table of partial interleaved RoPE, built on the host in
+// double exactly as the page builds it (see mla_abi.cpp).
+void rope_inverse_frequencies(int32_t rotary, double theta, float* out);
+
+}  // namespace mla

@@ -1,0 +1,323 @@
+// C ABI of libmla.so: argument checks (mirroring the checks the pages make
+// before computing), row tables, launch setup.  No allocation, no
+// synchronisation: every entry point enqueues work on the caller's stream.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <string>
+
+#include "../../include/mla.h"
+#include "launch.hpp"
+
+namespace mla {
+
+void rope_inverse_frequencies(int32_t rotary, double theta, float* out) {
+  // Page "mlx-bun 0.0.11 -> 0.0.13", glm52-mla.ts, partialInterleavedRopeMlx:
+  // exponent = f32(-2p / R) with the quotient taken in double, inverse
+  // frequency = f32(pow(f32(theta), exponent)) with the power in double.
+  const double theta32 = static_cast<double>(static_cast<float>(theta));
+  for (int p = 0; p < rotary / 2; ++p) {
+    const float exponent = static_cast<float>(static_cast<double>(-2 * p) / static_cast<double>(rotary));
+    out[p] = static_cast<float>(pow(theta32, static_cast<double>(exponent)));
+  }
+}
+
+hipError_t launch_decode_generic(int32_t dtype, const DecodeParams& p, hipStream_t stream);
+bool decode_mfma_supported(int32_t dtype, int32_t heads, int32_t r, int32_t dr);
+hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
+size_t prefill_generic_workspace_bytes(const PrefillParams& p);
+hipError_t launch_prefill_generic(const PrefillParams& p, hipStream_t stream);
+
+}  // namespace mla
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+int ok() {
+  g_error.clear();
+  return MLA_OK;
+}
+
+int device(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(MLA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool valid_dtype(int32_t d) { return d == MLA_DTYPE_F32 || d == MLA_DTYPE_BF16; }
+size_t elem_size(int32_t d) { return d == MLA_DTYPE_BF16 ? 2 : 4; }
+
+const void* advance(const void* p, int64_t elems, int32_t dtype) {
+  return static_cast<const char*>(p) + elems * static_cast<int64_t>(elem_size(dtype));
+}
+
+constexpr double kMaxPosition = 9007199254740992.0;   // 2^53
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_last_error(void) { return g_error.c_str(); }
+
+int mla_version(void) { return 100; }
+
+int mla_rope_partial_interleaved(int32_t dtype, const void* x, void* y, int32_t batch, int32_t tokens,
+                                 int32_t inner, int32_t feat, int64_t stride_b, int64_t stride_t, int64_t stride_i,
+                                 int32_t rotary_dims, double theta, const int64_t* offsets, int32_t n_offsets,
+                                 hipStream_t stream) {
+  if (!valid_dtype(dtype)) return fail(MLA_ERR_ARG, "rope: unknown dtype %d", dtype);
+  if (batch < 0 || tokens < 0 || inner < 0 || feat < 1)
+    return fail(MLA_ERR_ARG, "rope: batch, tokens, inner must be >= 0 and feat >= 1");
+  if (!offsets) return fail(MLA_ERR_ARG, "rope: offsets is NULL");
+  if (n_offsets != 1 && n_offsets != batch)
+    return fail(MLA_ERR_ROPE, "RoPE row offsets %d != batch %d", n_offsets, batch);
+  for (int i = 0; i < n_offsets; ++i) {
+    if (offsets[i] < 0) return fail(MLA_ERR_ROPE, "RoPE position offset must be a non-negative integer");
+    if (static_cast<double>(offsets[i]) + tokens > kMaxPosition)
+      return fail(MLA_ERR_UNSUPPORTED, "rope: offset + tokens exceeds 2^53");
+  }
+  if (rotary_dims <= 0 || (rotary_dims & 1) || rotary_dims > feat)
+    return fail(MLA_ERR_ROPE, "RoPE dimensions must be positive, even, and fit the feature axis");
+  if (!(theta > 0.0) || !isfinite(theta)) return fail(MLA_ERR_ROPE, "RoPE theta must be positive");
+  if (rotary_dims > 2 * mla::kRopeMaxPairs)
+    return fail(MLA_ERR_UNSUPPORTED, "rope: rotary_dims %d > %d", rotary_dims, 2 * mla::kRopeMaxPairs);
+  if (static_cast<int64_t>(batch) * tokens * inner == 0) return ok();
+  if (!x || !y) return fail(MLA_ERR_ARG, "rope: x or y is NULL");
+  if (stride_b < 0 || stride_t < 0 || stride_i < 0) return fail(MLA_ERR_ARG, "rope: negative stride");
+
+  mla::RopeParams p{};
+  p.tokens = tokens;
+  p.inner = inner;
+  p.feat = feat;
+  p.sb = stride_b;
+  p.st = stride_t;
+  p.si = stride_i;
+  p.rotary = rotary_dims;
+  p.per_row = n_offsets == batch && batch > 1 ? 1 : 0;
+  p.copy_tail = (x != y) && rotary_dims < feat;
+  mla::rope_inverse_frequencies(rotary_dims, theta, p.inv);
+  if (!p.per_row) p.off[0] = offsets[0];
+  for (int b0 = 0; b0 < batch; b0 += mla::kRopeRowsPerLaunch) {
+    p.rows = std::min(batch - b0, mla::kRopeRowsPerLaunch);
+    p.x = advance(x, b0 * stride_b, dtype);
+    p.y = const_cast<void*>(advance(y, b0 * stride_b, dtype));
+    if (p.per_row)
+      for (int i = 0; i < p.rows; ++i) p.off[i] = offsets[b0 + i];
+    hipError_t e = mla::launch_rope(dtype, p, stream);
+    if (e != hipSuccess) return device(e, "rope launch");
+  }
+  return ok();
+}
+
+int mla_absorb_q(int32_t dtype, const void* q_nope, int64_t q_stride_b, int64_t q_stride_h, const void* w_kv_b,
+                 float* q_lat, int32_t batch, int32_t heads, int32_t qk_nope, int32_t v_head, int32_t kv_lora_rank,
+                 hipStream_t stream) {
+  if (!valid_dtype(dtype)) return fail(MLA_ERR_ARG, "absorb_q: unknown dtype %d", dtype);
+  if (batch < 0 || heads < 1 || qk_nope < 1 || v_head < 1 || kv_lora_rank < 1)
+    return fail(MLA_ERR_ARG, "absorb_q: batch >= 0 and positive heads, qk_nope, v_head, kv_lora_rank required");
+  if (batch == 0) return ok();
+  if (!q_nope || !w_kv_b || !q_lat) return fail(MLA_ERR_ARG, "absorb_q: NULL pointer");
+  if (q_stride_b < 0 || q_stride_h < 0) return fail(MLA_ERR_ARG, "absorb_q: negative stride");
+  if (batch > 65535 * 8) return fail(MLA_ERR_UNSUPPORTED, "absorb_q: batch too large");
+  mla::AbsorbQParams p{q_nope, q_stride_b, q_stride_h, w_kv_b, q_lat, batch, heads, qk_nope, v_head, kv_lora_rank};
+  return device(mla::launch_absorb_q(dtype, p, stream), "absorb_q launch");
+}
+
+int mla_absorb_v(int32_t dtype, const float* o_lat, const void* w_kv_b, float* ctx, int32_t batch, int32_t heads,
+                 int32_t qk_nope, int32_t v_head, int32_t kv_lora_rank, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return fail(MLA_ERR_ARG, "absorb_v: unknown dtype %d", dtype);
+  if (batch < 0 || heads < 1 || qk_nope < 1 || v_head < 1 || kv_lora_rank < 1)
+    return fail(MLA_ERR_ARG, "absorb_v: batch >= 0 and positive heads, qk_nope, v_head, kv_lora_rank required");
+  if (batch == 0) return ok();
+  if (!o_lat || !w_kv_b || !ctx) return fail(MLA_ERR_ARG, "absorb_v: NULL pointer");
+  mla::AbsorbVParams p{o_lat, w_kv_b, ctx, batch, heads, qk_nope, v_head, kv_lora_rank};
+  return device(mla::launch_absorb_v(dtype, p, stream), "absorb_v launch");
+}
+
+int mla_decode_latent_attn(int32_t dtype, const float* q_lat, const void* q_rope, int64_t qr_stride_b,
+                           int64_t qr_stride_h, const void* latent, int64_t latent_stride_b, int64_t latent_stride_t,
+                           const void* rope, int64_t rope_stride_b, int64_t rope_stride_t, int32_t batch,
+                           int32_t heads, int32_t kv_lora_rank, int32_t rope_dim, int32_t width,
+                           const int32_t* kv_len, const int32_t* sel_idx, const int32_t* sel_count,
+                           float softmax_scale, int32_t chunk_len, float* part_o, float* part_lse, int32_t s_max,
+                           int32_t* dev_err, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return fail(MLA_ERR_ARG, "decode: unknown dtype %d", dtype);
+  if (batch < 0 || heads < 1 || kv_lora_rank < 1 || rope_dim < 1 || width < 1)
+    return fail(MLA_ERR_ARG, "decode: batch >= 0 and positive heads, kv_lora_rank, rope_dim, width required");
+  if (chunk_len < 1) return fail(MLA_ERR_ARG, "decode: chunk_len must be >= 1");
+  if (!isfinite(softmax_scale)) return fail(MLA_ERR_ARG, "decode: softmax_scale must be finite");
+  if (batch == 0) return ok();
+  if (!q_lat || !q_rope || !latent || !rope || !kv_len || !part_o || !part_lse)
+    return fail(MLA_ERR_ARG, "decode: NULL pointer");
+  if (latent_stride_b < 0 || latent_stride_t < 1 || rope_stride_b < 0 || rope_stride_t < 1 || qr_stride_b < 0 ||
+      qr_stride_h < 0)
+    return fail(MLA_ERR_ARG, "decode: bad stride");
+  if (kv_lora_rank > 1024 || rope_dim > 256)
+    return fail(MLA_ERR_UNSUPPORTED, "decode: kv_lora_rank <= 1024 and rope_dim <= 256 supported");
+  if (heads > 65535) return fail(MLA_ERR_UNSUPPORTED, "decode: heads > 65535");
+  int64_t sel_total = 0;
+  int max_splits = 0;
+  bool any_sel = false;
+  for (int b = 0; b < batch; ++b) {
+    if (kv_len[b] < 1 || kv_len[b] > width)
+      return fail(MLA_ERR_SHAPE, "decode: kv_len[%d] = %d outside [1, %d]", b, kv_len[b], width);
+    int n = kv_len[b];
+    if (sel_count) {
+      if (sel_count[b] == 0) return fail(MLA_ERR_SELECTION, "DSA selection cannot be empty (row %d)", b);
+      if (sel_count[b] < -1) return fail(MLA_ERR_SELECTION, "decode: sel_count[%d] = %d", b, sel_count[b]);
+      if (sel_count[b] > 0) {
+        n = sel_count[b];
+        sel_total += n;
+        any_sel = true;
+      }
+    }
+    max_splits = std::max(max_splits, (n + chunk_len - 1) / chunk_len);
+  }
+  if (sel_total > 0x7fffffffLL) return fail(MLA_ERR_UNSUPPORTED, "decode: more than 2^31-1 selected indices");
+  if (any_sel && !sel_idx) return fail(MLA_ERR_ARG, "decode: sel_idx is NULL but rows are selected");
+  if (s_max < max_splits) return fail(MLA_ERR_SHAPE, "decode: s_max %d < %d splits", s_max, max_splits);
+
+  const bool mfma = mla::decode_mfma_supported(dtype, heads, kv_lora_rank, rope_dim);
+  mla::DecodeParams p{};
+  p.qr_sb = qr_stride_b;
+  p.qr_sh = qr_stride_h;
+  p.lat_sb = latent_stride_b;
+  p.lat_st = latent_stride_t;
+  p.rope_sb = rope_stride_b;
+  p.rope_st = rope_stride_t;
+  p.sel = sel_idx;
+  p.dev_err = dev_err;
+  p.heads = heads;
+  p.r = kv_lora_rank;
+  p.dr = rope_dim;
+  p.width = width;
+  p.chunk = chunk_len;
+  p.s_max = s_max;
+  p.scale = softmax_scale;
+  int32_t sel_off = 0;
+  for (int b0 = 0; b0 < batch; b0 += mla::kDecodeRowsPerLaunch) {
+    p.rows = std::min(batch - b0, mla::kDecodeRowsPerLaunch);
+    p.s_launch = 0;
+    for (int i = 0; i < p.rows; ++i) {
+      const int b = b0 + i;
+      const bool sel = sel_count && sel_count[b] > 0;
+      p.tab.kv_len[i] = kv_len[b];
+      p.tab.n_att[i] = sel ? sel_count[b] : kv_len[b];
+      p.tab.sel_off[i] = sel ? sel_off : -1;
+      if (sel) sel_off += sel_count[b];
+      p.s_launch = std::max(p.s_launch, (p.tab.n_att[i] + chunk_len - 1) / chunk_len);
+    }
+    p.q_lat = q_lat + static_cast<int64_t>(b0) * heads * kv_lora_rank;
+    p.q_rope = advance(q_rope, b0 * qr_stride_b, dtype);
+    p.latent = advance(latent, b0 * latent_stride_b, dtype);
+    p.rope = advance(rope, b0 * rope_stride_b, dtype);
+    p.part_o = part_o + static_cast<int64_t>(b0) * heads * s_max * kv_lora_rank;
+    p.part_lse = part_lse + static_cast<int64_t>(b0) * heads * s_max;
+    hipError_t e = mfma ? mla::launch_decode_mfma(p, stream) : mla::launch_decode_generic(dtype, p, stream);
+    if (e != hipSuccess) return device(e, "decode launch");
+  }
+  return ok();
+}
+
+int mla_decode_combine(const float* part_o, const float* part_lse, int32_t batch, int32_t heads, int32_t kv_lora_rank,
+                       int32_t s_max, const int32_t* n_splits, float* o_lat, float* lse, hipStream_t stream) {
+  if (batch < 0 || heads < 1 || kv_lora_rank < 1 || s_max < 1)
+    return fail(MLA_ERR_ARG, "combine: batch >= 0 and positive heads, kv_lora_rank, s_max required");
+  if (batch == 0) return ok();
+  if (!part_o || !part_lse || !n_splits || !o_lat) return fail(MLA_ERR_ARG, "combine: NULL pointer");
+  if (heads > 65535) return fail(MLA_ERR_UNSUPPORTED, "combine: heads > 65535");
+  for (int b = 0; b < batch; ++b)
+    if (n_splits[b] < 1 || n_splits[b] > s_max)
+      return fail(MLA_ERR_SHAPE, "combine: n_splits[%d] = %d outside [1, %d]", b, n_splits[b], s_max);
+  mla::CombineParams p{};
+  p.heads = heads;
+  p.r = kv_lora_rank;
+  p.s_max = s_max;
+  for (int b0 = 0; b0 < batch; b0 += mla::kCombineRowsPerLaunch) {
+    p.rows = std::min(batch - b0, mla::kCombineRowsPerLaunch);
+    for (int i = 0; i < p.rows; ++i) p.n_splits[i] = n_splits[b0 + i];
+    const int64_t bh = static_cast<int64_t>(b0) * heads;
+    p.part_o = part_o + bh * s_max * kv_lora_rank;
+    p.part_lse = part_lse + bh * s_max;
+    p.o_lat = o_lat + bh * kv_lora_rank;
+    p.lse = lse ? lse + bh : nullptr;
+    hipError_t e = mla::launch_combine(p, stream);
+    if (e != hipSuccess) return device(e, "combine launch");
+  }
+  return ok();
+}
+
+int mla_prefill_reconstructed(int32_t dtype, int32_t batch, int32_t tokens, int32_t keys, int32_t heads,
+                              int32_t q_lora_rank, int32_t kv_lora_rank, int32_t qk_nope, int32_t qk_rope,
+                              int32_t v_head, const void* q_c, const void* w_q_b, const void* latent,
+                              const void* rope, const void* w_kv_b, const int64_t* q_offsets, double theta,
+                              const int32_t* left_pad, float softmax_scale, void* workspace, size_t* workspace_bytes,
+                              float* ctx, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return fail(MLA_ERR_ARG, "prefill: unknown dtype %d", dtype);
+  if (batch < 0 || tokens < 1 || keys < 1 || heads < 1 || q_lora_rank < 1 || kv_lora_rank < 1 || qk_nope < 1 ||
+      qk_rope < 1 || v_head < 1)
+    return fail(MLA_ERR_ARG, "prefill: batch >= 0 and positive geometry required");
+  if (keys < tokens) return fail(MLA_ERR_SHAPE, "MLA state cannot be shorter than the query block");
+  if (qk_rope & 1) return fail(MLA_ERR_ROPE, "RoPE dimensions must be positive, even, and fit the feature axis");
+  if (!(theta > 0.0) || !isfinite(theta)) return fail(MLA_ERR_ROPE, "RoPE theta must be positive");
+  if (!isfinite(softmax_scale)) return fail(MLA_ERR_ARG, "prefill: softmax_scale must be finite");
+  if (qk_nope + qk_rope > 256 || v_head > 256 || qk_rope > 2 * mla::kRopeMaxPairs)
+    return fail(MLA_ERR_UNSUPPORTED, "prefill: qk_nope + qk_rope <= 256 and v_head <= 256 supported");
+  if (heads > 65535) return fail(MLA_ERR_UNSUPPORTED, "prefill: heads > 65535");
+  if (!workspace_bytes) return fail(MLA_ERR_ARG, "prefill: workspace_bytes is NULL");
+  mla::PrefillParams p{};
+  p.dtype = dtype;
+  p.batch = batch;
+  p.tokens = tokens;
+  p.keys = keys;
+  p.heads = heads;
+  p.ql = q_lora_rank;
+  p.r = kv_lora_rank;
+  p.dn = qk_nope;
+  p.dr = qk_rope;
+  p.dv = v_head;
+  p.q_c = q_c;
+  p.w_qb = w_q_b;
+  p.latent = latent;
+  p.rope = rope;
+  p.w_kvb = w_kv_b;
+  p.q_offsets = q_offsets;
+  p.left_pad = left_pad;
+  p.theta = theta;
+  p.scale = softmax_scale;
+  p.ctx = ctx;
+  const size_t need = mla::prefill_workspace_bytes(p);
+  if (!workspace) {
+    *workspace_bytes = need;
+    return ok();
+  }
+  if (*workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "prefill: workspace %zu bytes < %zu required", *workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(MLA_ERR_WORKSPACE, "prefill: workspace not 256-byte aligned");
+  if (batch == 0) return ok();
+  if (!q_c || !w_q_b || !latent || !rope || !w_kv_b || !q_offsets || !ctx)
+    return fail(MLA_ERR_ARG, "prefill: NULL pointer");
+  for (int b = 0; b < batch; ++b) {
+    if (q_offsets[b] < 0) return fail(MLA_ERR_ROPE, "RoPE position offset must be a non-negative integer");
+    if (static_cast<double>(q_offsets[b]) + tokens > kMaxPosition)
+      return fail(MLA_ERR_UNSUPPORTED, "prefill: offset + tokens exceeds 2^53");
+    if (left_pad && (left_pad[b] < 0 || left_pad[b] > keys))
+      return fail(MLA_ERR_SHAPE, "prefill: left_pad[%d] = %d outside [0, %d]", b, left_pad[b], keys);
+  }
+  p.workspace = workspace;
+  return device(mla::launch_prefill(p, stream), "prefill launch");
+}
+
+}  // extern "C"

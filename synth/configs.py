@@ -124,12 +124,21 @@ class DecodeInputs:
         return self.sel_idx[start : start + int(self.sel_count[row])].astype(np.int64)
 
 
-def decode_inputs(cfg: DecodeConfig, layer: int = 0, batch: int | None = None) -> DecodeInputs:
-    """Seeded inputs of a decode workload.  `batch` overrides the row count (ragged only)."""
+def decode_inputs(cfg: DecodeConfig, layer: int = 0, batch: int | None = None,
+                  lengths=None) -> DecodeInputs:
+    """Seeded inputs of a decode workload.
+
+    `batch` overrides the row count (ragged draws); `lengths` fixes the per-row
+    cache lengths instead of drawing them (smaller parity cases).
+    """
     cid = cfg.config_id
     b = cfg.batch if batch is None else batch
     h, dn, dr, dv, r = cfg.heads, cfg.qk_nope, cfg.qk_rope, cfg.v_head, cfg.kv_lora_rank
-    if cfg.ragged is not None:
+    if lengths is not None:
+        lengths = np.asarray(lengths, dtype=np.int32)
+        b = len(lengths)
+        width = int(lengths.max())
+    elif cfg.ragged is not None:
         lengths = g.ragged_lengths(cid, b, cfg.ragged[0], cfg.ragged[1], layer)
         width = int(lengths.max())
     else:
@@ -170,11 +179,15 @@ class PrefillInputs:
     left_pad: np.ndarray | None = None   # int32 [B]
 
 
-def prefill_inputs(cfg: PrefillConfig, layer: int = 0, tokens: int | None = None) -> PrefillInputs:
-    """Seeded prefill inputs.  `tokens` overrides T = K (smaller parity sizes)."""
+def prefill_inputs(cfg: PrefillConfig, layer: int = 0, tokens: int | None = None,
+                   keys: int | None = None) -> PrefillInputs:
+    """Seeded prefill inputs.  `tokens` / `keys` override T and K (smaller parity
+    sizes; keys defaults to tokens when only tokens is given)."""
     cid = cfg.config_id
     t = cfg.tokens if tokens is None else tokens
-    k = cfg.keys if tokens is None else tokens
+    k = (cfg.keys if tokens is None else tokens) if keys is None else keys
+    if k < t:
+        raise ValueError("keys must be >= tokens")
     b, h, ql = cfg.batch, cfg.heads, cfg.q_lora_rank
     dn, dr, dv, r = cfg.qk_nope, cfg.qk_rope, cfg.v_head, cfg.kv_lora_rank
     c_q = store(g.normal_f32(cid, g.T_C_Q, (b, t, ql), layer=layer), cfg.dtype)

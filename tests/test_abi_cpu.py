@@ -1,0 +1,121 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+entry point, and rejects bad arguments before touching the GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from mla_latent_kv_partial_amd import _lib
+from mla_latent_kv_partial_amd._lib import i32_array, i64_array, lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, ARG, SHAPE, ROPE, SEL, WS, DEV, UNSUP = 0, -1, -2, -3, -4, -5, -6, -7
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails on the host first
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "mla.h")).read()
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_version_and_empty_error():
+    assert lib.mla_version() >= 100
+    assert isinstance(lib.mla_last_error(), bytes)
+
+
+def _rope(**kw):
+    a = dict(dtype=0, x=FAKE, y=FAKE, batch=2, tokens=3, inner=4, feat=16, sb=192, st=64, si=16, rot=16,
+             theta=1e4, offs=[1, 2], n=2)
+    a.update(kw)
+    return lib.mla_rope_partial_interleaved(a["dtype"], a["x"], a["y"], a["batch"], a["tokens"], a["inner"],
+                                            a["feat"], a["sb"], a["st"], a["si"], a["rot"], a["theta"],
+                                            i64_array(a["offs"]), a["n"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), ARG),
+    (dict(rot=15), ROPE), (dict(rot=0), ROPE), (dict(rot=18), ROPE),
+    (dict(theta=0.0), ROPE), (dict(theta=float("inf")), ROPE), (dict(theta=float("nan")), ROPE),
+    (dict(offs=[-1, 0]), ROPE), (dict(n=3, offs=[0, 1, 2]), ROPE),
+    (dict(feat=1024, rot=1024), UNSUP),
+    (dict(offs=[2 ** 53, 0]), UNSUP),
+])
+def test_rope_rejections(kw, code):
+    assert _rope(**kw) == code
+    assert lib.mla_last_error() != b""
+
+
+def test_rope_empty_is_a_no_op():
+    assert _rope(batch=0, offs=[0], n=1) == OK
+    assert _rope(tokens=0) == OK
+
+
+def _decode(**kw):
+    a = dict(dtype=1, b=2, h=64, r=512, dr=64, w=100, kv=[100, 50], sel=None, cnt=None, chunk=32, s_max=4,
+             scale=0.07, sel_idx=None)
+    a.update(kw)
+    return lib.mla_decode_latent_attn(
+        a["dtype"], FAKE, FAKE, 64 * 64, 64, FAKE, 100 * 576, 576, FAKE, 100 * 576, 576, a["b"], a["h"], a["r"],
+        a["dr"], a["w"], i32_array(a["kv"]), a["sel_idx"], None if a["cnt"] is None else i32_array(a["cnt"]),
+        a["scale"], a["chunk"], FAKE, FAKE, a["s_max"], None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kv=[0, 5]), SHAPE), (dict(kv=[101, 5]), SHAPE),
+    (dict(s_max=3), SHAPE),
+    (dict(cnt=[0, -1], sel_idx=FAKE), SEL), (dict(cnt=[-2, -1], sel_idx=FAKE), SEL),
+    (dict(cnt=[5, -1], sel_idx=None), ARG),
+    (dict(chunk=0), ARG), (dict(h=0), ARG), (dict(dtype=3), ARG), (dict(scale=float("nan")), ARG),
+    (dict(r=2048), UNSUP), (dict(dr=512), UNSUP),
+])
+def test_decode_rejections(kw, code):
+    assert _decode(**kw) == code
+
+
+def test_decode_empty_batch_is_ok():
+    assert _decode(b=0, kv=[]) == OK
+
+
+@pytest.mark.parametrize("ns,code", [([0, 1], SHAPE), ([5, 1], SHAPE)])
+def test_combine_rejections(ns, code):
+    assert lib.mla_decode_combine(FAKE, FAKE, 2, 4, 8, 4, i32_array(ns), FAKE, None, None) == code
+
+
+def test_absorb_rejections():
+    assert lib.mla_absorb_q(5, FAKE, 1, 1, FAKE, FAKE, 1, 1, 1, 1, 1, None) == ARG
+    assert lib.mla_absorb_q(0, None, 1, 1, FAKE, FAKE, 1, 1, 1, 1, 1, None) == ARG
+    assert lib.mla_absorb_v(0, FAKE, FAKE, FAKE, 1, 0, 1, 1, 1, None) == ARG
+    assert lib.mla_absorb_v(0, FAKE, FAKE, FAKE, 0, 1, 1, 1, 1, None) == OK
+
+
+def _prefill(ws=None, size=0, **kw):
+    a = dict(dtype=1, b=1, t=16, k=16, h=4, ql=32, r=32, dn=16, dr=8, dv=16, offs=[0], theta=1e4, pad=None)
+    a.update(kw)
+    sz = ctypes.c_size_t(size)
+    code = lib.mla_prefill_reconstructed(
+        a["dtype"], a["b"], a["t"], a["k"], a["h"], a["ql"], a["r"], a["dn"], a["dr"], a["dv"], FAKE, FAKE, FAKE,
+        FAKE, FAKE, i64_array(a["offs"]), a["theta"], None if a["pad"] is None else i32_array(a["pad"]), 0.1,
+        ws, ctypes.byref(sz), FAKE, None)
+    return code, sz.value
+
+
+def test_prefill_workspace_query_and_rejections():
+    code, need = _prefill()
+    assert code == OK and need > 0
+    assert _prefill(ws=ctypes.c_void_p(0x10000), size=need - 1)[0] == WS
+    assert _prefill(ws=ctypes.c_void_p(0x10010), size=need)[0] == WS        # misaligned
+    assert _prefill(t=17)[0] == SHAPE                                          # keys < tokens
+    assert _prefill(dr=7)[0] == ROPE
+    assert _prefill(theta=-1.0)[0] == ROPE
+    assert _prefill(dn=250)[0] == UNSUP
+    assert _prefill(ws=ctypes.c_void_p(0x10000), size=need, offs=[-1])[0] == ROPE
+    assert _prefill(ws=ctypes.c_void_p(0x10000), size=need, pad=[17])[0] == SHAPE

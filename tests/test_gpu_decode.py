@@ -1,0 +1,257 @@
+"""GPU parity of the decode chain (RoPE -> absorb_q -> latent attention -> combine
+-> absorb_v) against the oracle on the four decode workloads, and the bitwise
+invariants of the attention kernel."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import configs as cf
+from tests.gpu_util import TOL, assert_close, bitwise_equal, dev, host_values, say
+
+pytestmark = pytest.mark.gpu
+
+CHUNK = {"tiny_f32": 32, "dense_bf16": 256, "ragged_bf16": 512, "dsa_bf16": 256}
+
+
+def _mla():
+    import mla_latent_kv_partial_amd as mla
+    return mla
+
+
+class Step:
+    """Device tensors of one decode workload and the GPU chain over them."""
+
+    def __init__(self, inp: cf.DecodeInputs, packed: bool = True):
+        self.inp = inp
+        c = inp.cfg
+        self.cfg = c
+        self.q_nope = dev(inp.q_nope)
+        self.q_rope = dev(inp.q_rope_raw)
+        self.w = dev(inp.w_kvb)
+        if packed:
+            cache = np.concatenate([inp.latent, inp.rope], axis=-1)
+            self.cache = dev(cache)
+            self.latent = self.cache[..., : c.kv_lora_rank]
+            self.rope = self.cache[..., c.kv_lora_rank:]
+        else:
+            self.latent = dev(inp.latent)
+            self.rope = dev(inp.rope)
+        self.sel = dev(inp.sel_idx) if inp.sel_idx is not None else None
+        self.err = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def run(self, chunk):
+        mla = _mla()
+        c, inp = self.cfg, self.inp
+        q_rope = self.q_rope.clone()
+        view = q_rope.view(q_rope.shape[0], 1, c.heads, c.qk_rope)
+        mla.mla_rope_partial_interleaved(view, [int(o) for o in inp.offsets], c.qk_rope, c.theta, out=view)
+        q_lat = mla.mla_absorb_q(self.q_nope, self.w, c.v_head)
+        po, pl, ns = mla.mla_decode_latent_attn(q_lat, q_rope, self.latent, self.rope, inp.kv_len, c.softmax_scale,
+                                                chunk, sel_idx=self.sel, sel_count=inp.sel_count, dev_err=self.err)
+        o_lat, lse = mla.mla_decode_combine(po, pl, ns)
+        ctx = mla.mla_absorb_v(o_lat, self.w, c.qk_nope, c.v_head)
+        torch.cuda.synchronize()
+        return dict(q_rope=q_rope, q_lat=q_lat, part_o=po, part_lse=pl, n_splits=ns, o_lat=o_lat, lse=lse, ctx=ctx)
+
+
+def _selections(inp):
+    if inp.sel_count is None:
+        return None
+    return [inp.attended(b) if inp.sel_count[b] > 0 else None for b in range(len(inp.kv_len))]
+
+
+def _oracle(inp, reconstructed=False):
+    c = inp.cfg
+    q_rope = oracle.rope_partial_interleaved(cf.values(inp.q_rope_raw)[:, None], [int(o) for o in inp.offsets],
+                                             c.qk_rope, c.theta)[:, 0]
+    args = (cf.values(inp.q_nope), q_rope, cf.values(inp.latent), cf.values(inp.rope), cf.values(inp.w_kvb),
+            inp.kv_len, _selections(inp), c.softmax_scale, c.qk_nope, c.v_head)
+    out = oracle.decode_absorbed(*args)
+    out["q_rope"] = q_rope
+    if reconstructed:
+        out["ctx_rec"] = oracle.decode_reconstructed(*args)
+    return out
+
+
+@pytest.mark.parametrize("cfg", cf.DECODE_CONFIGS, ids=lambda c: c.name)
+def test_decode_chain_matches_oracle(cfg):
+    say(f"decode chain {cfg.name}: generating")
+    inp = cf.decode_inputs(cfg)
+    step = Step(inp)
+    say(f"decode chain {cfg.name}: gpu")
+    got = step.run(CHUNK[cfg.name])
+    assert int(step.err.item()) == 0
+    say(f"decode chain {cfg.name}: oracle")
+    ref = _oracle(inp, reconstructed=cfg.name in ("tiny_f32", "dense_bf16"))
+    assert_close(host_values(got["q_lat"]), ref["q_lat"], cfg.dtype, "q_lat")
+    assert_close(host_values(got["o_lat"]), ref["o_lat"], cfg.dtype, "o_lat")
+    assert_close(host_values(got["lse"]), ref["lse"], cfg.dtype, "lse")
+    assert_close(host_values(got["ctx"]), ref["ctx"], cfg.dtype, "ctx vs absorbed oracle")
+    if "ctx_rec" in ref:
+        assert_close(host_values(got["ctx"]), ref["ctx_rec"], cfg.dtype, "ctx vs reconstructed oracle")
+
+
+def _small_ragged(lengths=(700, 1, 333), seed_layer=5):
+    """The ragged workload's head geometry at short, fixed per-row lengths."""
+    return cf.decode_inputs(cf.RAGGED_BF16, layer=seed_layer, lengths=lengths)
+
+
+@pytest.mark.parametrize("chunk", [1, 7, 64, 100, 256, 1024])
+def test_partials_match_oracle(chunk):
+    inp = _small_ragged(lengths=(40, 1, 9) if chunk == 1 else (700, 1, 333), seed_layer=7)
+    step = Step(inp, packed=False)
+    got = step.run(chunk)
+    c = inp.cfg
+    q_lat = host_values(got["q_lat"])
+    q_rope = host_values(got["q_rope"])
+    po, pl, ns = oracle.latent_attention_partials(q_lat, q_rope, cf.values(inp.latent), cf.values(inp.rope),
+                                                  inp.kv_len, None, c.softmax_scale, chunk)
+    assert list(ns) == got["n_splits"]
+    gpo, gpl = host_values(got["part_o"]), host_values(got["part_lse"])
+    for b in range(len(ns)):
+        n = int(ns[b])
+        assert_close(gpo[b, :, :n], po[b, :, :n], c.dtype, f"part_o row {b}")
+        assert_close(gpl[b, :, :n], pl[b, :, :n], c.dtype, f"part_lse row {b}")
+
+
+def test_batched_rows_equal_separate_calls_bitwise():
+    inp = _small_ragged(lengths=(700, 5, 333), seed_layer=8)
+    step = Step(inp, packed=True)
+    mla = _mla()
+    c = inp.cfg
+    q_lat = mla.mla_absorb_q(step.q_nope, step.w, c.v_head)
+    po, pl, ns = mla.mla_decode_latent_attn(q_lat, step.q_rope, step.latent, step.rope, inp.kv_len,
+                                            c.softmax_scale, 128)
+    w = step.latent.shape[1]
+    for b in range(3):
+        n = int(inp.kv_len[b])
+        po_b, pl_b, ns_b = mla.mla_decode_latent_attn(
+            q_lat[b:b + 1], step.q_rope[b:b + 1], step.latent[b:b + 1, w - n:], step.rope[b:b + 1, w - n:], [n],
+            c.softmax_scale, 128, s_max=po.shape[2])
+        assert ns_b[0] == ns[b]
+        assert bitwise_equal(po_b[0, :, :ns[b]], po[b, :, :ns[b]])
+        assert bitwise_equal(pl_b[0, :, :ns[b]], pl[b, :, :ns[b]])
+
+
+def test_selection_of_all_equals_dense_bitwise():
+    inp = _small_ragged(lengths=(700, 5, 333), seed_layer=9)
+    step = Step(inp)
+    mla = _mla()
+    c = inp.cfg
+    q_lat = mla.mla_absorb_q(step.q_nope, step.w, c.v_head)
+    dense = mla.mla_decode_latent_attn(q_lat, step.q_rope, step.latent, step.rope, inp.kv_len, c.softmax_scale, 64)
+    sel = torch.cat([torch.arange(int(n), dtype=torch.int32) for n in inp.kv_len]).cuda()
+    counts = [int(n) for n in inp.kv_len]
+    picked = mla.mla_decode_latent_attn(q_lat, step.q_rope, step.latent, step.rope, inp.kv_len, c.softmax_scale, 64,
+                                        sel_idx=sel, sel_count=counts)
+    for b in range(3):
+        n = dense[2][b]
+        assert bitwise_equal(dense[0][b, :, :n], picked[0][b, :, :n])
+        assert bitwise_equal(dense[1][b, :, :n], picked[1][b, :, :n])
+
+
+def test_dsa_gather_equals_compacted_dense_bitwise():
+    """Full-size DSA workload: gathering 2048 of 131072 tokens is bit-identical to
+    attending a cache that holds exactly those tokens in the same order."""
+    inp = cf.decode_inputs(cf.DSA_BF16)
+    step = Step(inp)
+    mla = _mla()
+    c = inp.cfg
+    q_lat = mla.mla_absorb_q(step.q_nope, step.w, c.v_head)
+    sparse = mla.mla_decode_latent_attn(q_lat, step.q_rope, step.latent, step.rope, inp.kv_len, c.softmax_scale,
+                                        256, sel_idx=step.sel, sel_count=inp.sel_count, dev_err=step.err)
+    idx = torch.from_numpy(inp.sel_idx.astype(np.int64)).cuda() + (step.latent.shape[1] - int(inp.kv_len[0]))
+    compact = step.cache[:, idx].contiguous()
+    dense = mla.mla_decode_latent_attn(q_lat, step.q_rope, compact[..., :512], compact[..., 512:],
+                                       [len(inp.sel_idx)], c.softmax_scale, 256)
+    torch.cuda.synchronize()
+    assert int(step.err.item()) == 0
+    assert sparse[2] == dense[2] == [8]
+    assert bitwise_equal(sparse[0], dense[0]) and bitwise_equal(sparse[1], dense[1])
+
+
+def test_selection_permutation_within_tolerance_and_bad_index_flagged():
+    inp = _small_ragged(lengths=(700, 5, 333), seed_layer=10)
+    step = Step(inp)
+    mla = _mla()
+    c = inp.cfg
+    q_lat = mla.mla_absorb_q(step.q_nope, step.w, c.v_head)
+    rng = np.random.default_rng(0)
+    rows = [np.sort(rng.choice(700, 300, replace=False)), np.array([4, 0, 2]), np.sort(rng.choice(333, 50, False))]
+    counts = [len(r) for r in rows]
+
+    def run(rws, err=None):
+        sel = torch.from_numpy(np.concatenate(rws).astype(np.int32)).cuda()
+        po, pl, ns = mla.mla_decode_latent_attn(q_lat, step.q_rope, step.latent, step.rope, inp.kv_len,
+                                                c.softmax_scale, 64, sel_idx=sel, sel_count=[len(r) for r in rws],
+                                                dev_err=err)
+        o, lse = mla.mla_decode_combine(po, pl, ns)
+        return host_values(o), host_values(lse)
+
+    a = run(rows)
+    b = run([rng.permutation(r) for r in rows])
+    assert_close(b[0], a[0], c.dtype, "permuted selection o_lat")
+    # an index outside [0, kv_len) is skipped and flagged
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bad = [rows[0], np.array([4, 0, 2, 5, -1]), rows[2]]
+    got = run(bad, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) != 0
+    assert_close(got[0], a[0], c.dtype, "masked bad indices")
+
+
+def test_single_token_and_uniform_closed_forms():
+    inp = _small_ragged(lengths=(1, 40, 9), seed_layer=11)
+    step = Step(inp)
+    mla = _mla()
+    c = inp.cfg
+    q_lat = mla.mla_absorb_q(step.q_nope, step.w, c.v_head)
+    po, pl, ns = mla.mla_decode_latent_attn(q_lat, step.q_rope, step.latent, step.rope, inp.kv_len,
+                                            c.softmax_scale, 16)
+    o, lse = mla.mla_decode_combine(po, pl, ns)
+    c0 = step.latent[0, -1].float()
+    assert torch.equal(o[0], c0.expand_as(o[0])), "one attended token must be returned exactly"
+    zq = torch.zeros_like(q_lat)
+    zr = torch.zeros_like(step.q_rope)
+    po, pl, ns = mla.mla_decode_latent_attn(zq, zr, step.latent, step.rope, inp.kv_len, c.softmax_scale, 16)
+    o, lse = mla.mla_decode_combine(po, pl, ns)
+    for b in range(3):
+        n = int(inp.kv_len[b])
+        mean = host_values(step.latent[b, -n:]).mean(axis=0)
+        assert_close(host_values(o[b]), np.broadcast_to(mean, (c.heads, mean.size)), c.dtype, f"uniform row {b}",
+                     tol=1e-5)
+        assert np.allclose(host_values(lse[b]), math.log(n), rtol=1e-5)
+
+
+@pytest.mark.parametrize("dtype,batch", [(cf.F32, 1), (cf.BF16, 1), (cf.BF16, 8), (cf.BF16, 33)])
+def test_absorb_matches_oracle(dtype, batch):
+    cfg = cf.TINY_F32 if dtype == cf.F32 else cf.DENSE_BF16
+    from synth import generators as g
+    h, dn, dv, r = cfg.heads, cfg.qk_nope, cfg.v_head, cfg.kv_lora_rank
+    q = cf.store(g.normal_f32(95, 1, (batch, h, dn)), dtype)
+    w = cf.store(g.normal_f32(95, 2, (h * (dn + dv), r), std=1 / math.sqrt(r)), dtype)
+    o = g.normal_f32(95, 3, (batch, h, r))
+    mla = _mla()
+    q_lat = mla.mla_absorb_q(dev(q), dev(w), dv)
+    ctx = mla.mla_absorb_v(dev(o), dev(w), dn, dv)
+    torch.cuda.synchronize()
+    assert_close(host_values(q_lat), oracle.absorb_q(cf.values(q), cf.values(w), dn, dv), dtype, "absorb_q")
+    assert_close(host_values(ctx), oracle.absorb_v(o.astype(np.float64), cf.values(w), dn, dv), dtype, "absorb_v",
+                 tol=TOL[dtype] if dtype == cf.F32 else 2e-2)
+
+
+def test_absorb_unit_query_selects_weight_row_exactly():
+    cfg = cf.DENSE_BF16
+    from synth import generators as g
+    h, dn, dv, r = cfg.heads, cfg.qk_nope, cfg.v_head, cfg.kv_lora_rank
+    w = cf.store(g.normal_f32(96, 2, (h * (dn + dv), r), std=1 / math.sqrt(r)), cf.BF16)
+    q = np.zeros((2, h, dn), dtype=np.float32)
+    q[0, :, 5] = 1.0
+    q[1, :, 127] = 1.0
+    q_lat = _mla().mla_absorb_q(dev(cf.store(q, cf.BF16)), dev(w), dv)
+    wt = dev(w).float().view(h, dn + dv, r)
+    assert torch.equal(q_lat[0], wt[:, 5]) and torch.equal(q_lat[1], wt[:, 127])
