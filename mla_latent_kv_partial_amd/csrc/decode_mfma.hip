@@ -1,12 +1,481 @@
-// MFMA latent decode attention for the bf16 GLM geometry (placeholder: the
-// generic kernel serves every shape until this kernel lands).
+// MFMA latent decode attention for the bf16 GLM geometry: kv_lora_rank 512,
+// rope 64, heads a multiple of 16.  Computes the split-T partials of the
+// page's absorbed decode (page "mlx-bun 0.0.11 -> 0.0.13", glm52-mla.ts,
+// Glm52Mla.attendAbsorbed: scores = scale * (q_lat . latent + q_rope . rope),
+// softmax over the attended tokens, latent context = P . latent), including
+// its DSA gather and the ragged right-aligned rows of Glm52Mla.forward.
+//
+// One workgroup serves one (row, split) for up to 64 heads, so the cache is
+// read once for all heads.  The workgroup has two kinds of waves, two per SIMD:
+//   * score waves (w < NW, heads 16w..16w+15) hold Q in registers, compute
+//     S^T[token, head] = K . Q^T on v_mfma_f32_16x16x32_bf16 from K fragments
+//     read by ds_read_b128, run the online softmax in fp32 / exp2 (each lane
+//     owns one head) and hand P (bf16, already in MFMA operand layout) and the
+//     rescale factors to the context waves through LDS;
+//   * context waves (w >= NW) hold the fp32 context accumulators and, one tile
+//     behind, compute O^T[dim, head] += V^T . P^T with V^T fragments read from
+//     the token-major tile by ds_read_b64_tr_b16.
+// Splitting the two halves keeps each wave under 256 registers, so two waves
+// share each SIMD and hide each other's LDS and MFMA latencies.
+//
+// HBM -> LDS: 32-token tiles stream through a 4-stage LDS ring by
+// global_load_lds_dwordx4 (each lane moves 16 bytes), two tiles ahead of the
+// score waves.  A token occupies one 1168-byte LDS row: latent (1024 B), rope
+// (128 B), 16 B of padding.  A gathered row uses the same copies with
+// per-token addresses, so a gather and a dense read of the same tokens are
+// bit-identical.  The running max of a head only moves when a tile exceeds it
+// by more than 2^8, so accumulator rescales are rare.
+//
+// Bank layout: the 73-chunk row stride is odd in 16-byte bank groups, so the
+// 16 rows of a score fragment hit 16 distinct groups; score row m of a 16-token
+// block holds token sigma(m), which spaces the 4 rows of each transposing read
+// two apart, so those are conflict-free as well.  Every LDS read address is a
+// per-lane base plus an immediate.
+#include <math.h>
+
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace mla {
+namespace {
 
-bool decode_mfma_supported(int32_t, int32_t, int32_t, int32_t) { return false; }
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-hipError_t launch_decode_mfma(const DecodeParams&, hipStream_t) { return hipErrorNotSupported; }
+constexpr int kR = 512;
+constexpr int kDR = 64;
+constexpr int kNT = 32;                    // tokens per tile
+constexpr int kRowChunks = 73;             // 16-byte chunks per token row (64 latent, 8 rope, 1 pad)
+constexpr int kRowBytes = kRowChunks * 16;
+constexpr int kDmaPerTile = (kNT * kRowChunks + 63) / 64;   // 37 copies of 1 KB
+constexpr int kTileBytes = kDmaPerTile * 1024;              // rows + tail of the last copy
+constexpr int kStageBytes = kTileBytes + kNT * 4;           // + the tile's selection indices
+constexpr int kStages = 4;
+constexpr int kQSteps = kR / 32 + kDR / 32;                 // 18 k-steps of the scores
+constexpr int kDimBlocks = kR / 16;                         // 32 output blocks of 16 dims
+constexpr float kRescaleSlack = 8.f;                        // log2 units
+constexpr int kMaxHeadGroups = 4;                           // 16-head groups per workgroup
+
+__shared__ __attribute__((aligned(1024))) char g_stage[kStages * kStageBytes];
+__shared__ __attribute__((aligned(16))) char g_p[2][kMaxHeadGroups][kWave * 16];   // P operands, by tile parity
+__shared__ float g_alpha[2][kMaxHeadGroups][16];                                     // rescale factor per head
+__shared__ int g_moved[2][kMaxHeadGroups];                                           // any rescale in the wave
+__shared__ float g_l[kMaxHeadGroups][16];                                            // softmax denominators
+
+// Token held by score row m of a 16-token block.
+__device__ __forceinline__ int sigma(int m) {
+  const int g = m >> 2, j = m & 3;
+  return 2 * j + 8 * (g & 1) + (g >> 1);
+}
+
+// The tile pipeline is driven by hand: the HBM -> LDS copies, the waits on
+// them and the workgroup barrier are issued as instructions whose ordering the
+// compiler keeps ("memory" clobbers) but does not try to track, so the number
+// of copies in flight is exactly what the code below states.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
+}
+
+// Each lane copies 16 bytes from `src` to lds + 16 * lane (lds is wave-uniform).
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
+
+// Same, from the wave-uniform base `sbase` plus a per-lane 32-bit byte offset.
+__device__ __forceinline__ void dma16_off(const void* sbase, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+
+// Each active lane copies 4 bytes from `src` to lds + 4 * lane.
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// NW head groups of 16 per workgroup (2 NW waves).  PACKED: rope = latent + 512
+// elements with the same strides (one [B, W, 576] cache) and every row offset
+// below 2^32: copies use an SGPR base plus a 32-bit lane offset; otherwise
+// each lane forms a 64-bit address.
+template <int NW, bool GATHER, bool PACKED>
+struct Decode {
+  static constexpr int kWaves = 2 * NW;
+  // Wave v issues tile copies n = v, v + kWaves, ... below kDmaPerTile:
+  // kMaxDma or kMaxDma - 1 of them.
+  static constexpr int kMaxDma = (kDmaPerTile + kWaves - 1) / kWaves;
+
+  const DecodeParams& p;
+  int lane, wave, hw, h, g, head;
+  bool scorer;
+  int n_tok, nt, len, pad, sel_base, n_dma;
+  bool gather_row;              // this row reads its tokens through the selection list
+  bool bad_index;               // an out-of-range selection index was seen (flagged at the end)
+  const char* lat_base;
+  const char* rope_base;
+  int64_t lat_st, rope_st;      // bytes
+  float scale_log2;
+  int dma_row[kMaxDma];         // token row of this lane's chunk in copy i
+  int dma_off[kMaxDma];         // byte offset of the chunk in its latent row, or rope row (sign bit set)
+  uint32_t qk_base, tr_base;    // per-lane LDS byte offsets of the fragment reads within a stage
+  // Score waves: reg[0..17] hold the Q operands (bf16 bits).  Context waves:
+  // reg[db] accumulates O^T for dims 16 db + 4 g + (0..3) of head h.
+  f32x4 reg[kDimBlocks];
+  float m_run, l_run;
+  uint32_t mask0, mask1, mask2;  // validity of tiles i, i+1, i+2 (bit t: token t)
+
+  __device__ __forceinline__ Decode(const DecodeParams& prm) : p(prm) {}
+
+  // Row slot and validity of tile token `lane` (lanes < 32) from its index into the valid slice.
+  __device__ __forceinline__ int slot_of(int tile, int idx, uint32_t& m) {
+    const bool in = lane < kNT && tile * kNT + lane < n_tok;
+    const bool ok = in && idx >= 0 && idx < len;
+    bad_index |= in && !ok;
+    m = static_cast<uint32_t>(__ballot(ok));
+    return ok ? pad + idx : p.width - 1;   // masked tokens read a valid row, weighted by zero
+  }
+
+  __device__ __forceinline__ int dense_index(int tile) const { return sel_base + tile * kNT + lane; }
+
+  __device__ __forceinline__ static char* stage(int s) { return g_stage + s * kStageBytes; }
+  __device__ __forceinline__ static int* idx_area(int s) { return reinterpret_cast<int*>(stage(s) + kTileBytes); }
+
+  __device__ __forceinline__ void copy(int i, int slot_v, uint32_t dst) const {
+    const int slot = __shfl(slot_v, dma_row[i], kWave);
+    const int off = dma_off[i];
+    if (PACKED) {
+      dma16_off(lat_base, static_cast<uint32_t>(slot) * static_cast<uint32_t>(lat_st) + static_cast<uint32_t>(off),
+                dst + (wave + kWaves * i) * 1024);
+    } else {
+      const char* src = off >= 0 ? lat_base + slot * lat_st + off : rope_base + slot * rope_st + (off & 0x7fff);
+      dma16(src, dst + (wave + kWaves * i) * 1024);
+    }
+  }
+
+  // Copy one tile into stage s.  slot_v: lane t < 32 holds token t's row slot.
+  __device__ __forceinline__ void issue_tile(int s, int slot_v) const {
+    const uint32_t dst = lds_addr(stage(s));
+#pragma unroll
+    for (int i = 0; i < kMaxDma - 1; ++i) copy(i, slot_v, dst);   // every wave has these
+    if (n_dma == kMaxDma) copy(kMaxDma - 1, slot_v, dst);
+  }
+
+  // Gathered rows: copy the 32 selection indices of a tile (clamped inside the
+  // row's list) into the index area of stage s.  Wave 0 only.
+  __device__ __forceinline__ void issue_idx(int s, int tile) const {
+    if (gather_row && wave == 0 && lane < kNT) {
+      const int j = min(tile * kNT + lane, n_tok - 1);
+      dma4(p.sel + sel_base + j, lds_addr(idx_area(s)));
+    }
+  }
+
+  // Wait for tile i's copies; with `more`, the copies of tile i+1 (issued one
+  // step ago) may stay in flight.
+  __device__ __forceinline__ void wait_tile(bool more) const {
+    if (more) {
+      if (n_dma == kMaxDma)
+        wait_vm<kMaxDma>();
+      else
+        wait_vm<kMaxDma - 1>();
+    } else {
+      wait_vm<0>();
+    }
+  }
+
+  // Score wave, tile i in stage s: scores, softmax, P and rescale factors out.
+  __device__ __forceinline__ void score(int s, int parity, uint32_t valid) {
+    const char* st = stage(s);
+    // two 16-token blocks, each over two accumulators (even / odd k-steps)
+    f32x4 acc[4] = {};
+#pragma unroll
+    for (int ks = 0; ks < kQSteps; ++ks) {
+      const int off = ks < kR / 32 ? ks * 64 : kR * 2 + (ks - kR / 32) * 64;
+      const bf16x8 q = __builtin_bit_cast(bf16x8, reg[ks]);
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + qk_base + tb * 16 * kRowBytes + off);
+        acc[2 * tb + (ks & 1)] = mfma(a, q, acc[2 * tb + (ks & 1)]);
+      }
+    }
+    // lane owns head h and score rows 4g+i of both blocks: tokens 16tb + sigma(4g+i)
+    float x[8];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * tb + sigma(4 * g + i);
+        const float sc = acc[2 * tb][i] + acc[2 * tb + 1][i];
+        x[4 * tb + i] = ((valid >> t) & 1u) ? sc * scale_log2 : -INFINITY;
+      }
+    float mt = x[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) mt = fmaxf(mt, x[k]);
+    mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+    // Move the reference max only when this tile exceeds it by the slack (the
+    // first valid tile always moves it from -inf).
+    const bool move = mt > m_run + kRescaleSlack;
+    const bool any_move = __any(move);
+    float alpha = 1.f;
+    if (move) {
+      alpha = __builtin_amdgcn_exp2f(m_run - mt);
+      m_run = mt;
+    }
+    l_run *= alpha;
+    bf16x8 pb;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float pr = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[k] - m_run);
+      l_run += pr;
+      pb[k] = static_cast<__bf16>(pr);
+    }
+    *reinterpret_cast<bf16x8*>(&g_p[parity][hw][lane * 16]) = pb;
+    if (any_move) {
+      if (g == 0) g_alpha[parity][hw][h] = alpha;
+    }
+    if (lane == 0) g_moved[parity][hw] = any_move ? 1 : 0;
+  }
+
+  // Context wave, tile i-1 in stage s: rescale if asked, then O^T += V^T . P^T.
+  __device__ __forceinline__ void context(int s, int parity) {
+    if (g_moved[parity][hw]) {
+      const float alpha = g_alpha[parity][hw][h];
+#pragma unroll
+      for (int db = 0; db < kDimBlocks; ++db) reg[db] *= alpha;
+    }
+    const bf16x8 pb = *reinterpret_cast<const bf16x8*>(&g_p[parity][hw][lane * 16]);
+    const char* st = stage(s);
+#pragma unroll
+    for (int db = 0; db < kDimBlocks; ++db) {
+      lds_s16x4* a1 = (lds_s16x4*)(st + tr_base + db * 32);
+      lds_s16x4* a2 = (lds_s16x4*)(st + tr_base + 16 * kRowBytes + db * 32);
+      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(a1);
+      const s16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(a2);
+      const s16x8 v = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
+      reg[db] = mfma(__builtin_bit_cast(bf16x8, v), pb, reg[db]);
+    }
+  }
+
+  __device__ __forceinline__ void run(int b, int s) {
+    // ---- per-lane copy plan (the same for every tile): copy i of this wave
+    // moves stage chunk k = 64 (wave + kWaves i) + lane, which is chunk c of
+    // token row k / 73 (c < 64 latent, c < 72 rope, 72 padding).
+    n_dma = (kDmaPerTile - wave + kWaves - 1) / kWaves;
+#pragma unroll
+    for (int i = 0; i < kMaxDma; ++i) {
+      const int k = 64 * (wave + kWaves * i) + lane;
+      int row = k / kRowChunks;
+      const int c = k - row * kRowChunks;
+      row = min(row, kNT - 1);   // the tail of the last copy lands past the rows; it reads a valid token
+      dma_row[i] = row;
+      if (PACKED)
+        dma_off[i] = c < 72 ? c * 16 : 0;   // rope follows the latent in the packed row
+      else
+        dma_off[i] = c < 64 ? c * 16 : (c < 72 ? static_cast<int>(0x80000000u | static_cast<uint32_t>((c - 64) * 16)) : 0);
+    }
+    // ---- per-lane LDS fragment bases
+    qk_base = sigma(h) * kRowBytes + g * 16;
+    tr_base = sigma(4 * g + (h >> 2)) * kRowBytes + ((h & 3) >> 1) * 16 + (h & 1) * 8;
+
+    // ---- prologue.  Issue order: query loads (score waves), then the copies
+    // of tiles 0 and 1 (and the indices of tile 2); converting the queries then
+    // waits once for all of them, so the latencies overlap.
+    float4 qraw[2 * (kR / 32)];
+    short qrraw[kDR / 32][8];
+    if (scorer) {
+      const float* ql = p.q_lat + (static_cast<int64_t>(b) * p.heads + head) * kR;
+#pragma unroll
+      for (int ks = 0; ks < kR / 32; ++ks) {
+        qraw[2 * ks] = *reinterpret_cast<const float4*>(ql + 8 * g + 32 * ks);
+        qraw[2 * ks + 1] = *reinterpret_cast<const float4*>(ql + 8 * g + 32 * ks + 4);
+      }
+      const uint16_t* qr = static_cast<const uint16_t*>(p.q_rope) + b * p.qr_sb + head * p.qr_sh;
+#pragma unroll
+      for (int ks = 0; ks < kDR / 32; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qrraw[ks][e] = static_cast<short>(qr[8 * g + 32 * ks + e]);
+    }
+    {
+      int idx0v, idx1v;
+      if (GATHER && gather_row) {
+        idx0v = lane < kNT ? p.sel[sel_base + min(lane, n_tok - 1)] : 0;
+        idx1v = lane < kNT ? p.sel[sel_base + min(kNT + lane, n_tok - 1)] : 0;
+      } else {
+        idx0v = dense_index(0);
+        idx1v = dense_index(1);
+      }
+      const int slot0 = slot_of(0, idx0v, mask0);
+      issue_tile(0, slot0);
+      if (GATHER && gather_row && nt > 2) issue_idx(2, 2);
+      // Tile 1 is copied even for single-tile splits (all of its tokens are
+      // then masked and read a valid row), which keeps the wait counts fixed.
+      const int slot1 = slot_of(1, idx1v, mask1);
+      issue_tile(1, slot1);
+    }
+    if (scorer) {
+#pragma unroll
+      for (int ks = 0; ks < kR / 32; ++ks) {
+        const float4 u = qraw[2 * ks], v = qraw[2 * ks + 1];
+        bf16x8 q;
+        q[0] = static_cast<__bf16>(u.x); q[1] = static_cast<__bf16>(u.y);
+        q[2] = static_cast<__bf16>(u.z); q[3] = static_cast<__bf16>(u.w);
+        q[4] = static_cast<__bf16>(v.x); q[5] = static_cast<__bf16>(v.y);
+        q[6] = static_cast<__bf16>(v.z); q[7] = static_cast<__bf16>(v.w);
+        reg[ks] = __builtin_bit_cast(f32x4, q);
+      }
+#pragma unroll
+      for (int ks = 0; ks < kDR / 32; ++ks) {
+        s16x8 q;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q[e] = qrraw[ks][e];
+        reg[kR / 32 + ks] = __builtin_bit_cast(f32x4, q);
+      }
+#pragma unroll
+      for (int k = kQSteps; k < kDimBlocks; ++k) reg[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    } else {
+#pragma unroll
+      for (int db = 0; db < kDimBlocks; ++db) reg[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // Materialise the registers ahead of the pipeline's first copy issue
+    // (volatile asm statements keep their relative order).
+#pragma unroll
+    for (int k = 0; k < kDimBlocks; ++k) asm volatile("" : "+v"(reg[k]));
+    m_run = -INFINITY;
+    l_run = 0.f;
+
+    // ---- pipeline: step i scores tile i and accumulates the context of tile
+    // i - 1; tile i + 2 is requested at its start.
+    for (int i = 0; i <= nt; ++i) {
+      if (i < nt) wait_tile(i + 1 < nt || i == 0);
+      barrier();
+      if (i + 2 < nt) {
+        int idx;
+        if (GATHER && gather_row) {
+          idx = lane < kNT ? idx_area((i + 2) % kStages)[lane] : 0;
+          if (i + 3 < nt) issue_idx((i + 3) % kStages, i + 3);
+        } else {
+          idx = dense_index(i + 2);
+        }
+        const int slot = slot_of(i + 2, idx, mask2);
+        issue_tile((i + 2) % kStages, slot);
+      }
+      if (scorer) {
+        if (i < nt) score(i % kStages, i & 1, mask0);
+      } else if (i >= 1) {
+        context((i - 1) % kStages, (i - 1) & 1);
+      }
+      mask0 = mask1;
+      mask1 = mask2;
+    }
+
+    // ---- normalise and store the split's partials
+    const int64_t ps = (static_cast<int64_t>(b) * p.heads + head) * p.s_max + s;
+    if (scorer) {
+      float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
+      l_tot += __shfl_xor(l_tot, 32, kWave);
+      if (g == 0) {
+        g_l[hw][h] = l_tot;
+        p.part_lse[ps] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+      }
+    }
+    barrier();
+    if (!scorer) {
+      const float l_tot = g_l[hw][h];
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      float* out = p.part_o + ps * kR + 4 * g;
+#pragma unroll
+      for (int db = 0; db < kDimBlocks; ++db) {
+        const f32x4 v = reg[db] * inv;
+        *reinterpret_cast<float4*>(out + 16 * db) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    }
+    if (GATHER && bad_index && p.dev_err) atomicOr(p.dev_err, 1);
+  }
+};
+
+template <int NW, bool GATHER, bool PACKED>
+__global__ __launch_bounds__(2 * NW * kWave) void decode_mfma_kernel(DecodeParams p) {
+  const int s = blockIdx.x, b = blockIdx.y;
+  const int n_att = p.tab.n_att[b];
+  const int j0 = s * p.chunk;
+  if (j0 >= n_att) return;
+  Decode<NW, GATHER, PACKED> d(p);
+  d.lane = threadIdx.x & (kWave - 1);
+  d.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  d.scorer = d.wave < NW;
+  d.hw = d.scorer ? d.wave : d.wave - NW;
+  d.h = d.lane & 15;
+  d.g = d.lane >> 4;
+  d.head = blockIdx.z * (16 * NW) + d.hw * 16 + d.h;
+  d.n_tok = min(p.chunk, n_att - j0);
+  d.nt = (d.n_tok + kNT - 1) / kNT;
+  d.len = p.tab.kv_len[b];
+  d.pad = p.width - d.len;
+  d.gather_row = GATHER && p.tab.sel_off[b] >= 0;
+  d.bad_index = false;
+  d.sel_base = d.gather_row ? p.tab.sel_off[b] + j0 : j0;
+  d.lat_base = static_cast<const char*>(p.latent) + static_cast<int64_t>(b) * p.lat_sb * 2;
+  d.rope_base = static_cast<const char*>(p.rope) + static_cast<int64_t>(b) * p.rope_sb * 2;
+  d.lat_st = p.lat_st * 2;
+  d.rope_st = p.rope_st * 2;
+  d.scale_log2 = p.scale * 1.4426950408889634f;
+  d.run(b, s);
+}
+
+template <int NW, bool GATHER>
+hipError_t launch_nw(const DecodeParams& p, bool packed, int groups, hipStream_t stream) {
+  dim3 grid(p.s_launch, p.rows, groups);
+  if (packed)
+    hipLaunchKernelGGL((decode_mfma_kernel<NW, GATHER, true>), grid, dim3(2 * NW * kWave), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<NW, GATHER, false>), grid, dim3(2 * NW * kWave), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool decode_mfma_supported(int32_t dtype, int32_t heads, int32_t r, int32_t dr) {
+  return dtype == kBF16 && r == kR && dr == kDR && heads % 16 == 0 && (heads <= 64 || heads % 64 == 0);
+}
+
+// Layout requirements of the copy path: 16-byte aligned rows.
+bool decode_mfma_layout_ok(const void* q_lat, const void* latent, int64_t lat_sb, int64_t lat_st, const void* rope,
+                           int64_t rope_sb, int64_t rope_st) {
+  auto al = [](const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15) == 0; };
+  return al(q_lat) && al(latent) && al(rope) && lat_sb % 8 == 0 && lat_st % 8 == 0 && rope_sb % 8 == 0 &&
+         rope_st % 8 == 0;
+}
+
+hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
+  if (p.rows == 0 || p.s_launch == 0) return hipSuccess;
+  bool gather = false;
+  for (int i = 0; i < p.rows; ++i) gather |= p.tab.sel_off[i] >= 0;
+  const int nw = p.heads >= 64 ? 4 : p.heads / 16;
+  const int groups = p.heads / (16 * nw);
+  // Packed cache: rope right after the latent, same strides, and every byte
+  // offset of a row start (plus its 1152 bytes) below 2^32.
+  const bool packed = static_cast<const char*>(p.rope) == static_cast<const char*>(p.latent) + 2 * kR &&
+                      p.rope_sb == p.lat_sb && p.rope_st == p.lat_st &&
+                      (static_cast<int64_t>(p.rows - 1) * p.lat_sb + static_cast<int64_t>(p.width - 1) * p.lat_st) * 2 +
+                              2 * (kR + kDR) <= 0xffffffffLL;
+  switch (nw) {
+    case 1: return gather ? launch_nw<1, true>(p, packed, groups, stream) : launch_nw<1, false>(p, packed, groups, stream);
+    case 2: return gather ? launch_nw<2, true>(p, packed, groups, stream) : launch_nw<2, false>(p, packed, groups, stream);
+    default: return gather ? launch_nw<4, true>(p, packed, groups, stream) : launch_nw<4, false>(p, packed, groups, stream);
+  }
+}
 
 }  // namespace mla

@@ -26,6 +26,8 @@ void rope_inverse_frequencies(int32_t rotary, double theta, float* out) {
 
 hipError_t launch_decode_generic(int32_t dtype, const DecodeParams& p, hipStream_t stream);
 bool decode_mfma_supported(int32_t dtype, int32_t heads, int32_t r, int32_t dr);
+bool decode_mfma_layout_ok(const void* q_lat, const void* latent, int64_t lat_sb, int64_t lat_st, const void* rope,
+                           int64_t rope_sb, int64_t rope_st);
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
 size_t prefill_generic_workspace_bytes(const PrefillParams& p);
 hipError_t launch_prefill_generic(const PrefillParams& p, hipStream_t stream);
@@ -189,7 +191,10 @@ int mla_decode_latent_attn(int32_t dtype, const float* q_lat, const void* q_rope
   if (any_sel && !sel_idx) return fail(MLA_ERR_ARG, "decode: sel_idx is NULL but rows are selected");
   if (s_max < max_splits) return fail(MLA_ERR_SHAPE, "decode: s_max %d < %d splits", s_max, max_splits);
 
-  const bool mfma = mla::decode_mfma_supported(dtype, heads, kv_lora_rank, rope_dim);
+  const bool mfma = mla::decode_mfma_supported(dtype, heads, kv_lora_rank, rope_dim) &&
+                    mla::decode_mfma_layout_ok(q_lat, latent, latent_stride_b, latent_stride_t, rope, rope_stride_b,
+                                               rope_stride_t) &&
+                    (reinterpret_cast<uintptr_t>(part_o) & 15) == 0;
   mla::DecodeParams p{};
   p.qr_sb = qr_stride_b;
   p.qr_sh = qr_stride_h;
