@@ -1,0 +1,342 @@
+#!/usr/bin/env python3
+"""Benchmark of the MLA latent-KV decode hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L]
+
+Timed step: one decode step of the batched ragged workload (B=8 rows, H=64,
+qk_nope=128, qk_rope=64, v_head=128, kv_lora_rank=512, per-row cache lengths
+drawn from U{1024..32768}, bf16 cache, fp32 accumulation) over L distinct layer
+instances (default 8, about 1.25 GB of caches, beyond the 256 MB last-level
+cache).  Per layer the step runs the whole chain through the C ABI:
+  partial interleaved RoPE of q_rope -> absorb_q -> latent attention (split-T
+  partials) -> combine -> absorb_v.
+The step is captured once in a HIP graph and replayed; W warmup replays, then
+K timed replays between synchronisations.
+
+Printed: one JSON line.  value = rows*layers/s of the step.  roofline = the
+latent attention kernel (the dominant kernel): algorithmic cache bytes per
+launch (attended tokens x 1152 B) / its mean launch time, measured with HIP
+events around eager launches on the launch stream.  cpu_baseline = the CPU
+oracle's reconstructed decode on a bounded sample of the same rows.  extra =
+the dense (chained and layer-stacked), DSA and prefill workloads.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+TOKEN_BYTES = (512 + 64) * 2    # latent + rope per cached token, bf16
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 512 MiB device copy (for FETCH_SIZE / WRITE_SIZE scaling)")
+    return ap.parse_args()
+
+
+class DecodeLayer:
+    """Device tensors of one layer instance of a decode workload, packed cache [B, W, 576]."""
+
+    def __init__(self, cfg, layer, torch, cf, dev, batch=None):
+        inp = cf.decode_inputs(cfg, layer=layer, batch=batch)
+        self.inp = inp
+        import numpy as np
+        cache = np.concatenate([inp.latent, inp.rope], axis=-1)
+        self.cache = torch.from_numpy(cache.view(np.int16)).to(dev).view(torch.bfloat16)
+        del cache
+        self.latent = self.cache[..., : cfg.kv_lora_rank]
+        self.rope = self.cache[..., cfg.kv_lora_rank:]
+        b = inp.q_nope.shape[0]
+        self.q_nope = torch.from_numpy(inp.q_nope.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.q_rope_raw = torch.from_numpy(inp.q_rope_raw.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.w = torch.from_numpy(inp.w_kvb.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.sel = torch.from_numpy(inp.sel_idx).to(dev) if inp.sel_idx is not None else None
+        self.kv_len = [int(v) for v in inp.kv_len]
+        self.sel_count = None if inp.sel_count is None else [int(v) for v in inp.sel_count]
+        self.offsets = [int(v) for v in inp.offsets]
+        self.n_att = [c if self.sel_count is not None and c > 0 else n
+                      for n, c in zip(self.kv_len, self.sel_count or [-1] * b)]
+        self.q_rope = torch.empty_like(self.q_rope_raw)
+        self.q_lat = torch.empty((b, cfg.heads, cfg.kv_lora_rank), dtype=torch.float32, device=dev)
+        self.o_lat = torch.empty_like(self.q_lat)
+        self.lse = torch.empty((b, cfg.heads), dtype=torch.float32, device=dev)
+        self.ctx = torch.empty((b, cfg.heads * cfg.v_head), dtype=torch.float32, device=dev)
+        self.cfg = cfg
+        # drop the host copies of the large arrays
+        inp.latent = inp.rope = None
+
+    def plan(self, mla, slots, torch, dev):
+        self.chunk = mla.plan_chunk_len(self.n_att, slots)
+        self.n_splits = [mla.split_count(n, self.chunk) for n in self.n_att]
+        self.s_max = max(self.n_splits)
+        b = len(self.kv_len)
+        self.part_o = torch.empty((b, self.cfg.heads, self.s_max, self.cfg.kv_lora_rank), dtype=torch.float32,
+                                  device=dev)
+        self.part_lse = torch.empty((b, self.cfg.heads, self.s_max), dtype=torch.float32, device=dev)
+
+    def attn(self, mla):
+        c = self.cfg
+        mla.mla_decode_latent_attn(self.q_lat, self.q_rope, self.latent, self.rope, self.kv_len, c.softmax_scale,
+                                   self.chunk, sel_idx=self.sel, sel_count=self.sel_count, part_o=self.part_o,
+                                   part_lse=self.part_lse, s_max=self.s_max)
+
+    def step(self, mla):
+        c = self.cfg
+        b = len(self.kv_len)
+        mla.mla_rope_partial_interleaved(self.q_rope_raw.view(b, 1, c.heads, c.qk_rope), self.offsets, c.qk_rope,
+                                         c.theta, out=self.q_rope.view(b, 1, c.heads, c.qk_rope))
+        mla.mla_absorb_q(self.q_nope, self.w, c.v_head, q_lat=self.q_lat)
+        self.attn(mla)
+        mla.mla_decode_combine(self.part_o, self.part_lse, self.n_splits, o_lat=self.o_lat, lse=self.lse)
+        mla.mla_absorb_v(self.o_lat, self.w, c.qk_nope, c.v_head, ctx=self.ctx)
+
+    @property
+    def cache_bytes(self):
+        return sum(self.n_att) * TOKEN_BYTES
+
+
+def time_graph(torch, fn, steps, warmup):
+    """Capture fn() in a HIP graph; mean ms per replay over `steps` replays."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()   # eager run on the capture stream before capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, g
+
+
+def time_launches(torch, fns, reps):
+    """Mean ms per launch of each fn, HIP events around every eager launch on the current stream."""
+    for fn in fns:
+        fn()
+    torch.cuda.synchronize()
+    pairs = []
+    for _ in range(reps):
+        for fn in fns:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            pairs.append((a, b))
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+
+
+def cpu_baseline(cf, oracle, layer0, budget_s=12.0):
+    """The oracle's reconstructed decode (the plain definition) on rows of layer 0
+    of the timed workload, until about `budget_s` seconds of CPU work."""
+    import numpy as np
+    import threadpoolctl
+    inp = cf.decode_inputs(layer0.cfg, layer=0)
+    c = inp.cfg
+    q_rope = oracle.rope_partial_interleaved(cf.values(inp.q_rope_raw)[:, None], [int(o) for o in inp.offsets],
+                                             c.qk_rope, c.theta)[:, 0]
+    lat, rope, w = cf.values(inp.latent), cf.values(inp.rope), cf.values(inp.w_kvb)
+    q_nope = cf.values(inp.q_nope)
+    order = np.argsort(inp.kv_len)            # shortest rows first keeps the sample bounded
+    rows, tokens, t0 = 0, 0, time.perf_counter()
+    for b in order:
+        oracle.decode_reconstructed(q_nope[b:b + 1], q_rope[b:b + 1], lat[b:b + 1], rope[b:b + 1], w,
+                                    inp.kv_len[b:b + 1], None, c.softmax_scale, c.qk_nope, c.v_head)
+        rows += 1
+        tokens += int(inp.kv_len[b])
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
+    return {
+        "value": rows / dt, "unit": "rows*layers/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"reconstructed fp64 decode of {rows} row(s) of layer 0 ({tokens} cached tokens) in {dt:.1f}s",
+        "cache_GBps": tokens * TOKEN_BYTES / dt / 1e9,
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
+              "(the multi-GPU design is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import mla_latent_kv_partial_amd as mla
+    from synth import configs as cf
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    slots = props.multi_processor_count
+    log(f"device {props.name} CUs={slots}")
+
+    # ------------------------------------------------------------- timed step
+    cfg = cf.RAGGED_BF16
+    layers = []
+    for l in range(args.layers):
+        layers.append(DecodeLayer(cfg, l, torch, cf, dev))
+        layers[-1].plan(mla, slots, torch, dev)
+        log(f"layer {l}: rows {layers[-1].kv_len} chunk {layers[-1].chunk} splits {sum(layers[-1].n_splits)}")
+    rows = len(layers[0].kv_len)
+
+    def step():
+        for ly in layers:
+            ly.step(mla)
+
+    ms_step, _ = time_graph(torch, step, args.steps, args.warmup)
+    cache_bytes = sum(ly.cache_bytes for ly in layers)
+    log(f"step {ms_step:.3f} ms  ({cache_bytes / 1e6:.0f} MB of cache per step)")
+
+    # dominant kernel: latent attention, events around each eager launch
+    ms_attn = time_launches(torch, [(lambda ly=ly: ly.attn(mla)) for ly in layers], max(args.steps // 2, 3))
+    per_launch_bytes = cache_bytes / len(layers)
+    achieved = per_launch_bytes / (ms_attn * 1e-3) / 1e9
+    log(f"attention {ms_attn * 1e3:.1f} us/launch  {achieved:.0f} GB/s")
+
+    result = {
+        "metric": "MLA decode rows*layers/s and achieved latent-cache HBM GB/s (% of peak)",
+        "value": rows * len(layers) / (ms_step * 1e-3),
+        "unit": "rows*layers/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, fan-in scaled weights)",
+        "config": {
+            "workload": "ragged_bf16 decode: B=8, H=64, qk_nope=128, qk_rope=64, v_head=128, kv_lora_rank=512, "
+                        "lengths U{1024..32768}, 1 query token, bf16 cache, fp32 accumulate",
+            "layers": len(layers), "rows": rows, "cache_MB_per_step": cache_bytes / 1e6,
+            "step_GBps_cache": cache_bytes / (ms_step * 1e-3) / 1e9,
+            "chain": "rope -> absorb_q -> latent_attn -> combine -> absorb_v per layer, HIP graph",
+        },
+        "roofline": {
+            "kernel": "mla_decode_latent_attn (decode_mfma_kernel)",
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+            "per_launch_bytes": per_launch_bytes, "launch_us": ms_attn * 1e3,
+        },
+    }
+
+    # ------------------------------------------------------------- extras
+    if not args.no_extra:
+        extra = {}
+        # dense workload, 64 layer instances: chained (one graph) and stacked (one launch, 64 rows)
+        dcfg = cf.DENSE_BF16
+        n_dense = 64
+        dl = [DecodeLayer(dcfg, l, torch, cf, dev) for l in range(n_dense)]
+        for ly in dl:
+            ly.plan(mla, slots, torch, dev)
+        ms_d, _ = time_graph(torch, lambda: [ly.step(mla) for ly in dl], args.steps, args.warmup)
+        extra["dense_chained"] = {"layers": n_dense, "ms_per_step": ms_d,
+                                  "rows_layers_per_s": n_dense / (ms_d * 1e-3),
+                                  "cache_GBps": sum(ly.cache_bytes for ly in dl) / (ms_d * 1e-3) / 1e9}
+        stacked = torch.cat([ly.cache for ly in dl], dim=0)          # [64, 4096, 576]
+        q_lat = torch.cat([ly.q_lat for ly in dl], dim=0)
+        q_rope = torch.cat([ly.q_rope for ly in dl], dim=0)
+        lens = [dcfg.tokens] * n_dense
+        chunk = mla.plan_chunk_len(lens, slots)
+        ns = [mla.split_count(n, chunk) for n in lens]
+        po = torch.empty((n_dense, dcfg.heads, max(ns), dcfg.kv_lora_rank), dtype=torch.float32, device=dev)
+        pl = torch.empty((n_dense, dcfg.heads, max(ns)), dtype=torch.float32, device=dev)
+        ms_s = time_launches(torch, [lambda: mla.mla_decode_latent_attn(
+            q_lat, q_rope, stacked[..., :512], stacked[..., 512:], lens, dcfg.softmax_scale, chunk, part_o=po,
+            part_lse=pl, s_max=max(ns))], args.steps)
+        sb = n_dense * dcfg.tokens * TOKEN_BYTES
+        extra["dense_stacked_attn"] = {"rows": n_dense, "chunk": chunk, "launch_us": ms_s * 1e3,
+                                       "cache_GBps": sb / (ms_s * 1e-3) / 1e9,
+                                       "frac_hbm": sb / (ms_s * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del dl, stacked, q_lat, q_rope, po, pl
+        torch.cuda.empty_cache()
+        # DSA workload, 8 layer instances (each 131072-token cache, 2048 selected)
+        scfg = cf.DSA_BF16
+        sl = [DecodeLayer(scfg, l, torch, cf, dev) for l in range(args.layers)]
+        for ly in sl:
+            ly.plan(mla, slots, torch, dev)
+        ms_dsa, _ = time_graph(torch, lambda: [ly.step(mla) for ly in sl], args.steps, args.warmup)
+        ms_dsa_attn = time_launches(torch, [(lambda ly=ly: ly.attn(mla)) for ly in sl], max(args.steps // 2, 3))
+        gb = scfg.selected * TOKEN_BYTES
+        extra["dsa_chained"] = {"layers": len(sl), "ms_per_step": ms_dsa,
+                                "rows_layers_per_s": len(sl) / (ms_dsa * 1e-3),
+                                "attn_launch_us": ms_dsa_attn * 1e3,
+                                "gathered_GBps": gb / (ms_dsa_attn * 1e-3) / 1e9}
+        del sl
+        torch.cuda.empty_cache()
+        # reconstructed causal prefill, 4096 tokens
+        pcfg = cf.PREFILL_BF16
+        import numpy as np
+        pin = cf.prefill_inputs(pcfg)
+        t = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        c_q, w_qb, latent, w_kvb = t(pin.c_q), t(pin.w_qb), t(pin.latent), t(pin.w_kvb)
+        rope = t(pin.k_rope_raw)
+        mla.mla_rope_partial_interleaved(rope, 0, pcfg.qk_rope, pcfg.theta, out=rope)
+        need = mla.prefill_workspace_bytes(torch.bfloat16, 1, pcfg.tokens, pcfg.keys, pcfg.heads, pcfg.q_lora_rank,
+                                           pcfg.kv_lora_rank, pcfg.qk_nope, pcfg.qk_rope, pcfg.v_head)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        ctx = torch.empty((1, pcfg.tokens, pcfg.heads * pcfg.v_head), dtype=torch.float32, device=dev)
+        run = lambda: mla.mla_prefill_reconstructed(c_q, w_qb, latent, rope, w_kvb, pcfg.heads, pcfg.qk_nope,
+                                                    pcfg.qk_rope, pcfg.v_head, [0], pcfg.theta, workspace=ws,
+                                                    ctx=ctx)
+        ms_p = time_launches(torch, [run], 3)
+        tt, kk, h = pcfg.tokens, pcfg.keys, pcfg.heads
+        flops = (2 * tt * pcfg.q_lora_rank * h * (pcfg.qk_nope + pcfg.qk_rope)
+                 + 2 * kk * pcfg.kv_lora_rank * h * (pcfg.qk_nope + pcfg.v_head)
+                 + 2 * h * (tt * (tt + 1) // 2) * (pcfg.qk_nope + pcfg.qk_rope + pcfg.v_head))
+        extra["prefill"] = {"tokens": tt, "ms": ms_p, "algorithmic_GFLOP": flops / 1e9,
+                            "TFLOPs": flops / (ms_p * 1e-3) / 1e12,
+                            "frac_bf16_mfma": flops / (ms_p * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
+        del c_q, w_qb, latent, w_kvb, rope, ws, ctx
+        torch.cuda.empty_cache()
+        result["extra"] = extra
+
+    if args.copy_calibration:
+        a = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    if not args.no_cpu_baseline:
+        import oracle
+        log("cpu baseline: oracle")
+        result["cpu_baseline"] = cpu_baseline(cf, oracle, layers[0])
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

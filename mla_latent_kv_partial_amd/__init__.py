@@ -20,6 +20,7 @@ from ._lib import (EXPORTS, LIB_PATH, MLA_DTYPE_BF16, MLA_DTYPE_F32, MlaError, c
 __all__ = [
     "MlaError", "LIB_PATH", "EXPORTS", "mla_rope_partial_interleaved", "mla_absorb_q", "mla_decode_latent_attn",
     "mla_decode_combine", "mla_absorb_v", "mla_prefill_reconstructed", "mla_version", "split_count",
+    "plan_chunk_len", "prefill_workspace_bytes",
 ]
 
 
@@ -69,6 +70,21 @@ def mla_version() -> int:
 
 def split_count(n_attended: int, chunk_len: int) -> int:
     return -(-int(n_attended) // int(chunk_len))
+
+
+def plan_chunk_len(n_attended, slots: int, tile: int = 32) -> int:
+    """Smallest multiple of `tile` whose split count over all rows fits `slots`
+    concurrent workgroups (the decode kernel runs one workgroup per CU), so the
+    launch finishes in one round.  Host-side scheduling only."""
+    n = [int(v) for v in n_attended]
+    total = sum(n)
+    if not n or total == 0:
+        return tile
+    chunk = max(tile, -(-total // max(slots - len(n), 1)))
+    chunk = -(-chunk // tile) * tile
+    while sum(split_count(v, chunk) for v in n) > slots and chunk < max(n):
+        chunk += tile
+    return chunk
 
 
 def mla_rope_partial_interleaved(x: torch.Tensor, position_offset, rotary_dims: int, theta: float,
