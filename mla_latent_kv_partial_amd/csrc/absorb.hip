@@ -5,11 +5,12 @@
 //   absorb_q:  q_lat[b,h,:] = q_nope[b,h,:] . W_UK[h]        ([dn] x [dn,r])
 //   absorb_v:  ctx[b,h*dv+v] = o_lat[b,h,:] . W_UV[h][v,:]    ([r] x [r,dv])
 //
-// Both are weight-streaming products at decode batch sizes: every weight
-// element is read once per launch and used for all batch rows.  absorb_q
-// walks W_UK row by row (coalesced along r) and keeps up to kRowsQ batch rows
-// of accumulators per thread; absorb_v gives each wave one output feature and
-// reduces along r.
+// These are the generic kernels (fp32 weights and geometries outside the
+// MFMA kernels' limits); bf16 weights of the usual geometry go to the MFMA
+// kernels.  Every weight element is read once per launch and used for all
+// batch rows: absorb_q walks W_UK row by row (coalesced along r) with up to
+// kRowsQ batch rows of accumulators per thread; absorb_v gives each wave one
+// output feature and reduces along r.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -60,8 +61,14 @@ __global__ __launch_bounds__(256) void absorb_v_kernel(AbsorbVParams p) {
 
 }  // namespace
 
+bool absorb_q_mfma_ok(const AbsorbQParams& p);
+bool absorb_v_mfma_ok(const AbsorbVParams& p);
+hipError_t launch_absorb_q_mfma(const AbsorbQParams& p, hipStream_t stream);
+hipError_t launch_absorb_v_mfma(const AbsorbVParams& p, hipStream_t stream);
+
 hipError_t launch_absorb_q(int32_t dtype, const AbsorbQParams& p, hipStream_t stream) {
   if (p.batch == 0) return hipSuccess;
+  if (dtype == kBF16 && absorb_q_mfma_ok(p)) return launch_absorb_q_mfma(p, stream);
   dim3 grid((p.r + 255) / 256, p.heads, (p.batch + kRowsQ - 1) / kRowsQ);
   if (dtype == kBF16)
     hipLaunchKernelGGL(absorb_q_kernel<uint16_t>, grid, dim3(256), 0, stream, p);
@@ -72,6 +79,7 @@ hipError_t launch_absorb_q(int32_t dtype, const AbsorbQParams& p, hipStream_t st
 
 hipError_t launch_absorb_v(int32_t dtype, const AbsorbVParams& p, hipStream_t stream) {
   if (p.batch == 0) return hipSuccess;
+  if (dtype == kBF16 && absorb_v_mfma_ok(p)) return launch_absorb_v_mfma(p, stream);
   const int outs = p.heads * p.dv;
   dim3 grid((outs + 3) / 4);
   if (dtype == kBF16)

@@ -1,0 +1,160 @@
+// MFMA weight absorption for bf16 weights (page "mlx-bun 0.0.11 -> 0.0.13",
+// glm52-mla.ts, Glm52Mla.attendAbsorbed: W_UK[h] = kv_b rows [h(dn+dv),
+// h(dn+dv)+dn), W_UV[h] = the next dv rows; q_lat = q_nope . W_UK,
+// ctx = o_lat . W_UV^T).  Both are weight-streaming contractions at decode
+// batch sizes: every weight byte is read once and reused for all batch rows.
+//
+// absorb_q: workgroup = (128-column block of r, head).  W_UK[h][:, block] is
+//   [dn x 128] with the output columns contiguous and the contraction (d)
+//   strided, so the tile is staged in LDS by global_load_lds_dwordx4 and the
+//   d-packed MFMA operand is read with ds_read_b64_tr_b16.  Chunks of a tile
+//   row are XOR-swizzled (f(d) below) so those reads are bank-conflict free.
+//   q_nope rows (bf16) are the other operand, straight from global memory.
+// absorb_v: workgroup = (32-column block of dv, head).  The contraction runs
+//   along the contiguous latent axis of both o_lat and W_UV, so both operands
+//   load directly; the latent axis is split over the 4 waves and the partial
+//   sums are added in LDS.  o_lat (fp32) enters as a bf16 high part plus a
+//   bf16 residual (two MFMAs), which keeps about 16 bits of its mantissa.
+#include "cdna4.hpp"
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mla {
+namespace {
+
+constexpr int kQCols = 128;     // absorb_q output columns per workgroup
+constexpr int kVCols = 32;      // absorb_v output columns per workgroup
+
+__device__ __forceinline__ int swz(int d) { return ((d & 3) << 1) ^ (((d >> 3) & 1) << 3); }
+
+__shared__ __attribute__((aligned(1024))) char g_wtile[256 * kQCols * 2];   // up to dn = 256 rows
+__shared__ float g_vsum[4][16][kVCols + 1];
+
+__global__ __launch_bounds__(256) void absorb_q_mfma_kernel(AbsorbQParams p) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c0 = blockIdx.x * kQCols;
+  const int h = blockIdx.y;
+  const int dn = p.dn;
+  const uint16_t* w = static_cast<const uint16_t*>(p.w) + (static_cast<int64_t>(h) * (dn + p.dv)) * p.r + c0;
+  // ---- stage W_UK[h][0..dn)[c0 .. c0+128): position k = 16 d + s holds chunk s ^ swz(d)
+  const int copies = dn * 16 / 64;          // 1 KB each
+  const uint32_t dst = lds_addr(g_wtile);
+  for (int n = wave; n < copies; n += 4) {
+    const int k = 64 * n + lane;
+    const int d = k >> 4, s = k & 15;
+    dma16(w + static_cast<int64_t>(d) * p.r + 8 * (s ^ swz(d)), dst + n * 1024);
+  }
+  wait_vm<0>();
+  lds_barrier();
+  // ---- wave: output columns c0 + 32 wave + (0..31), two 16-column blocks
+  const int m = lane & 15, g = lane >> 4;
+  const uint16_t* q = static_cast<const uint16_t*>(p.q);
+  for (int b0 = 0; b0 < p.batch; b0 += 16) {
+    f32x4 acc[2] = {};
+    const int b = b0 + m;
+    for (int ks = 0; ks < dn / 32; ++ks) {
+      bf16x8 a;
+      if (b < p.batch)
+        a = *reinterpret_cast<const bf16x8*>(q + b * p.q_sb + h * p.q_sh + 32 * ks + 8 * g);
+      else
+        a = bf16x8{};
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int cc = (32 * wave + 16 * nb) / 8 + ((m & 3) >> 1);
+        const int r1 = 32 * ks + 8 * g + (m >> 2);
+        const int r2 = r1 + 4;
+        const char* t = g_wtile;
+        const s16x4 v1 = lds_read_tr16(t + r1 * 256 + ((cc ^ swz(r1)) << 4) + (m & 1) * 8);
+        const s16x4 v2 = lds_read_tr16(t + r2 * 256 + ((cc ^ swz(r2)) << 4) + (m & 1) * 8);
+        const s16x8 bv = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[nb] = mfma16x16x32(a, __builtin_bit_cast(bf16x8, bv), acc[nb]);
+      }
+    }
+    // acc[nb] lane (column m, group g): rows b0 + 4g + i
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int bb = b0 + 4 * g + i;
+        if (bb < p.batch)
+          p.q_lat[(static_cast<int64_t>(bb) * p.heads + h) * p.r + c0 + 32 * wave + 16 * nb + m] = acc[nb][i];
+      }
+  }
+}
+
+__global__ __launch_bounds__(256) void absorb_v_mfma_kernel(AbsorbVParams p) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int v0 = blockIdx.x * kVCols;
+  const int h = blockIdx.y;
+  const int m = lane & 15, g = lane >> 4;
+  const int kq = p.r / 4;                   // latent range of this wave
+  const uint16_t* w = static_cast<const uint16_t*>(p.w) +
+                      (static_cast<int64_t>(h) * (p.dn + p.dv) + p.dn + v0) * p.r + wave * kq;
+  for (int b0 = 0; b0 < p.batch; b0 += 16) {
+    const int b = b0 + m;
+    const float* o = p.o_lat + (static_cast<int64_t>(b) * p.heads + h) * p.r + wave * kq;
+    f32x4 acc[2] = {};
+    for (int ks = 0; ks < kq / 32; ++ks) {
+      bf16x8 hi = bf16x8{}, lo = bf16x8{};
+      if (b < p.batch) {
+        const float4 u = *reinterpret_cast<const float4*>(o + 32 * ks + 8 * g);
+        const float4 v = *reinterpret_cast<const float4*>(o + 32 * ks + 8 * g + 4);
+        hi = to_bf16x8(u, v);
+        const float4 ru = make_float4(u.x - static_cast<float>(hi[0]), u.y - static_cast<float>(hi[1]),
+                                      u.z - static_cast<float>(hi[2]), u.w - static_cast<float>(hi[3]));
+        const float4 rv = make_float4(v.x - static_cast<float>(hi[4]), v.y - static_cast<float>(hi[5]),
+                                      v.z - static_cast<float>(hi[6]), v.w - static_cast<float>(hi[7]));
+        lo = to_bf16x8(ru, rv);
+      }
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        // B[k = latent 32ks + 8g .. +8][n = value column 16nb + m]
+        const bf16x8 bw = *reinterpret_cast<const bf16x8*>(w + static_cast<int64_t>(16 * nb + m) * p.r + 32 * ks + 8 * g);
+        acc[nb] = mfma16x16x32(hi, bw, acc[nb]);
+        acc[nb] = mfma16x16x32(lo, bw, acc[nb]);
+      }
+    }
+    // partial sums of this wave: lane (column m, group g) holds rows 4g + i
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) g_vsum[wave][4 * g + i][16 * nb + m] = acc[nb][i];
+    __syncthreads();
+    for (int e = threadIdx.x; e < 16 * kVCols; e += 256) {
+      const int row = e / kVCols, col = e % kVCols;
+      const int bb = b0 + row;
+      if (bb < p.batch) {
+        const float sum = g_vsum[0][row][col] + g_vsum[1][row][col] + g_vsum[2][row][col] + g_vsum[3][row][col];
+        p.ctx[static_cast<int64_t>(bb) * p.heads * p.dv + static_cast<int64_t>(h) * p.dv + v0 + col] = sum;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+bool absorb_q_mfma_ok(const AbsorbQParams& p) {
+  auto al = [](const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15) == 0; };
+  return p.dn % 32 == 0 && p.dn <= 256 && p.r % kQCols == 0 && p.q_sb % 8 == 0 && p.q_sh % 8 == 0 && al(p.q) &&
+         al(p.w) && p.heads <= 65535;
+}
+
+bool absorb_v_mfma_ok(const AbsorbVParams& p) {
+  auto al = [](const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15) == 0; };
+  return p.dv % kVCols == 0 && p.r % 128 == 0 && p.dn % 8 == 0 && al(p.o_lat) && al(p.w) && p.heads <= 65535;
+}
+
+hipError_t launch_absorb_q_mfma(const AbsorbQParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(absorb_q_mfma_kernel, dim3(p.r / kQCols, p.heads), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_absorb_v_mfma(const AbsorbVParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(absorb_v_mfma_kernel, dim3(p.dv / kVCols, p.heads), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace mla

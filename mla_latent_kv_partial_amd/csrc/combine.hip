@@ -3,8 +3,9 @@
 // attendAbsorbed).  For row b, head h over its n_b splits:
 //   LSE = ln sum_s exp(lse_s),  o = sum_s exp(lse_s - LSE) o_s.
 // One workgroup per (head, row): the split weights are formed once in LDS,
-// then each thread owns latent features and streams the partials, which are
-// contiguous per (b, h).
+// then each thread owns four consecutive latent features (one 16-byte load per
+// split) and streams the partials, which are contiguous per (b, h), with
+// several independent loads in flight.
 #include <math.h>
 
 #include "common.hpp"
@@ -13,8 +14,13 @@
 namespace mla {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kMaxSplitsLds = 2048;
+constexpr int kThreads = 128;
+constexpr int kMaxSplitsLds = 4096;
+constexpr int kUnroll = 4;
+
+__device__ __forceinline__ float split_weight(float v, float m) {
+  return (m == -INFINITY || v == -INFINITY) ? 0.f : expf(v - m);
+}
 
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
   const int h = blockIdx.x, b = blockIdx.y;
@@ -31,26 +37,51 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
   m = block_reduce(m, MaxOp(), red);
   float part = 0.f;
   for (int s = tid; s < n; s += kThreads) {
-    const float v = lse_in[s];
-    const float w = (m == -INFINITY || v == -INFINITY) ? 0.f : expf(v - m);
+    const float w = split_weight(lse_in[s], m);
     if (s < kMaxSplitsLds) w_s[s] = w;
     part += w;
   }
   const float tot = block_reduce(part, SumOp(), red);   // publishes w_s
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
-  for (int c = tid; c < p.r; c += kThreads) {
-    float acc = 0.f;
-    for (int s = 0; s < n; ++s) {
-      float w;
-      if (s < kMaxSplitsLds) {
-        w = w_s[s];
-      } else {
-        const float v = lse_in[s];
-        w = (m == -INFINITY || v == -INFINITY) ? 0.f : expf(v - m);
+  const bool vec = (p.r & 3) == 0 && (reinterpret_cast<uintptr_t>(po) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(p.o_lat + bh * p.r) & 15) == 0 && n <= kMaxSplitsLds;
+  if (vec) {
+    for (int c = 4 * tid; c < p.r; c += 4 * kThreads) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      int s = 0;
+      for (; s + kUnroll <= n; s += kUnroll) {
+        float4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) v[u] = *reinterpret_cast<const float4*>(po + static_cast<int64_t>(s + u) * p.r + c);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const float w = w_s[s + u];
+          if (w != 0.f) {   // a split with no valid token holds o = 0, lse = -inf
+            acc.x = fmaf(w, v[u].x, acc.x); acc.y = fmaf(w, v[u].y, acc.y);
+            acc.z = fmaf(w, v[u].z, acc.z); acc.w = fmaf(w, v[u].w, acc.w);
+          }
+        }
       }
-      if (w != 0.f) acc = fmaf(w, po[static_cast<int64_t>(s) * p.r + c], acc);
+      for (; s < n; ++s) {
+        const float w = w_s[s];
+        if (w != 0.f) {
+          const float4 v = *reinterpret_cast<const float4*>(po + static_cast<int64_t>(s) * p.r + c);
+          acc.x = fmaf(w, v.x, acc.x); acc.y = fmaf(w, v.y, acc.y);
+          acc.z = fmaf(w, v.z, acc.z); acc.w = fmaf(w, v.w, acc.w);
+        }
+      }
+      *reinterpret_cast<float4*>(p.o_lat + bh * p.r + c) =
+          make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
     }
-    p.o_lat[bh * p.r + c] = acc * inv;
+  } else {
+    for (int c = tid; c < p.r; c += kThreads) {
+      float acc = 0.f;
+      for (int s = 0; s < n; ++s) {
+        const float w = s < kMaxSplitsLds ? w_s[s] : split_weight(lse_in[s], m);
+        if (w != 0.f) acc = fmaf(w, po[static_cast<int64_t>(s) * p.r + c], acc);
+      }
+      p.o_lat[bh * p.r + c] = acc * inv;
+    }
   }
   if (p.lse && tid == 0) p.lse[bh] = tot > 0.f ? m + logf(tot) : -INFINITY;
 }

@@ -33,17 +33,12 @@
 // per-lane base plus an immediate.
 #include <math.h>
 
+#include "cdna4.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace mla {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kR = 512;
 constexpr int kDR = 64;
@@ -71,38 +66,6 @@ __device__ __forceinline__ int sigma(int m) {
   return 2 * j + 8 * (g & 1) + (g >> 1);
 }
 
-// The tile pipeline is driven by hand: the HBM -> LDS copies, the waits on
-// them and the workgroup barrier are issued as instructions whose ordering the
-// compiler keeps ("memory" clobbers) but does not try to track, so the number
-// of copies in flight is exactly what the code below states.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
-}
-
-// Each lane copies 16 bytes from `src` to lds + 16 * lane (lds is wave-uniform).
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
-}
-
-// Same, from the wave-uniform base `sbase` plus a per-lane 32-bit byte offset.
-__device__ __forceinline__ void dma16_off(const void* sbase, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(sbase), "s"(lds)
-               : "memory", "m0");
-}
-
-// Each active lane copies 4 bytes from `src` to lds + 4 * lane.
-__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
-}
-
-// Wait until at most N vector-memory operations of this wave are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
-
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -128,7 +91,7 @@ struct Decode {
   const char* rope_base;
   int64_t lat_st, rope_st;      // bytes
   float scale_log2;
-  int dma_row[kMaxDma];         // token row of this lane's chunk in copy i
+  int dma_src[kMaxDma];         // bpermute address (4 x token row) of this lane's chunk in copy i
   int dma_off[kMaxDma];         // byte offset of the chunk in its latent row, or rope row (sign bit set)
   uint32_t qk_base, tr_base;    // per-lane LDS byte offsets of the fragment reads within a stage
   // Score waves: reg[0..17] hold the Q operands (bf16 bits).  Context waves:
@@ -139,12 +102,17 @@ struct Decode {
 
   __device__ __forceinline__ Decode(const DecodeParams& prm) : p(prm) {}
 
-  // Row slot and validity of tile token `lane` (lanes < 32) from its index into the valid slice.
+  // Row slot and validity of tile token `lane` (lanes < 32) from its index
+  // into the valid slice.  Only the score waves use the validity mask and
+  // flag out-of-range indices.
+  template <bool SC>
   __device__ __forceinline__ int slot_of(int tile, int idx, uint32_t& m) {
     const bool in = lane < kNT && tile * kNT + lane < n_tok;
     const bool ok = in && idx >= 0 && idx < len;
-    bad_index |= in && !ok;
-    m = static_cast<uint32_t>(__ballot(ok));
+    if (SC) {
+      bad_index |= in && !ok;
+      m = static_cast<uint32_t>(__ballot(ok));
+    }
     return ok ? pad + idx : p.width - 1;   // masked tokens read a valid row, weighted by zero
   }
 
@@ -153,14 +121,15 @@ struct Decode {
   __device__ __forceinline__ static char* stage(int s) { return g_stage + s * kStageBytes; }
   __device__ __forceinline__ static int* idx_area(int s) { return reinterpret_cast<int*>(stage(s) + kTileBytes); }
 
-  __device__ __forceinline__ void copy(int i, int slot_v, uint32_t dst) const {
-    const int slot = __shfl(slot_v, dma_row[i], kWave);
+  // row_v: lane t < 32 holds token t's row, as a byte offset from lat_base
+  // (PACKED) or as a row slot.
+  __device__ __forceinline__ void copy(int i, int row_v, uint32_t dst) const {
+    const int v = __builtin_amdgcn_ds_bpermute(dma_src[i], row_v);
     const int off = dma_off[i];
     if (PACKED) {
-      dma16_off(lat_base, static_cast<uint32_t>(slot) * static_cast<uint32_t>(lat_st) + static_cast<uint32_t>(off),
-                dst + (wave + kWaves * i) * 1024);
+      dma16_off(lat_base, static_cast<uint32_t>(v) + static_cast<uint32_t>(off), dst + (wave + kWaves * i) * 1024);
     } else {
-      const char* src = off >= 0 ? lat_base + slot * lat_st + off : rope_base + slot * rope_st + (off & 0x7fff);
+      const char* src = off >= 0 ? lat_base + v * lat_st + off : rope_base + v * rope_st + (off & 0x7fff);
       dma16(src, dst + (wave + kWaves * i) * 1024);
     }
   }
@@ -168,9 +137,10 @@ struct Decode {
   // Copy one tile into stage s.  slot_v: lane t < 32 holds token t's row slot.
   __device__ __forceinline__ void issue_tile(int s, int slot_v) const {
     const uint32_t dst = lds_addr(stage(s));
+    const int row_v = PACKED ? static_cast<int>(static_cast<uint32_t>(slot_v) * static_cast<uint32_t>(lat_st)) : slot_v;
 #pragma unroll
-    for (int i = 0; i < kMaxDma - 1; ++i) copy(i, slot_v, dst);   // every wave has these
-    if (n_dma == kMaxDma) copy(kMaxDma - 1, slot_v, dst);
+    for (int i = 0; i < kMaxDma - 1; ++i) copy(i, row_v, dst);   // every wave has these
+    if (n_dma == kMaxDma) copy(kMaxDma - 1, row_v, dst);
   }
 
   // Gathered rows: copy the 32 selection indices of a tile (clamped inside the
@@ -269,6 +239,19 @@ struct Decode {
     }
   }
 
+  // Score waves: the queries as bf16 MFMA operands in reg[0..17].
+  __device__ __forceinline__ void convert_queries(const float4* qraw, const short (*qrraw)[8]) {
+#pragma unroll
+    for (int ks = 0; ks < kR / 32; ++ks) reg[ks] = __builtin_bit_cast(f32x4, to_bf16x8(qraw[2 * ks], qraw[2 * ks + 1]));
+#pragma unroll
+    for (int ks = 0; ks < kDR / 32; ++ks) {
+      s16x8 q;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q[e] = qrraw[ks][e];
+      reg[kR / 32 + ks] = __builtin_bit_cast(f32x4, q);
+    }
+  }
+
   __device__ __forceinline__ void run(int b, int s) {
     // ---- per-lane copy plan (the same for every tile): copy i of this wave
     // moves stage chunk k = 64 (wave + kWaves i) + lane, which is chunk c of
@@ -280,7 +263,7 @@ struct Decode {
       int row = k / kRowChunks;
       const int c = k - row * kRowChunks;
       row = min(row, kNT - 1);   // the tail of the last copy lands past the rows; it reads a valid token
-      dma_row[i] = row;
+      dma_src[i] = 4 * row;
       if (PACKED)
         dma_off[i] = c < 72 ? c * 16 : 0;   // rope follows the latent in the packed row
       else
@@ -289,13 +272,26 @@ struct Decode {
     // ---- per-lane LDS fragment bases
     qk_base = sigma(h) * kRowBytes + g * 16;
     tr_base = sigma(4 * g + (h >> 2)) * kRowBytes + ((h & 3) >> 1) * 16 + (h & 1) * 8;
+    // The two roles run separate copies of the pipeline, so each is register
+    // allocated on its own (the score waves never hold the accumulators).
+    if (scorer)
+      pipeline<true>(b, s);
+    else
+      pipeline<false>(b, s);
+    if (GATHER && bad_index && p.dev_err) atomicOr(p.dev_err, 1);
+  }
 
+  template <bool SC>
+  __device__ __forceinline__ void pipeline(int b, int s) {
     // ---- prologue.  Issue order: query loads (score waves), then the copies
     // of tiles 0 and 1 (and the indices of tile 2); converting the queries then
-    // waits once for all of them, so the latencies overlap.
+    // waits once for all of them, so the latencies overlap.  A launch with
+    // gathered rows first needs the indices of tiles 0 and 1 to address their
+    // copies; it converts the queries as soon as those indices are in, which
+    // costs no extra latency.
     float4 qraw[2 * (kR / 32)];
     short qrraw[kDR / 32][8];
-    if (scorer) {
+    if (SC) {
       const float* ql = p.q_lat + (static_cast<int64_t>(b) * p.heads + head) * kR;
 #pragma unroll
       for (int ks = 0; ks < kR / 32; ++ks) {
@@ -308,51 +304,34 @@ struct Decode {
 #pragma unroll
         for (int e = 0; e < 8; ++e) qrraw[ks][e] = static_cast<short>(qr[8 * g + 32 * ks + e]);
     }
+    int idx0v, idx1v;
+    if (GATHER && gather_row) {
+      idx0v = lane < kNT ? p.sel[sel_base + min(lane, n_tok - 1)] : 0;
+      idx1v = lane < kNT ? p.sel[sel_base + min(kNT + lane, n_tok - 1)] : 0;
+    } else {
+      idx0v = dense_index(0);
+      idx1v = dense_index(1);
+    }
+    if (SC && GATHER) convert_queries(qraw, qrraw);
     {
-      int idx0v, idx1v;
-      if (GATHER && gather_row) {
-        idx0v = lane < kNT ? p.sel[sel_base + min(lane, n_tok - 1)] : 0;
-        idx1v = lane < kNT ? p.sel[sel_base + min(kNT + lane, n_tok - 1)] : 0;
-      } else {
-        idx0v = dense_index(0);
-        idx1v = dense_index(1);
-      }
-      const int slot0 = slot_of(0, idx0v, mask0);
+      const int slot0 = slot_of<SC>(0, idx0v, mask0);
       issue_tile(0, slot0);
       if (GATHER && gather_row && nt > 2) issue_idx(2, 2);
       // Tile 1 is copied even for single-tile splits (all of its tokens are
       // then masked and read a valid row), which keeps the wait counts fixed.
-      const int slot1 = slot_of(1, idx1v, mask1);
+      const int slot1 = slot_of<SC>(1, idx1v, mask1);
       issue_tile(1, slot1);
     }
-    if (scorer) {
-#pragma unroll
-      for (int ks = 0; ks < kR / 32; ++ks) {
-        const float4 u = qraw[2 * ks], v = qraw[2 * ks + 1];
-        bf16x8 q;
-        q[0] = static_cast<__bf16>(u.x); q[1] = static_cast<__bf16>(u.y);
-        q[2] = static_cast<__bf16>(u.z); q[3] = static_cast<__bf16>(u.w);
-        q[4] = static_cast<__bf16>(v.x); q[5] = static_cast<__bf16>(v.y);
-        q[6] = static_cast<__bf16>(v.z); q[7] = static_cast<__bf16>(v.w);
-        reg[ks] = __builtin_bit_cast(f32x4, q);
-      }
-#pragma unroll
-      for (int ks = 0; ks < kDR / 32; ++ks) {
-        s16x8 q;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) q[e] = qrraw[ks][e];
-        reg[kR / 32 + ks] = __builtin_bit_cast(f32x4, q);
-      }
-#pragma unroll
-      for (int k = kQSteps; k < kDimBlocks; ++k) reg[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-    } else {
+    if (SC && !GATHER) convert_queries(qraw, qrraw);
+    if (!SC) {
 #pragma unroll
       for (int db = 0; db < kDimBlocks; ++db) reg[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     // Materialise the registers ahead of the pipeline's first copy issue
     // (volatile asm statements keep their relative order).
+    constexpr int kLive = SC ? kQSteps : kDimBlocks;
 #pragma unroll
-    for (int k = 0; k < kDimBlocks; ++k) asm volatile("" : "+v"(reg[k]));
+    for (int k = 0; k < kLive; ++k) asm volatile("" : "+v"(reg[k]));
     m_run = -INFINITY;
     l_run = 0.f;
 
@@ -360,7 +339,7 @@ struct Decode {
     // i - 1; tile i + 2 is requested at its start.
     for (int i = 0; i <= nt; ++i) {
       if (i < nt) wait_tile(i + 1 < nt || i == 0);
-      barrier();
+      lds_barrier();
       if (i + 2 < nt) {
         int idx;
         if (GATHER && gather_row) {
@@ -369,21 +348,21 @@ struct Decode {
         } else {
           idx = dense_index(i + 2);
         }
-        const int slot = slot_of(i + 2, idx, mask2);
+        const int slot = slot_of<SC>(i + 2, idx, mask2);
         issue_tile((i + 2) % kStages, slot);
       }
-      if (scorer) {
+      if (SC) {
         if (i < nt) score(i % kStages, i & 1, mask0);
+        mask0 = mask1;
+        mask1 = mask2;
       } else if (i >= 1) {
         context((i - 1) % kStages, (i - 1) & 1);
       }
-      mask0 = mask1;
-      mask1 = mask2;
     }
 
     // ---- normalise and store the split's partials
     const int64_t ps = (static_cast<int64_t>(b) * p.heads + head) * p.s_max + s;
-    if (scorer) {
+    if (SC) {
       float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
       l_tot += __shfl_xor(l_tot, 32, kWave);
       if (g == 0) {
@@ -391,8 +370,8 @@ struct Decode {
         p.part_lse[ps] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
       }
     }
-    barrier();
-    if (!scorer) {
+    lds_barrier();
+    if (!SC) {
       const float l_tot = g_l[hw][h];
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
       float* out = p.part_o + ps * kR + 4 * g;
@@ -402,7 +381,6 @@ struct Decode {
         *reinterpret_cast<float4*>(out + 16 * db) = make_float4(v[0], v[1], v[2], v[3]);
       }
     }
-    if (GATHER && bad_index && p.dev_err) atomicOr(p.dev_err, 1);
   }
 };
 

@@ -1,0 +1,47 @@
+"""ISA checks of the hand-pipelined kernels (compiled here for gfx950, no GPU).
+
+The HBM -> LDS copies set m0 in inline assembly; that is only sound if the
+compiler itself never keeps a value in m0 in those kernels.  Also checks that
+the kernels fit their register budgets without spilling.
+"""
+
+import os
+import re
+import subprocess
+
+import pytest
+
+from mla_latent_kv_partial_amd import build as B
+
+SRC = ["decode_mfma.hip", "absorb_mfma.hip"]
+
+
+def _asm(name, tmp_path):
+    out = tmp_path / (name + ".s")
+    cmd = [B.HIPCC, *B.COMMON, "-x", "hip", "-S", "--cuda-device-only", os.path.join(B.CSRC, name), "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    return out.read_text()
+
+
+@pytest.mark.parametrize("name", SRC)
+def test_m0_only_set_by_the_copy_sequences(name, tmp_path):
+    text = _asm(name, tmp_path)
+    lines = [ln.strip() for ln in text.splitlines() if re.search(r"\bm0\b", ln) and not ln.strip().startswith(";")]
+    assert lines, "expected the copy sequences to set m0"
+    others = [ln for ln in lines if not ln.startswith("s_mov_b32 m0,")]
+    assert not others, f"compiler-generated uses of m0: {others[:5]}"
+    # every m0 write is immediately followed by an LDS copy
+    body = [ln.strip() for ln in text.splitlines()]
+    for i, ln in enumerate(body):
+        if ln.startswith("s_mov_b32 m0,"):
+            assert body[i + 1].startswith("global_load_lds_dword"), body[i + 1]
+
+
+@pytest.mark.parametrize("name", SRC)
+def test_no_spills(name, tmp_path):
+    text = _asm(name, tmp_path)
+    spills = [int(v) for v in re.findall(r"\.vgpr_spill_count:\s+(\d+)", text)]
+    names = re.findall(r"\.name:\s+(\S+)", text)
+    hot = [s for n, s in zip(names, spills) if "ILi4E" in n or "absorb" in n]
+    assert hot and max(hot) == 0, list(zip(names, spills))
