@@ -53,7 +53,7 @@ _SIGNATURES = {
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"libmla.so not found at {LIB_PATH}: build it with `python -m mla_latent_kv_partial_amd.build` "
+            f"libmla.so not found at {LIB_PATH}: build it with `python mla_latent_kv_partial_amd/build.py` "
             "(there is no non-HIP fallback)")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in _SIGNATURES.items():

@@ -1,6 +1,8 @@
 """Build libmla.so (HIP, gfx950) in-tree.
 
-    python -m mla_latent_kv_partial_amd.build [-v]
+    python mla_latent_kv_partial_amd/build.py [-v]
+
+(run as a script: importing the package loads the library this builds)
 
 Every .hip / .cpp under csrc/ is compiled by hipcc for gfx950 into
 _build/*.o, then linked into mla_latent_kv_partial_amd/libmla.so.

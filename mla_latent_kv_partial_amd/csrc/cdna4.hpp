@@ -67,9 +67,25 @@ __device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding.
+// Loads (register or LDS destination) complete in issue order, so this also
+// waits for every load issued before the N most recent ones.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// wait_vm with a wave-uniform count; counts above MAX wait for MAX.
+template <int MAX>
+__device__ __forceinline__ void wait_vm_upto(int n) {
+  if constexpr (MAX > 0) {
+    if (n >= MAX) {
+      wait_vm<MAX>();
+      return;
+    }
+    wait_vm_upto<MAX - 1>(n);
+  } else {
+    wait_vm<0>();
+  }
 }
 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }

@@ -14,7 +14,10 @@
 //     rescale factors to the context waves through LDS;
 //   * context waves (w >= NW) hold the fp32 context accumulators and, one tile
 //     behind, compute O^T[dim, head] += V^T . P^T with V^T fragments read from
-//     the token-major tile by ds_read_b64_tr_b16.
+//     the token-major tile by ds_read_b64_tr_b16.  Context wave c owns the
+//     latent dims [512c/NW, 512(c+1)/NW) for all heads of the workgroup, so
+//     each V^T fragment is read from LDS once and feeds NW MFMAs (LDS read
+//     bandwidth, not HBM, is the per-CU limit of this loop).
 // Splitting the two halves keeps each wave under 256 registers, so two waves
 // share each SIMD and hide each other's LDS and MFMA latencies.
 //
@@ -80,9 +83,12 @@ struct Decode {
   // Wave v issues tile copies n = v, v + kWaves, ... below kDmaPerTile:
   // kMaxDma or kMaxDma - 1 of them.
   static constexpr int kMaxDma = (kDmaPerTile + kWaves - 1) / kWaves;
+  // Context waves: dim blocks per wave; reg[db * NW + hb] holds dims
+  // 16 (c kCtxBlocks + db) + 4 g + (0..3) of head 16 hb + h.
+  static constexpr int kCtxBlocks = kDimBlocks / NW;
 
   const DecodeParams& p;
-  int lane, wave, hw, h, g, head;
+  int lane, wave, hw, h, g, head, head0;   // hw: head group (score) / dim slice (context)
   bool scorer;
   int n_tok, nt, len, pad, sel_base, n_dma;
   bool gather_row;              // this row reads its tokens through the selection list
@@ -95,7 +101,7 @@ struct Decode {
   int dma_off[kMaxDma];         // byte offset of the chunk in its latent row, or rope row (sign bit set)
   uint32_t qk_base, tr_base;    // per-lane LDS byte offsets of the fragment reads within a stage
   // Score waves: reg[0..17] hold the Q operands (bf16 bits).  Context waves:
-  // reg[db] accumulates O^T for dims 16 db + 4 g + (0..3) of head h.
+  // the O^T accumulators (see kCtxBlocks).
   f32x4 reg[kDimBlocks];
   float m_run, l_run;
   uint32_t mask0, mask1, mask2;  // validity of tiles i, i+1, i+2 (bit t: token t)
@@ -152,18 +158,11 @@ struct Decode {
     }
   }
 
-  // Wait for tile i's copies; with `more`, the copies of tile i+1 (issued one
-  // step ago) may stay in flight.
-  __device__ __forceinline__ void wait_tile(bool more) const {
-    if (more) {
-      if (n_dma == kMaxDma)
-        wait_vm<kMaxDma>();
-      else
-        wait_vm<kMaxDma - 1>();
-    } else {
-      wait_vm<0>();
-    }
-  }
+  // Vector-memory operations this wave issued after the copies of tile i, in
+  // the issue order of pipeline() (prologue: C0 C1, then step j issues
+  // C(j+2); C = the n_dma copies of a tile).  Index copies of gathered rows
+  // are not counted, which only makes a wait stronger.
+  __device__ __forceinline__ int ops_after(int i) const { return i == 0 || i + 1 < nt ? n_dma : 0; }
 
   // Score wave, tile i in stage s: scores, softmax, P and rescale factors out.
   __device__ __forceinline__ void score(int s, int parity, uint32_t valid) {
@@ -221,21 +220,27 @@ struct Decode {
 
   // Context wave, tile i-1 in stage s: rescale if asked, then O^T += V^T . P^T.
   __device__ __forceinline__ void context(int s, int parity) {
-    if (g_moved[parity][hw]) {
-      const float alpha = g_alpha[parity][hw][h];
 #pragma unroll
-      for (int db = 0; db < kDimBlocks; ++db) reg[db] *= alpha;
+    for (int hb = 0; hb < NW; ++hb) {
+      if (g_moved[parity][hb]) {
+        const float alpha = g_alpha[parity][hb][h];
+#pragma unroll
+        for (int db = 0; db < kCtxBlocks; ++db) reg[db * NW + hb] *= alpha;
+      }
     }
-    const bf16x8 pb = *reinterpret_cast<const bf16x8*>(&g_p[parity][hw][lane * 16]);
+    bf16x8 pb[NW];
+#pragma unroll
+    for (int hb = 0; hb < NW; ++hb) pb[hb] = *reinterpret_cast<const bf16x8*>(&g_p[parity][hb][lane * 16]);
     const char* st = stage(s);
 #pragma unroll
-    for (int db = 0; db < kDimBlocks; ++db) {
+    for (int db = 0; db < kCtxBlocks; ++db) {
       lds_s16x4* a1 = (lds_s16x4*)(st + tr_base + db * 32);
       lds_s16x4* a2 = (lds_s16x4*)(st + tr_base + 16 * kRowBytes + db * 32);
       const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(a1);
       const s16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(a2);
-      const s16x8 v = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
-      reg[db] = mfma(__builtin_bit_cast(bf16x8, v), pb, reg[db]);
+      const bf16x8 v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int hb = 0; hb < NW; ++hb) reg[db * NW + hb] = mfma(v, pb[hb], reg[db * NW + hb]);
     }
   }
 
@@ -271,7 +276,7 @@ struct Decode {
     }
     // ---- per-lane LDS fragment bases
     qk_base = sigma(h) * kRowBytes + g * 16;
-    tr_base = sigma(4 * g + (h >> 2)) * kRowBytes + ((h & 3) >> 1) * 16 + (h & 1) * 8;
+    tr_base = sigma(4 * g + (h >> 2)) * kRowBytes + ((h & 3) >> 1) * 16 + (h & 1) * 8 + hw * kCtxBlocks * 32;
     // The two roles run separate copies of the pipeline, so each is register
     // allocated on its own (the score waves never hold the accumulators).
     if (scorer)
@@ -338,7 +343,7 @@ struct Decode {
     // ---- pipeline: step i scores tile i and accumulates the context of tile
     // i - 1; tile i + 2 is requested at its start.
     for (int i = 0; i <= nt; ++i) {
-      if (i < nt) wait_tile(i + 1 < nt || i == 0);
+      if (i < nt) wait_vm_upto<kMaxDma>(ops_after(i));
       lds_barrier();
       if (i + 2 < nt) {
         int idx;
@@ -361,24 +366,28 @@ struct Decode {
     }
 
     // ---- normalise and store the split's partials
-    const int64_t ps = (static_cast<int64_t>(b) * p.heads + head) * p.s_max + s;
     if (SC) {
       float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
       l_tot += __shfl_xor(l_tot, 32, kWave);
       if (g == 0) {
+        const int64_t ps = (static_cast<int64_t>(b) * p.heads + head) * p.s_max + s;
         g_l[hw][h] = l_tot;
         p.part_lse[ps] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
       }
     }
     lds_barrier();
     if (!SC) {
-      const float l_tot = g_l[hw][h];
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      float* out = p.part_o + ps * kR + 4 * g;
 #pragma unroll
-      for (int db = 0; db < kDimBlocks; ++db) {
-        const f32x4 v = reg[db] * inv;
-        *reinterpret_cast<float4*>(out + 16 * db) = make_float4(v[0], v[1], v[2], v[3]);
+      for (int hb = 0; hb < NW; ++hb) {
+        const float l_tot = g_l[hb][h];
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        const int64_t ps = (static_cast<int64_t>(b) * p.heads + head0 + 16 * hb + h) * p.s_max + s;
+        float* out = p.part_o + ps * kR + 16 * kCtxBlocks * hw + 4 * g;
+#pragma unroll
+        for (int db = 0; db < kCtxBlocks; ++db) {
+          const f32x4 v = reg[db * NW + hb] * inv;
+          *reinterpret_cast<float4*>(out + 16 * db) = make_float4(v[0], v[1], v[2], v[3]);
+        }
       }
     }
   }
@@ -386,10 +395,17 @@ struct Decode {
 
 template <int NW, bool GATHER, bool PACKED>
 __global__ __launch_bounds__(2 * NW * kWave) void decode_mfma_kernel(DecodeParams p) {
-  const int s = blockIdx.x, b = blockIdx.y;
+  // blockIdx.x enumerates the (row, split) pairs of the launch row by row;
+  // find the row by bisection of the split prefix table (uniform, scalar).
+  const int wg = blockIdx.x;
+  int b = 0, hi = p.rows;
+  while (hi - b > 1) {
+    const int mid = (b + hi) >> 1;
+    if (p.tab.split_begin[mid] <= wg) b = mid; else hi = mid;
+  }
+  const int s = wg - p.tab.split_begin[b];
   const int n_att = p.tab.n_att[b];
   const int j0 = s * p.chunk;
-  if (j0 >= n_att) return;
   Decode<NW, GATHER, PACKED> d(p);
   d.lane = threadIdx.x & (kWave - 1);
   d.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -397,7 +413,8 @@ __global__ __launch_bounds__(2 * NW * kWave) void decode_mfma_kernel(DecodeParam
   d.hw = d.scorer ? d.wave : d.wave - NW;
   d.h = d.lane & 15;
   d.g = d.lane >> 4;
-  d.head = blockIdx.z * (16 * NW) + d.hw * 16 + d.h;
+  d.head0 = blockIdx.z * (16 * NW);
+  d.head = d.head0 + d.hw * 16 + d.h;
   d.n_tok = min(p.chunk, n_att - j0);
   d.nt = (d.n_tok + kNT - 1) / kNT;
   d.len = p.tab.kv_len[b];
@@ -415,7 +432,11 @@ __global__ __launch_bounds__(2 * NW * kWave) void decode_mfma_kernel(DecodeParam
 
 template <int NW, bool GATHER>
 hipError_t launch_nw(const DecodeParams& p, bool packed, int groups, hipStream_t stream) {
-  dim3 grid(p.s_launch, p.rows, groups);
+  // One workgroup per (row, split) and head group, in a compact 1-D order:
+  // with at most one workgroup per CU in flight, consecutive ids land on the
+  // XCDs in turn, so a launch of S <= #CU splits never queues a second round
+  // on one XCD.
+  dim3 grid(p.s_total, 1, groups);
   if (packed)
     hipLaunchKernelGGL((decode_mfma_kernel<NW, GATHER, true>), grid, dim3(2 * NW * kWave), 0, stream, p);
   else
@@ -438,7 +459,7 @@ bool decode_mfma_layout_ok(const void* q_lat, const void* latent, int64_t lat_sb
 }
 
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
-  if (p.rows == 0 || p.s_launch == 0) return hipSuccess;
+  if (p.rows == 0 || p.s_total == 0) return hipSuccess;
   bool gather = false;
   for (int i = 0; i < p.rows; ++i) gather |= p.tab.sel_off[i] >= 0;
   const int nw = p.heads >= 64 ? 4 : p.heads / 16;

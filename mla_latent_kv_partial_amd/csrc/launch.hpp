@@ -56,6 +56,7 @@ struct DecodeRows {
   int32_t kv_len[kDecodeRowsPerLaunch];
   int32_t n_att[kDecodeRowsPerLaunch];   // attended count
   int32_t sel_off[kDecodeRowsPerLaunch]; // -1: dense row, else offset into sel
+  int32_t split_begin[kDecodeRowsPerLaunch + 1];   // prefix sum of the rows' split counts
 };
 
 struct DecodeParams {
@@ -72,6 +73,7 @@ struct DecodeParams {
   int32_t* dev_err;
   int32_t rows, heads, r, dr, width;
   int32_t chunk, s_max, s_launch;        // s_launch = max splits over the launch rows
+  int32_t s_total;                       // splits of all launch rows (= split_begin[rows])
   float scale;
   DecodeRows tab;
 };

@@ -215,6 +215,7 @@ int mla_decode_latent_attn(int32_t dtype, const float* q_lat, const void* q_rope
   for (int b0 = 0; b0 < batch; b0 += mla::kDecodeRowsPerLaunch) {
     p.rows = std::min(batch - b0, mla::kDecodeRowsPerLaunch);
     p.s_launch = 0;
+    p.tab.split_begin[0] = 0;
     for (int i = 0; i < p.rows; ++i) {
       const int b = b0 + i;
       const bool sel = sel_count && sel_count[b] > 0;
@@ -222,8 +223,11 @@ int mla_decode_latent_attn(int32_t dtype, const float* q_lat, const void* q_rope
       p.tab.n_att[i] = sel ? sel_count[b] : kv_len[b];
       p.tab.sel_off[i] = sel ? sel_off : -1;
       if (sel) sel_off += sel_count[b];
-      p.s_launch = std::max(p.s_launch, (p.tab.n_att[i] + chunk_len - 1) / chunk_len);
+      const int splits = (p.tab.n_att[i] + chunk_len - 1) / chunk_len;
+      p.s_launch = std::max(p.s_launch, splits);
+      p.tab.split_begin[i + 1] = p.tab.split_begin[i] + splits;
     }
+    p.s_total = p.tab.split_begin[p.rows];
     p.q_lat = q_lat + static_cast<int64_t>(b0) * heads * kv_lora_rank;
     p.q_rope = advance(q_rope, b0 * qr_stride_b, dtype);
     p.latent = advance(latent, b0 * latent_stride_b, dtype);

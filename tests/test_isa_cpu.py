@@ -11,7 +11,9 @@ import subprocess
 
 import pytest
 
-from mla_latent_kv_partial_amd import build as B
+from conftest import build_module
+
+B = build_module()
 
 SRC = ["decode_mfma.hip", "absorb_mfma.hip"]
 
