@@ -79,8 +79,8 @@ class DecodeLayer:
         self.n_att = [c if self.sel_count is not None and c > 0 else n
                       for n, c in zip(self.kv_len, self.sel_count or [-1] * b)]
         self.q_rope = torch.empty_like(self.q_rope_raw)
-        self.q_lat = torch.empty((b, cfg.heads, cfg.kv_lora_rank), dtype=torch.float32, device=dev)
-        self.o_lat = torch.empty_like(self.q_lat)
+        self.q_lat = torch.empty((b, cfg.heads, cfg.kv_lora_rank), dtype=self.cache.dtype, device=dev)
+        self.o_lat = torch.empty((b, cfg.heads, cfg.kv_lora_rank), dtype=torch.float32, device=dev)
         self.lse = torch.empty((b, cfg.heads), dtype=torch.float32, device=dev)
         self.ctx = torch.empty((b, cfg.heads * cfg.v_head), dtype=torch.float32, device=dev)
         self.cfg = cfg

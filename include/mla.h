@@ -23,8 +23,10 @@
  *   - Element strides are in elements, not bytes; the innermost (feature)
  *     stride is always 1.
  *   - dtype: MLA_DTYPE_F32 or MLA_DTYPE_BF16 names the storage type of the
- *     activations, cache and weights an entry reads.  Accumulation is always
- *     fp32; q_lat, partials, o_lat, lse and ctx are always fp32.
+ *     activations, cache and weights an entry reads, and of the absorbed query
+ *     q_lat (the bf16 path rounds its fp32 accumulation to nearest even once;
+ *     the MFMA score operand is bf16 either way).  Accumulation is always
+ *     fp32; partials, o_lat, lse and ctx are always fp32.
  *   - Errors: arguments are checked on the host before anything is enqueued,
  *     as the pages throw synchronously.  A failed check returns a negative
  *     mla_status and enqueues nothing; mla_last_error() then returns a
@@ -102,10 +104,10 @@ int mla_rope_partial_interleaved(int32_t dtype, const void* x, void* y,
  *
  * q_nope: [batch, heads, qk_nope] of `dtype`, strides (q_stride_b, q_stride_h, 1).
  * w_kv_b: [heads*(qk_nope+v_head), kv_lora_rank] of `dtype`, row-major, contiguous.
- * q_lat:  [batch, heads, kv_lora_rank] fp32, contiguous.
+ * q_lat:  [batch, heads, kv_lora_rank] of `dtype`, contiguous.
  */
 int mla_absorb_q(int32_t dtype, const void* q_nope, int64_t q_stride_b, int64_t q_stride_h,
-                 const void* w_kv_b, float* q_lat,
+                 const void* w_kv_b, void* q_lat,
                  int32_t batch, int32_t heads, int32_t qk_nope, int32_t v_head, int32_t kv_lora_rank,
                  hipStream_t stream);
 
@@ -141,7 +143,7 @@ int mla_absorb_q(int32_t dtype, const void* q_nope, int64_t q_stride_b, int64_t 
  * A split whose indices were all skipped stores o = 0 and lse = -inf.
  * Slots s >= n_b are left untouched.
  *
- * q_lat [batch, heads, kv_lora_rank] fp32 contiguous; q_rope [batch, heads,
+ * q_lat [batch, heads, kv_lora_rank] of `dtype`, contiguous; q_rope [batch, heads,
  * rope_dim] of `dtype`, strides (qr_stride_b, qr_stride_h, 1), already rotated.
  * kv_len [host] int32[batch], each in [1, width] (MLA_ERR_SHAPE otherwise).
  * sel_count [host] int32[batch] or NULL.  sel_idx device int32 (may be NULL
@@ -149,7 +151,7 @@ int mla_absorb_q(int32_t dtype, const void* q_nope, int64_t q_stride_b, int64_t 
  * part_lse [batch, heads, s_max] fp32; s_max >= max_b n_b (MLA_ERR_SHAPE).
  * Limits (MLA_ERR_UNSUPPORTED): kv_lora_rank <= 1024, rope_dim <= 256.
  */
-int mla_decode_latent_attn(int32_t dtype, const float* q_lat,
+int mla_decode_latent_attn(int32_t dtype, const void* q_lat,
                            const void* q_rope, int64_t qr_stride_b, int64_t qr_stride_h,
                            const void* latent, int64_t latent_stride_b, int64_t latent_stride_t,
                            const void* rope, int64_t rope_stride_b, int64_t rope_stride_t,

@@ -128,7 +128,7 @@ def mla_rope_partial_interleaved(x: torch.Tensor, position_offset, rotary_dims: 
 
 def mla_absorb_q(q_nope: torch.Tensor, w_kv_b: torch.Tensor, v_head: int,
                  q_lat: torch.Tensor | None = None) -> torch.Tensor:
-    """q_nope [B,H,dn] (strided, last stride 1), w_kv_b [H*(dn+dv), r] -> q_lat fp32 [B,H,r]."""
+    """q_nope [B,H,dn] (strided, last stride 1), w_kv_b [H*(dn+dv), r] -> q_lat [B,H,r] of q_nope's dtype."""
     b, h, dn = q_nope.shape
     r = w_kv_b.shape[1]
     if q_nope.dtype != w_kv_b.dtype:
@@ -136,7 +136,9 @@ def mla_absorb_q(q_nope: torch.Tensor, w_kv_b: torch.Tensor, v_head: int,
     if q_nope.stride(2) != 1 or not w_kv_b.is_contiguous():
         raise ValueError("q_nope needs feature stride 1 and w_kv_b must be contiguous")
     if q_lat is None:
-        q_lat = torch.empty((b, h, r), dtype=torch.float32, device=q_nope.device)
+        q_lat = torch.empty((b, h, r), dtype=q_nope.dtype, device=q_nope.device)
+    if q_lat.dtype != q_nope.dtype or not q_lat.is_contiguous() or tuple(q_lat.shape) != (b, h, r):
+        raise ValueError("q_lat must be a contiguous [B,H,r] tensor of q_nope's dtype")
     check(lib.mla_absorb_q(_dtype_code(q_nope), _ptr(q_nope), q_nope.stride(0), q_nope.stride(1), _ptr(w_kv_b),
                            _ptr(q_lat), b, h, dn, int(v_head), r, _stream(q_nope)), "mla_absorb_q")
     return q_lat
@@ -170,6 +172,8 @@ def mla_decode_latent_attn(q_lat: torch.Tensor, q_rope: torch.Tensor, latent: to
         raise TypeError("sel_idx must be int32")
     if latent.stride(2) != 1 or rope.stride(2) != 1 or q_rope.stride(2) != 1:
         raise ValueError("feature axes must have stride 1")
+    if q_lat.dtype != latent.dtype or not q_lat.is_contiguous():
+        raise ValueError("q_lat must be contiguous and share the cache dtype")
     check(lib.mla_decode_latent_attn(
         _dtype_code(latent), _ptr(q_lat), _ptr(q_rope), q_rope.stride(0), q_rope.stride(1),
         _ptr(latent), latent.stride(0), latent.stride(1), _ptr(rope), rope.stride(0), rope.stride(1),

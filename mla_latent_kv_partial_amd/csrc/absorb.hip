@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(AbsorbQParams p) {
   }
 #pragma unroll
   for (int j = 0; j < kRowsQ; ++j)
-    if (j < nb) p.q_lat[(static_cast<int64_t>(b0 + j) * p.heads + h) * p.r + c] = acc[j];
+    if (j < nb) st(static_cast<T*>(p.q_lat) + (static_cast<int64_t>(b0 + j) * p.heads + h) * p.r + c, acc[j]);
 }
 
 template <typename T>

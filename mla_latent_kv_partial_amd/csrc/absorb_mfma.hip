@@ -9,7 +9,8 @@
 //   strided, so the tile is staged in LDS by global_load_lds_dwordx4 and the
 //   d-packed MFMA operand is read with ds_read_b64_tr_b16.  Chunks of a tile
 //   row are XOR-swizzled (f(d) below) so those reads are bank-conflict free.
-//   q_nope rows (bf16) are the other operand, straight from global memory.
+//   q_nope rows (bf16) are the other operand, straight from global memory;
+//   q_lat is stored in bf16 (round to nearest even).
 // absorb_v: workgroup = (32-column block of dv, head).  The contraction runs
 //   along the contiguous latent axis of both o_lat and W_UV, so both operands
 //   load directly; the latent axis is split over the 4 waves and the partial
@@ -78,7 +79,8 @@ __global__ __launch_bounds__(256) void absorb_q_mfma_kernel(AbsorbQParams p) {
       for (int i = 0; i < 4; ++i) {
         const int bb = b0 + 4 * g + i;
         if (bb < p.batch)
-          p.q_lat[(static_cast<int64_t>(bb) * p.heads + h) * p.r + c0 + 32 * wave + 16 * nb + m] = acc[nb][i];
+          static_cast<uint16_t*>(p.q_lat)[(static_cast<int64_t>(bb) * p.heads + h) * p.r + c0 + 32 * wave + 16 * nb + m] =
+              f32_to_bf16(acc[nb][i]);
       }
   }
 }

@@ -38,9 +38,9 @@ __global__ __launch_bounds__(kTile) void decode_generic_kernel(DecodeParams p) {
   __shared__ int slot_s[kTile];
   __shared__ float red[kTile / kWave];
 
-  const float* ql = p.q_lat + (static_cast<int64_t>(b) * p.heads + h) * p.r;
+  const T* ql = static_cast<const T*>(p.q_lat) + (static_cast<int64_t>(b) * p.heads + h) * p.r;
   const T* qr = static_cast<const T*>(p.q_rope) + b * p.qr_sb + h * p.qr_sh;
-  for (int c = tid; c < p.r; c += kTile) q_s[c] = ql[c];
+  for (int c = tid; c < p.r; c += kTile) q_s[c] = ld(ql + c);
   for (int c = tid; c < p.dr; c += kTile) qr_s[c] = ld(qr + c);
   __syncthreads();
 

@@ -244,10 +244,10 @@ struct Decode {
     }
   }
 
-  // Score waves: the queries as bf16 MFMA operands in reg[0..17].
-  __device__ __forceinline__ void convert_queries(const float4* qraw, const short (*qrraw)[8]) {
+  // Score waves: the queries (bf16) as MFMA operands in reg[0..17].
+  __device__ __forceinline__ void convert_queries(const f32x4* qraw, const short (*qrraw)[8]) {
 #pragma unroll
-    for (int ks = 0; ks < kR / 32; ++ks) reg[ks] = __builtin_bit_cast(f32x4, to_bf16x8(qraw[2 * ks], qraw[2 * ks + 1]));
+    for (int ks = 0; ks < kR / 32; ++ks) reg[ks] = qraw[ks];
 #pragma unroll
     for (int ks = 0; ks < kDR / 32; ++ks) {
       s16x8 q;
@@ -294,15 +294,12 @@ struct Decode {
     // gathered rows first needs the indices of tiles 0 and 1 to address their
     // copies; it converts the queries as soon as those indices are in, which
     // costs no extra latency.
-    float4 qraw[2 * (kR / 32)];
+    f32x4 qraw[kR / 32];   // 8 bf16 each
     short qrraw[kDR / 32][8];
     if (SC) {
-      const float* ql = p.q_lat + (static_cast<int64_t>(b) * p.heads + head) * kR;
+      const uint16_t* ql = static_cast<const uint16_t*>(p.q_lat) + (static_cast<int64_t>(b) * p.heads + head) * kR;
 #pragma unroll
-      for (int ks = 0; ks < kR / 32; ++ks) {
-        qraw[2 * ks] = *reinterpret_cast<const float4*>(ql + 8 * g + 32 * ks);
-        qraw[2 * ks + 1] = *reinterpret_cast<const float4*>(ql + 8 * g + 32 * ks + 4);
-      }
+      for (int ks = 0; ks < kR / 32; ++ks) qraw[ks] = *reinterpret_cast<const f32x4*>(ql + 8 * g + 32 * ks);
       const uint16_t* qr = static_cast<const uint16_t*>(p.q_rope) + b * p.qr_sb + head * p.qr_sh;
 #pragma unroll
       for (int ks = 0; ks < kDR / 32; ++ks)

@@ -38,7 +38,7 @@ struct AbsorbQParams {
   const void* q;          // [B,H,dn] strided
   int64_t q_sb, q_sh;
   const void* w;          // [H*(dn+dv), r]
-  float* q_lat;           // [B,H,r]
+  void* q_lat;            // [B,H,r] of the dtype
   int32_t batch, heads, dn, dv, r;
 };
 hipError_t launch_absorb_q(int32_t dtype, const AbsorbQParams& p, hipStream_t stream);
@@ -60,7 +60,7 @@ struct DecodeRows {
 };
 
 struct DecodeParams {
-  const float* q_lat;     // [rows,H,r] (already offset to the first row of the launch)
+  const void* q_lat;      // [rows,H,r] of the dtype (already offset to the first row of the launch)
   const void* q_rope;     // strided
   int64_t qr_sb, qr_sh;
   const void* latent;     // strided, first row of the launch

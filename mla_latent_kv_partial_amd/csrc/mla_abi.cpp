@@ -124,7 +124,7 @@ int mla_rope_partial_interleaved(int32_t dtype, const void* x, void* y, int32_t 
 }
 
 int mla_absorb_q(int32_t dtype, const void* q_nope, int64_t q_stride_b, int64_t q_stride_h, const void* w_kv_b,
-                 float* q_lat, int32_t batch, int32_t heads, int32_t qk_nope, int32_t v_head, int32_t kv_lora_rank,
+                 void* q_lat, int32_t batch, int32_t heads, int32_t qk_nope, int32_t v_head, int32_t kv_lora_rank,
                  hipStream_t stream) {
   if (!valid_dtype(dtype)) return fail(MLA_ERR_ARG, "absorb_q: unknown dtype %d", dtype);
   if (batch < 0 || heads < 1 || qk_nope < 1 || v_head < 1 || kv_lora_rank < 1)
@@ -148,7 +148,7 @@ int mla_absorb_v(int32_t dtype, const float* o_lat, const void* w_kv_b, float* c
   return device(mla::launch_absorb_v(dtype, p, stream), "absorb_v launch");
 }
 
-int mla_decode_latent_attn(int32_t dtype, const float* q_lat, const void* q_rope, int64_t qr_stride_b,
+int mla_decode_latent_attn(int32_t dtype, const void* q_lat, const void* q_rope, int64_t qr_stride_b,
                            int64_t qr_stride_h, const void* latent, int64_t latent_stride_b, int64_t latent_stride_t,
                            const void* rope, int64_t rope_stride_b, int64_t rope_stride_t, int32_t batch,
                            int32_t heads, int32_t kv_lora_rank, int32_t rope_dim, int32_t width,
@@ -228,7 +228,7 @@ int mla_decode_latent_attn(int32_t dtype, const float* q_lat, const void* q_rope
       p.tab.split_begin[i + 1] = p.tab.split_begin[i] + splits;
     }
     p.s_total = p.tab.split_begin[p.rows];
-    p.q_lat = q_lat + static_cast<int64_t>(b0) * heads * kv_lora_rank;
+    p.q_lat = advance(q_lat, static_cast<int64_t>(b0) * heads * kv_lora_rank, dtype);
     p.q_rope = advance(q_rope, b0 * qr_stride_b, dtype);
     p.latent = advance(latent, b0 * latent_stride_b, dtype);
     p.rope = advance(rope, b0 * rope_stride_b, dtype);

@@ -10,6 +10,7 @@ import torch
 
 import oracle
 from synth import configs as cf
+from synth import generators as gen
 from tests.gpu_util import TOL, assert_close, bitwise_equal, dev, host_values, say
 
 pytestmark = pytest.mark.gpu
@@ -102,16 +103,20 @@ def _small_ragged(lengths=(700, 1, 333), seed_layer=5):
 
 @pytest.mark.parametrize("chunk", [1, 7, 64, 100, 256, 1024])
 def test_partials_match_oracle(chunk):
+    """The attention kernel alone: seeded latent-space and rotated queries go to
+    both sides unchanged, so the partials of every split are compared directly."""
     inp = _small_ragged(lengths=(40, 1, 9) if chunk == 1 else (700, 1, 333), seed_layer=7)
-    step = Step(inp, packed=False)
-    got = step.run(chunk)
     c = inp.cfg
-    q_lat = host_values(got["q_lat"])
-    q_rope = host_values(got["q_rope"])
-    po, pl, ns = oracle.latent_attention_partials(q_lat, q_rope, cf.values(inp.latent), cf.values(inp.rope),
-                                                  inp.kv_len, None, c.softmax_scale, chunk)
-    assert list(ns) == got["n_splits"]
-    gpo, gpl = host_values(got["part_o"]), host_values(got["part_lse"])
+    b = len(inp.kv_len)
+    ql = cf.store(gen.normal_f32(c.config_id, gen.T_MISC, (b, c.heads, c.kv_lora_rank), layer=100 + chunk), c.dtype)
+    qr = cf.store(gen.normal_f32(c.config_id, gen.T_MISC, (b, c.heads, c.qk_rope), layer=200 + chunk), c.dtype)
+    got_o, got_l, got_ns = _mla().mla_decode_latent_attn(dev(ql), dev(qr), dev(inp.latent), dev(inp.rope), inp.kv_len,
+                                                         c.softmax_scale, chunk)
+    torch.cuda.synchronize()
+    po, pl, ns = oracle.latent_attention_partials(cf.values(ql), cf.values(qr), cf.values(inp.latent),
+                                                  cf.values(inp.rope), inp.kv_len, None, c.softmax_scale, chunk)
+    assert list(ns) == got_ns
+    gpo, gpl = host_values(got_o), host_values(got_l)
     for b in range(len(ns)):
         n = int(ns[b])
         assert_close(gpo[b, :, :n], po[b, :, :n], c.dtype, f"part_o row {b}")
