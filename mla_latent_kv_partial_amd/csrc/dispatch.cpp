@@ -1,4 +1,4 @@
-// Kernel selection between the generic VALU kernels and the MFMA kernels of
+// Kernel selection between the generic VALU prefill and the MFMA prefill of
 // the bf16 GLM geometry.
 #include "launch.hpp"
 
@@ -6,9 +6,16 @@ namespace mla {
 
 size_t prefill_generic_workspace_bytes(const PrefillParams& p);
 hipError_t launch_prefill_generic(const PrefillParams& p, hipStream_t stream);
+bool prefill_mfma_supported(const PrefillParams& p);
+size_t prefill_mfma_workspace_bytes(const PrefillParams& p);
+hipError_t launch_prefill_mfma(const PrefillParams& p, hipStream_t stream);
 
-size_t prefill_workspace_bytes(const PrefillParams& p) { return prefill_generic_workspace_bytes(p); }
+size_t prefill_workspace_bytes(const PrefillParams& p) {
+  return prefill_mfma_supported(p) ? prefill_mfma_workspace_bytes(p) : prefill_generic_workspace_bytes(p);
+}
 
-hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) { return launch_prefill_generic(p, stream); }
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
+  return prefill_mfma_supported(p) ? launch_prefill_mfma(p, stream) : launch_prefill_generic(p, stream);
+}
 
 }  // namespace mla

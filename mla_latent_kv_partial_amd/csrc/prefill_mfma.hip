@@ -1,0 +1,471 @@
+// MFMA reconstructed causal prefill for the bf16 GLM geometry (qk_nope 128,
+// qk_rope 64, v_head 128).  Page "mlx-bun 0.0.11 -> 0.0.13", glm52-mla.ts:
+// Glm52Mla.project (q = q_b_proj(c_q), split into q_nope and q_rope, RoPE of
+// q_rope at offset + t) and Glm52Mla.attendReconstructed (kv_b_proj expansion
+// of the latent into per-head k_nope and v, scores over [q_nope|q_rope] .
+// [k_nope|rope], causal mask, softmax, P.V); page "mlx-bun 0.2.0 -> 0.4.0",
+// glm52-mla.ts: keys before the row's left pad are masked.
+//
+// Three kernels over a bf16 workspace:
+//   gemm_nt_mfma_kernel<true>   Q  [rows*T, H*192] = c_q . w_q_b^T, with the
+//                               RoPE of each head's last 64 columns applied to
+//                               the fp32 accumulators before rounding;
+//   gemm_nt_mfma_kernel<false>  KV [rows*K, H*256] = latent . w_kv_b^T (per head
+//                               k_nope then v);
+//   flash_attn_kernel           one workgroup per (head, 128 queries): causal
+//                               online-softmax attention, K/V tiles of 32 keys
+//                               streamed through LDS, fp32 context out.
+// Both contractions run on v_mfma_f32_16x16x32_bf16.  Operand tiles move
+// HBM -> LDS with global_load_lds_dwordx4 into rows padded to an odd number of
+// 16-byte chunks, so the fragment reads of 16 consecutive rows are free of
+// bank conflicts.
+#include <math.h>
+
+#include "cdna4.hpp"
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mla {
+
+bool prefill_mfma_supported(const PrefillParams& p);
+size_t prefill_mfma_workspace_bytes(const PrefillParams& p);
+hipError_t launch_prefill_mfma(const PrefillParams& p, hipStream_t stream);
+
+namespace {
+
+constexpr int kDn = 128, kDr = 64, kDv = 128;
+constexpr int kQk = kDn + kDr;          // 192
+constexpr int kKvw = kDn + kDv;         // 256
+constexpr int kBatchPerLaunch = 128;    // per-row tables travel in the kernel arguments
+
+// ------------------------------------------------------------------ NT GEMM
+// C[m, n] = sum_k A[m, k] B[n, k]: both operands K-contiguous, bf16; fp32
+// accumulation; bf16 result (round to nearest even).  Workgroup tile 128 x 128,
+// K step 64, 4 waves of 64 x 64 (4 x 4 MFMA blocks), 3-stage LDS ring filled
+// two K steps ahead.
+constexpr int kGT = 128;
+constexpr int kGK = 64;
+constexpr int kGRowChunks = kGK / 8 + 1;            // eight data chunks + one pad
+constexpr int kGRowBytes = kGRowChunks * 16;        // 144
+constexpr int kGOpChunks = kGT * kGRowChunks;       // 1152 per operand tile
+constexpr int kGOpDma = kGOpChunks / 64;            // 18 copies of 1 KB
+constexpr int kGOpBytes = kGOpChunks * 16;
+constexpr int kGStageBytes = 2 * kGOpBytes;         // A tile then B tile
+constexpr int kGStages = 3;
+constexpr int kGMaxDma = (kGOpDma + 3) / 4;         // copies per wave per operand (5 or 4)
+
+__shared__ __attribute__((aligned(1024))) char g_gemm[kGStages * kGStageBytes];
+
+struct GemmNT {
+  const uint16_t* a;
+  int64_t lda;
+  const uint16_t* b;
+  int64_t ldb;
+  uint16_t* c;
+  int64_t ldc;
+  int32_t m, n, k;
+  int32_t m_tiles, n_tiles;
+  // RoPE epilogue: row m is token m % tokens of batch row m / tokens; columns
+  // d = n % 192 >= 128 of a head hold its interleaved rope pairs.
+  int32_t tokens;
+  int64_t off[kBatchPerLaunch];
+  float inv[kDr / 2];
+};
+
+template <bool ROPE>
+__global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(GemmNT p) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Tile order: workgroup ids go round-robin over the 8 XCDs; give each XCD
+  // a contiguous run of tiles, M fastest, so the workgroups that share an
+  // XCD's L2 also share B tiles.
+  const int tiles = p.m_tiles * p.n_tiles;
+  const int per_xcd = (tiles + 7) / 8;
+  int tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (tiles % 8 != 0) tile = blockIdx.x;   // uneven split: plain order
+  const int m0 = (tile % p.m_tiles) * kGT;
+  const int n0 = (tile / p.m_tiles) * kGT;
+
+  // copy plan: copy j of this wave moves chunk q = 64 (wave + 4 j) + lane of
+  // an operand tile: row q / 9, chunk q % 9 (chunk 8 is padding and re-reads
+  // chunk 0); rows past the matrix edge re-read its last row.
+  const int n_dma = (kGOpDma - wave + 3) / 4;
+  const uint16_t* asrc[kGMaxDma];
+  const uint16_t* bsrc[kGMaxDma];
+#pragma unroll
+  for (int j = 0; j < kGMaxDma; ++j) {
+    const int q = 64 * (wave + 4 * j) + lane;
+    const int row = q / kGRowChunks;
+    int c = q - row * kGRowChunks;
+    c = c < 8 ? c : 0;
+    asrc[j] = p.a + static_cast<int64_t>(min(m0 + row, p.m - 1)) * p.lda + 8 * c;
+    bsrc[j] = p.b + static_cast<int64_t>(min(n0 + row, p.n - 1)) * p.ldb + 8 * c;
+  }
+  auto issue = [&](int s, int k0) {
+    const uint32_t da = lds_addr(g_gemm + s * kGStageBytes);
+    const uint32_t db = da + kGOpBytes;
+#pragma unroll
+    for (int j = 0; j < kGMaxDma - 1; ++j) {
+      dma16(asrc[j] + k0, da + (wave + 4 * j) * 1024);
+      dma16(bsrc[j] + k0, db + (wave + 4 * j) * 1024);
+    }
+    if (n_dma == kGMaxDma) {
+      dma16(asrc[kGMaxDma - 1] + k0, da + (wave + 4 * (kGMaxDma - 1)) * 1024);
+      dma16(bsrc[kGMaxDma - 1] + k0, db + (wave + 4 * (kGMaxDma - 1)) * 1024);
+    }
+  };
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int i16 = lane & 15, g = lane >> 4;
+  const uint32_t a_frag = (64 * wm + i16) * kGRowBytes + g * 16;
+  const uint32_t b_frag = kGOpBytes + (64 * wn + i16) * kGRowBytes + g * 16;
+
+  const int nk = p.k / kGK;
+  issue(0, 0);
+  if (nk > 1) issue(1, kGK);
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn) acc[bm][bn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int i = 0; i < nk; ++i) {
+    // tile i's copies done; those of tile i + 1 (issued one step ago) may fly
+    if (i + 1 < nk)
+      wait_vm_upto<2 * kGMaxDma>(2 * n_dma);
+    else
+      wait_vm<0>();
+    lds_barrier();
+    if (i + 2 < nk) issue((i + 2) % kGStages, (i + 2) * kGK);
+    const char* st = g_gemm + (i % kGStages) * kGStageBytes;
+#pragma unroll
+    for (int ks = 0; ks < kGK / 32; ++ks) {
+      bf16x8 af[4], bfr[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        af[t] = *reinterpret_cast<const bf16x8*>(st + a_frag + t * 16 * kGRowBytes + ks * 64);
+        bfr[t] = *reinterpret_cast<const bf16x8*>(st + b_frag + t * 16 * kGRowBytes + ks * 64);
+      }
+      // D^T blocks: lane (column m = i16, group g) receives C[m][n + 4g + (0..3)]
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+        for (int bn = 0; bn < 4; ++bn) acc[bm][bn] = mfma16x16x32(bfr[bn], af[bm], acc[bm][bn]);
+    }
+  }
+
+  // ---- epilogue: 4 consecutive columns per lane and block
+#pragma unroll
+  for (int bm = 0; bm < 4; ++bm) {
+    const int m = m0 + 64 * wm + 16 * bm + i16;
+    if (m >= p.m) continue;
+    uint16_t* crow = p.c + static_cast<int64_t>(m) * p.ldc;
+    double pos = 0.0;
+    if (ROPE) pos = static_cast<double>(p.off[m / p.tokens] + m % p.tokens);
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn) {
+      const int n = n0 + 64 * wn + 16 * bn + 4 * g;
+      if (n >= p.n) continue;
+      const f32x4 v = acc[bm][bn];
+      const int d = ROPE ? n % kQk : 0;
+      if (ROPE && d >= kDn) {
+        // pairs (v0, v1) and (v2, v3) are rope pairs q0 and q0 + 1 of the head
+        const int q0 = (d - kDn) >> 1;
+        uint16_t* head = crow + (n - d) + kDn;
+        uint16_t re[2], im[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float ang = static_cast<float>(pos * static_cast<double>(p.inv[q0 + e]));
+          double s, c;
+          sincos(static_cast<double>(ang), &s, &c);
+          const double a = v[2 * e], b = v[2 * e + 1];
+          re[e] = f64_to_bf16(a * c - b * s);
+          im[e] = f64_to_bf16(b * c + a * s);
+        }
+        *reinterpret_cast<uint32_t*>(head + q0) = re[0] | (static_cast<uint32_t>(re[1]) << 16);
+        *reinterpret_cast<uint32_t*>(head + kDr / 2 + q0) = im[0] | (static_cast<uint32_t>(im[1]) << 16);
+      } else {
+        const uint32_t lo = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+        const uint32_t hi = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+        *reinterpret_cast<uint2*>(crow + n) = make_uint2(lo, hi);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ attention
+// Workgroup = (head, 128 consecutive queries, batch row); wave w owns queries
+// 32w .. 32w + 31 as two 16-query blocks.  Per 32-key tile each wave computes
+// S^T[key, query] = K . Q^T (Q in registers, K fragments from LDS), the online
+// softmax in exp2 with a lazily moved reference max, and O^T[dim, query] +=
+// V^T . P^T (V^T fragments by ds_read_b64_tr_b16, each shared by the two
+// query blocks).  The layout tricks are those of the latent decode kernel: key
+// row m of a 16-key block holds key sigma(m), and a key row is 41 chunks
+// (k_nope 16, v 16, rope 8, pad 1), an odd count.
+constexpr int kAQ = 128;
+constexpr int kAK = 32;
+constexpr int kARowChunks = 41;
+constexpr int kARowBytes = kARowChunks * 16;                 // 656
+constexpr int kATileDma = (kAK * kARowChunks + 63) / 64;      // 21
+constexpr int kAStageBytes = kATileDma * 1024;
+constexpr int kAStages = 3;
+constexpr int kAMaxDma = (kATileDma + 3) / 4;                 // 6 (wave 0) or 5
+constexpr float kSlack = 8.f;
+
+__shared__ __attribute__((aligned(1024))) char g_attn[kAStages * kAStageBytes];
+
+struct AttnMfma {
+  const uint16_t* q;      // [rows*T, H*192]
+  const uint16_t* kv;     // [rows*K, H*256]
+  const uint16_t* rope;   // [rows*K, 64]
+  float* ctx;             // [rows*T, H*128]
+  int32_t tokens, keys, heads, q_tiles;
+  float scale_log2;
+  int32_t pad[kBatchPerLaunch];
+};
+
+__device__ __forceinline__ int sigma(int m) {
+  const int g = m >> 2, j = m & 3;
+  return 2 * j + 8 * (g & 1) + (g >> 1);
+}
+
+__global__ __launch_bounds__(256, 2) void flash_attn_kernel(AttnMfma p) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = blockIdx.x;
+  const int qt = p.q_tiles - 1 - static_cast<int>(blockIdx.y);   // heaviest tiles first
+  const int b = blockIdx.z;
+  const int t0 = qt * kAQ;
+  const int P = p.keys - p.tokens;
+  const int pad = p.pad[b];
+  const int m = lane & 15, g = lane >> 4;
+
+  // key tiles: from the left pad (rounded down) through the last key the
+  // workgroup's last query may see
+  const int k_first = (pad / kAK) * kAK;
+  const int k_last = min(p.keys - 1, P + min(t0 + kAQ, p.tokens) - 1);
+  const int nt = k_last >= k_first ? (k_last - k_first) / kAK + 1 : 0;
+
+  // ---- copy plan (same for every tile): chunk q = 64 (wave + 4 j) + lane is
+  // chunk c of key row q / 41; c < 32 from the KV workspace row of head h,
+  // c < 40 from the rope row, c = 40 padding (re-reads chunk 0)
+  const int n_dma = (kATileDma - wave + 3) / 4;
+  int c_row[kAMaxDma];
+  int c_off[kAMaxDma];   // byte offset in the KV head slice, or rope row (sign bit set)
+#pragma unroll
+  for (int j = 0; j < kAMaxDma; ++j) {
+    const int q = 64 * (wave + 4 * j) + lane;
+    const int row = q / kARowChunks;
+    const int c = q - row * kARowChunks;
+    c_row[j] = min(row, kAK - 1);
+    c_off[j] = c < 32 ? c * 16 : (c < 40 ? static_cast<int>(0x80000000u | static_cast<uint32_t>((c - 32) * 16)) : 0);
+  }
+  const char* kv_base = reinterpret_cast<const char*>(p.kv + (static_cast<int64_t>(b) * p.keys * p.heads + h) * kKvw);
+  const char* rope_base = reinterpret_cast<const char*>(p.rope + static_cast<int64_t>(b) * p.keys * kDr);
+  const int64_t kv_stride = static_cast<int64_t>(p.heads) * kKvw * 2;
+  auto copy = [&](int j, int k0, uint32_t dst) {
+    const int key = min(k0 + c_row[j], p.keys - 1);
+    const int off = c_off[j];
+    const char* src = off >= 0 ? kv_base + key * kv_stride + off : rope_base + key * (kDr * 2) + (off & 0x7fff);
+    dma16(src, dst + (wave + 4 * j) * 1024);
+  };
+  auto issue = [&](int s, int tile) {
+    const uint32_t dst = lds_addr(g_attn + s * kAStageBytes);
+    const int k0 = k_first + tile * kAK;
+#pragma unroll
+    for (int j = 0; j < kAMaxDma - 1; ++j) copy(j, k0, dst);
+    if (n_dma == kAMaxDma) copy(kAMaxDma - 1, k0, dst);
+  };
+
+  // ---- queries of this wave: two blocks of 16, B operands of the scores
+  f32x4 qreg[2][kQk / 32];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int t = min(t0 + 32 * wave + 16 * qb + m, p.tokens - 1);
+    const uint16_t* qrow = p.q + (static_cast<int64_t>(b) * p.tokens + t) * p.heads * kQk + h * kQk + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < kQk / 32; ++ks) qreg[qb][ks] = *reinterpret_cast<const f32x4*>(qrow + 32 * ks);
+  }
+  if (nt > 0) issue(0, 0);
+  if (nt > 1) issue(1, 1);
+
+  const uint32_t k_frag = sigma(m) * kARowBytes + g * 16;
+  const uint32_t v_frag = sigma(4 * g + (m >> 2)) * kARowBytes + kDn * 2 + ((m & 3) >> 1) * 16 + (m & 1) * 8;
+  f32x4 o[2][kDv / 16];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int db = 0; db < kDv / 16; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  const int t_lo = t0 + 32 * wave;           // first query of the wave
+  const int t_q[2] = {t_lo + m, t_lo + 16 + m};
+
+  for (int i = 0; i < nt; ++i) {
+    if (i + 1 < nt)
+      wait_vm_upto<kAMaxDma>(n_dma);
+    else
+      wait_vm<0>();
+    lds_barrier();
+    if (i + 2 < nt) issue((i + 2) % kAStages, i + 2);
+    const int k0 = k_first + i * kAK;
+    // tiles past every query of this wave contribute nothing
+    if (k0 > P + t_lo + 31 || k0 + kAK - 1 < pad) continue;
+    const char* st = g_attn + (i % kAStages) * kAStageBytes;
+    f32x4 s[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) s[qb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kQk / 32; ++ks) {
+      const int off = ks < kDn / 32 ? ks * 64 : 2 * kKvw + (ks - kDn / 32) * 64;   // k_nope, then rope
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(st + k_frag + tb * 16 * kARowBytes + off);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          s[qb][tb] = mfma16x16x32(kf, __builtin_bit_cast(bf16x8, qreg[qb][ks]), s[qb][tb]);
+      }
+    }
+    bf16x8 pb[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float x[8];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = k0 + 16 * tb + sigma(4 * g + e);
+          const bool vis = key >= pad && key <= P + t_q[qb];
+          x[4 * tb + e] = vis ? s[qb][tb][e] * p.scale_log2 : -INFINITY;
+        }
+      float mt = x[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mt = fmaxf(mt, x[e]);
+      mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+      const bool move = mt > m_run[qb] + kSlack;
+      if (__any(move)) {
+        const float alpha = move ? __builtin_amdgcn_exp2f(m_run[qb] - mt) : 1.f;
+        if (move) m_run[qb] = mt;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < kDv / 16; ++db) o[qb][db] *= alpha;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pr = m_run[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[e] - m_run[qb]);
+        l_run[qb] += pr;
+        pb[qb][e] = static_cast<__bf16>(pr);
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < kDv / 16; ++db) {
+      const s16x4 v1 = lds_read_tr16(st + v_frag + db * 32);
+      const s16x4 v2 = lds_read_tr16(st + v_frag + 16 * kARowBytes + db * 32);
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) o[qb][db] = mfma16x16x32(vf, pb[qb], o[qb][db]);
+    }
+  }
+
+  // ---- normalise and store: lane (query m, group g) holds dims 16 db + 4 g + (0..3)
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float l = l_run[qb] + __shfl_xor(l_run[qb], 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int t = t_q[qb];
+    if (t >= p.tokens) continue;
+    float* out = p.ctx + (static_cast<int64_t>(b) * p.tokens + t) * p.heads * kDv + h * kDv + 4 * g;
+#pragma unroll
+    for (int db = 0; db < kDv / 16; ++db) {
+      const f32x4 v = o[qb][db] * inv;
+      *reinterpret_cast<float4*>(out + 16 * db) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  }
+}
+
+size_t up256(size_t x) { return (x + 255) / 256 * 256; }
+
+}  // namespace
+
+bool prefill_mfma_supported(const PrefillParams& p) {
+  auto al = [](const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15) == 0; };
+  return p.dtype == kBF16 && p.dn == kDn && p.dr == kDr && p.dv == kDv && p.ql % kGK == 0 && p.r % kGK == 0 &&
+         al(p.q_c) && al(p.w_qb) && al(p.latent) && al(p.rope) && al(p.w_kvb) && al(p.ctx) && p.heads <= 65535;
+}
+
+size_t prefill_mfma_workspace_bytes(const PrefillParams& p) {
+  const size_t q = static_cast<size_t>(p.batch) * p.tokens * p.heads * kQk * 2;
+  const size_t kv = static_cast<size_t>(p.batch) * p.keys * p.heads * kKvw * 2;
+  return up256(q) + up256(kv);
+}
+
+hipError_t launch_prefill_mfma(const PrefillParams& p, hipStream_t stream) {
+  uint16_t* q = static_cast<uint16_t*>(p.workspace);
+  const size_t q_bytes = static_cast<size_t>(p.batch) * p.tokens * p.heads * kQk * 2;
+  uint16_t* kv = reinterpret_cast<uint16_t*>(static_cast<char*>(p.workspace) + up256(q_bytes));
+  const uint16_t* q_c = static_cast<const uint16_t*>(p.q_c);
+  const uint16_t* latent = static_cast<const uint16_t*>(p.latent);
+  const uint16_t* rope = static_cast<const uint16_t*>(p.rope);
+  float inv[kDr / 2];
+  rope_inverse_frequencies(kDr, p.theta, inv);
+  for (int b0 = 0; b0 < p.batch; b0 += kBatchPerLaunch) {
+    const int rows = min(p.batch - b0, kBatchPerLaunch);
+    // Q projection with the RoPE epilogue
+    GemmNT gq{};
+    gq.a = q_c + static_cast<int64_t>(b0) * p.tokens * p.ql;
+    gq.lda = p.ql;
+    gq.b = static_cast<const uint16_t*>(p.w_qb);
+    gq.ldb = p.ql;
+    gq.c = q + static_cast<int64_t>(b0) * p.tokens * p.heads * kQk;
+    gq.ldc = static_cast<int64_t>(p.heads) * kQk;
+    gq.m = rows * p.tokens;
+    gq.n = p.heads * kQk;
+    gq.k = p.ql;
+    gq.m_tiles = (gq.m + kGT - 1) / kGT;
+    gq.n_tiles = (gq.n + kGT - 1) / kGT;
+    gq.tokens = p.tokens;
+    for (int i = 0; i < rows; ++i) gq.off[i] = p.q_offsets[b0 + i];
+    for (int i = 0; i < kDr / 2; ++i) gq.inv[i] = inv[i];
+    hipLaunchKernelGGL(gemm_nt_mfma_kernel<true>, dim3(gq.m_tiles * gq.n_tiles), dim3(256), 0, stream, gq);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // KV expansion
+    GemmNT gk{};
+    gk.a = latent + static_cast<int64_t>(b0) * p.keys * p.r;
+    gk.lda = p.r;
+    gk.b = static_cast<const uint16_t*>(p.w_kvb);
+    gk.ldb = p.r;
+    gk.c = kv + static_cast<int64_t>(b0) * p.keys * p.heads * kKvw;
+    gk.ldc = static_cast<int64_t>(p.heads) * kKvw;
+    gk.m = rows * p.keys;
+    gk.n = p.heads * kKvw;
+    gk.k = p.r;
+    gk.m_tiles = (gk.m + kGT - 1) / kGT;
+    gk.n_tiles = (gk.n + kGT - 1) / kGT;
+    gk.tokens = p.keys;
+    hipLaunchKernelGGL(gemm_nt_mfma_kernel<false>, dim3(gk.m_tiles * gk.n_tiles), dim3(256), 0, stream, gk);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // attention
+    AttnMfma ap{};
+    ap.q = gq.c;
+    ap.kv = gk.c;
+    ap.rope = rope + static_cast<int64_t>(b0) * p.keys * kDr;
+    ap.ctx = p.ctx + static_cast<int64_t>(b0) * p.tokens * p.heads * kDv;
+    ap.tokens = p.tokens;
+    ap.keys = p.keys;
+    ap.heads = p.heads;
+    ap.q_tiles = (p.tokens + kAQ - 1) / kAQ;
+    ap.scale_log2 = p.scale * 1.4426950408889634f;
+    for (int i = 0; i < rows; ++i) ap.pad[i] = p.left_pad ? p.left_pad[b0 + i] : 0;
+    hipLaunchKernelGGL(flash_attn_kernel, dim3(p.heads, ap.q_tiles, rows), dim3(256), 0, stream, ap);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace mla
