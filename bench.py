@@ -15,8 +15,11 @@ K timed replays between synchronisations.
 
 Printed: one JSON line.  value = rows*layers/s of the step.  roofline = the
 latent attention kernel (the dominant kernel): algorithmic cache bytes per
-launch (attended tokens x 1152 B) / its mean launch time, measured with HIP
-events around eager launches on the launch stream.  cpu_baseline = the CPU
+launch (attended tokens x 1152 B) / its mean launch time: the attention
+launches of all layers captured alone in a HIP graph (kernels run back to
+back), HIP events around the replays.  traffic = HBM bytes per launch from the
+FETCH_SIZE / WRITE_SIZE counter runs recorded in the committed profile, only
+while the kernel sources still hash to the recorded digest.  cpu_baseline = the CPU
 oracle's reconstructed decode on a bounded sample of the same rows.  extra =
 the dense (chained and layer-stacked), DSA and prefill workloads.
 """
@@ -51,6 +54,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run only the 4096-token prefill leg (for MFMA counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (for FETCH_SIZE / WRITE_SIZE scaling)")
     return ap.parse_args()
@@ -140,21 +145,33 @@ def time_graph(torch, fn, steps, warmup):
     return e0.elapsed_time(e1) / steps, g
 
 
-def time_launches(torch, fns, reps):
-    """Mean ms per launch of each fn, HIP events around every eager launch on the current stream."""
-    for fn in fns:
-        fn()
-    torch.cuda.synchronize()
-    pairs = []
-    for _ in range(reps):
-        for fn in fns:
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn()
-            b.record()
-            pairs.append((a, b))
-    torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+def kernel_sources_digest(names):
+    """sha256 over the given csrc files, to tie recorded counters to a kernel version."""
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "mla_latent_kv_partial_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+ATTN_SOURCES = ("decode_mfma.hip", "cdna4.hpp", "launch.hpp", "common.hpp")
+ATTN_PROFILE = os.path.join(ROOT, "profiles", "decode_attn_ragged_bf16.md")
+
+
+def recorded_traffic(digest):
+    """HBM bytes per attention launch recorded by the FETCH_SIZE / WRITE_SIZE runs
+    of the committed profile, if they were taken on kernel sources with this digest."""
+    try:
+        with open(ATTN_PROFILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    import re
+    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.]+)\s+sources_sha256:\s*([0-9a-f]+)", text)
+    if not m or m.group(2) != digest:
+        return None
+    return float(m.group(1))
 
 
 def cpu_baseline(cf, oracle, layer0, budget_s=12.0):
@@ -187,6 +204,35 @@ def cpu_baseline(cf, oracle, layer0, budget_s=12.0):
     }
 
 
+def prefill_leg(torch, mla, cf, dev):
+    """The 4096-token reconstructed causal prefill: ms per call and algorithmic TFLOP/s."""
+    pcfg = cf.PREFILL_BF16
+    import numpy as np
+    pin = cf.prefill_inputs(pcfg)
+    t = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    c_q, w_qb, latent, w_kvb = t(pin.c_q), t(pin.w_qb), t(pin.latent), t(pin.w_kvb)
+    rope = t(pin.k_rope_raw)
+    mla.mla_rope_partial_interleaved(rope, 0, pcfg.qk_rope, pcfg.theta, out=rope)
+    need = mla.prefill_workspace_bytes(torch.bfloat16, 1, pcfg.tokens, pcfg.keys, pcfg.heads, pcfg.q_lora_rank,
+                                       pcfg.kv_lora_rank, pcfg.qk_nope, pcfg.qk_rope, pcfg.v_head)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    ctx = torch.empty((1, pcfg.tokens, pcfg.heads * pcfg.v_head), dtype=torch.float32, device=dev)
+    run = lambda: mla.mla_prefill_reconstructed(c_q, w_qb, latent, rope, w_kvb, pcfg.heads, pcfg.qk_nope,
+                                                pcfg.qk_rope, pcfg.v_head, [0], pcfg.theta, workspace=ws,
+                                                ctx=ctx)
+    ms_p = time_graph(torch, run, 3, 1)[0]
+    tt, kk, h = pcfg.tokens, pcfg.keys, pcfg.heads
+    flops = (2 * tt * pcfg.q_lora_rank * h * (pcfg.qk_nope + pcfg.qk_rope)
+             + 2 * kk * pcfg.kv_lora_rank * h * (pcfg.qk_nope + pcfg.v_head)
+             + 2 * h * (tt * (tt + 1) // 2) * (pcfg.qk_nope + pcfg.qk_rope + pcfg.v_head))
+    out = {"tokens": tt, "ms": ms_p, "algorithmic_GFLOP": flops / 1e9,
+           "TFLOPs": flops / (ms_p * 1e-3) / 1e12,
+           "frac_bf16_mfma": flops / (ms_p * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
+    del c_q, w_qb, latent, w_kvb, rope, ws, ctx
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -197,6 +243,9 @@ def main():
     import mla_latent_kv_partial_amd as mla
     from synth import configs as cf
     dev = torch.device("cuda:0")
+    if args.prefill_only:
+        print(json.dumps({"prefill": prefill_leg(torch, mla, cf, dev)}), flush=True)
+        return
     props = torch.cuda.get_device_properties(dev)
     slots = props.multi_processor_count
     log(f"device {props.name} CUs={slots}")
@@ -218,8 +267,9 @@ def main():
     cache_bytes = sum(ly.cache_bytes for ly in layers)
     log(f"step {ms_step:.3f} ms  ({cache_bytes / 1e6:.0f} MB of cache per step)")
 
-    # dominant kernel: latent attention, events around each eager launch
-    ms_attn = time_launches(torch, [(lambda ly=ly: ly.attn(mla)) for ly in layers], max(args.steps // 2, 3))
+    # dominant kernel: latent attention alone, one launch per layer captured in
+    # a graph (back-to-back kernels, no host gaps), events around the replays
+    ms_attn = time_graph(torch, lambda: [ly.attn(mla) for ly in layers], args.steps, args.warmup)[0] / len(layers)
     per_launch_bytes = cache_bytes / len(layers)
     achieved = per_launch_bytes / (ms_attn * 1e-3) / 1e9
     log(f"attention {ms_attn * 1e3:.1f} us/launch  {achieved:.0f} GB/s")
@@ -247,8 +297,9 @@ def main():
         "roofline": {
             "kernel": "mla_decode_latent_attn (decode_mfma_kernel)",
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+            "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(kernel_sources_digest(ATTN_SOURCES)),
             "per_launch_bytes": per_launch_bytes, "launch_us": ms_attn * 1e3,
+            "sources_sha256": kernel_sources_digest(ATTN_SOURCES),
         },
     }
 
@@ -273,9 +324,9 @@ def main():
         ns = [mla.split_count(n, chunk) for n in lens]
         po = torch.empty((n_dense, dcfg.heads, max(ns), dcfg.kv_lora_rank), dtype=torch.float32, device=dev)
         pl = torch.empty((n_dense, dcfg.heads, max(ns)), dtype=torch.float32, device=dev)
-        ms_s = time_launches(torch, [lambda: mla.mla_decode_latent_attn(
+        ms_s = time_graph(torch, lambda: mla.mla_decode_latent_attn(
             q_lat, q_rope, stacked[..., :512], stacked[..., 512:], lens, dcfg.softmax_scale, chunk, part_o=po,
-            part_lse=pl, s_max=max(ns))], args.steps)
+            part_lse=pl, s_max=max(ns)), args.steps, args.warmup)[0]
         sb = n_dense * dcfg.tokens * TOKEN_BYTES
         extra["dense_stacked_attn"] = {"rows": n_dense, "chunk": chunk, "launch_us": ms_s * 1e3,
                                        "cache_GBps": sb / (ms_s * 1e-3) / 1e9,
@@ -288,7 +339,7 @@ def main():
         for ly in sl:
             ly.plan(mla, slots, torch, dev)
         ms_dsa, _ = time_graph(torch, lambda: [ly.step(mla) for ly in sl], args.steps, args.warmup)
-        ms_dsa_attn = time_launches(torch, [(lambda ly=ly: ly.attn(mla)) for ly in sl], max(args.steps // 2, 3))
+        ms_dsa_attn = time_graph(torch, lambda: [ly.attn(mla) for ly in sl], args.steps, args.warmup)[0] / len(sl)
         gb = scfg.selected * TOKEN_BYTES
         extra["dsa_chained"] = {"layers": len(sl), "ms_per_step": ms_dsa,
                                 "rows_layers_per_s": len(sl) / (ms_dsa * 1e-3),
@@ -296,31 +347,7 @@ def main():
                                 "gathered_GBps": gb / (ms_dsa_attn * 1e-3) / 1e9}
         del sl
         torch.cuda.empty_cache()
-        # reconstructed causal prefill, 4096 tokens
-        pcfg = cf.PREFILL_BF16
-        import numpy as np
-        pin = cf.prefill_inputs(pcfg)
-        t = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
-        c_q, w_qb, latent, w_kvb = t(pin.c_q), t(pin.w_qb), t(pin.latent), t(pin.w_kvb)
-        rope = t(pin.k_rope_raw)
-        mla.mla_rope_partial_interleaved(rope, 0, pcfg.qk_rope, pcfg.theta, out=rope)
-        need = mla.prefill_workspace_bytes(torch.bfloat16, 1, pcfg.tokens, pcfg.keys, pcfg.heads, pcfg.q_lora_rank,
-                                           pcfg.kv_lora_rank, pcfg.qk_nope, pcfg.qk_rope, pcfg.v_head)
-        ws = torch.empty(need, dtype=torch.uint8, device=dev)
-        ctx = torch.empty((1, pcfg.tokens, pcfg.heads * pcfg.v_head), dtype=torch.float32, device=dev)
-        run = lambda: mla.mla_prefill_reconstructed(c_q, w_qb, latent, rope, w_kvb, pcfg.heads, pcfg.qk_nope,
-                                                    pcfg.qk_rope, pcfg.v_head, [0], pcfg.theta, workspace=ws,
-                                                    ctx=ctx)
-        ms_p = time_launches(torch, [run], 3)
-        tt, kk, h = pcfg.tokens, pcfg.keys, pcfg.heads
-        flops = (2 * tt * pcfg.q_lora_rank * h * (pcfg.qk_nope + pcfg.qk_rope)
-                 + 2 * kk * pcfg.kv_lora_rank * h * (pcfg.qk_nope + pcfg.v_head)
-                 + 2 * h * (tt * (tt + 1) // 2) * (pcfg.qk_nope + pcfg.qk_rope + pcfg.v_head))
-        extra["prefill"] = {"tokens": tt, "ms": ms_p, "algorithmic_GFLOP": flops / 1e9,
-                            "TFLOPs": flops / (ms_p * 1e-3) / 1e12,
-                            "frac_bf16_mfma": flops / (ms_p * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
-        del c_q, w_qb, latent, w_kvb, rope, ws, ctx
-        torch.cuda.empty_cache()
+        extra["prefill"] = prefill_leg(torch, mla, cf, dev)
         result["extra"] = extra
 
     if args.copy_calibration:
