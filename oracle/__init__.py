@@ -5,3 +5,4 @@ benchmark's CPU-baseline leg, never by the product path.
 """
 from .mla_oracle import *  # noqa: F401,F403
 from .mla_oracle import OracleError  # noqa: F401
+from .dsa_oracle import dsa_rank_keys, dsa_select, dsa_select_rows  # noqa: F401
