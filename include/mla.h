@@ -6,6 +6,7 @@
  *   [P1] "mlx-bun 0.0.11 -> 0.0.13", package/src/model/glm52-mla.ts
  *   [P2] "mlx-bun 0.2.0 -> 0.4.0", glm52-mla.ts (left-padding mask) and
  *        glm52-cache.ts (right-aligned rows, per-row lengths, left pad)
+ *   [P3] "mlx-bun 0.4.0 -> 1.0.0", glm52-dsa.ts (DSA top-k selection)
  *
  * A decode step is the chain
  *   mla_rope_partial_interleaved (q rope part)  ->  mla_absorb_q  ->
@@ -188,6 +189,35 @@ int mla_decode_combine(const float* part_o, const float* part_lse,
 int mla_absorb_v(int32_t dtype, const float* o_lat, const void* w_kv_b, float* ctx,
                  int32_t batch, int32_t heads, int32_t qk_nope, int32_t v_head, int32_t kv_lora_rank,
                  hipStream_t stream);
+
+/*
+ * DSA top-k position selection.  [P3] selectGlm52DsaDevice, with the dense
+ * fallback of the page's indexer (a context not longer than top_k is
+ * attended densely).  For row b with n = row_len[b] > top_k, over the fp32
+ * scores s[0..n) at scores + b * score_stride:
+ *   rank key  = bitwise NOT of the order-preserving uint32 image of s[i]
+ *               (negative values: all bits flipped; others: sign bit flipped)
+ *   selection = the top_k positions of smallest key, equal keys (equal score
+ *               bits) taken in ascending position order
+ *   threshold = the minimum selected score
+ *   output    = the selected positions with s[i] > threshold in ascending
+ *               order, then the other selected positions in ascending order
+ * Positions are relative to the row's score slice, i.e. to the valid slice of
+ * the row's cache, which is what mla_decode_latent_attn takes.
+ *
+ * scores: device fp32, row b at scores + b * score_stride (score_stride >=
+ *         max row_len when batch > 1).  Scores must not be NaN (the selection
+ *         of a NaN is not defined by the page; no error is raised).
+ * row_len [host] int32[batch], each in [1, 2^30].
+ * sel_count [host, written] int32[batch]: top_k for a selected row, -1 for a
+ *         dense row (row_len[b] <= top_k), as mla_decode_latent_attn takes it.
+ * sel_idx: device int32, written with top_k entries per selected row,
+ *         concatenated in row order; may be NULL only if no row is selected.
+ * Errors: MLA_ERR_ARG (NULL pointers, top_k < 1, batch < 0), MLA_ERR_SHAPE
+ * (row_len out of range or above score_stride).
+ */
+int mla_dsa_topk_select(const float* scores, int64_t score_stride, int32_t batch, const int32_t* row_len,
+                        int32_t top_k, int32_t* sel_idx, int32_t* sel_count, hipStream_t stream);
 
 /*
  * Reconstructed causal prefill.  [P1] Glm52Mla.project (q_b_proj of the

@@ -20,7 +20,7 @@ from ._lib import (EXPORTS, LIB_PATH, MLA_DTYPE_BF16, MLA_DTYPE_F32, MlaError, c
 __all__ = [
     "MlaError", "LIB_PATH", "EXPORTS", "mla_rope_partial_interleaved", "mla_absorb_q", "mla_decode_latent_attn",
     "mla_decode_combine", "mla_absorb_v", "mla_prefill_reconstructed", "mla_version", "split_count",
-    "plan_chunk_len", "prefill_workspace_bytes",
+    "plan_chunk_len", "prefill_workspace_bytes", "mla_dsa_topk_select",
 ]
 
 
@@ -245,3 +245,29 @@ def mla_prefill_reconstructed(q_c: torch.Tensor, w_q_b: torch.Tensor, latent: to
         None if pads is None else i32_array(pads), float(softmax_scale), _ptr(workspace), ctypes.byref(size),
         _ptr(ctx), _stream(q_c)), "mla_prefill_reconstructed")
     return ctx
+
+
+def mla_dsa_topk_select(scores: torch.Tensor, row_len, top_k: int, sel_idx: torch.Tensor | None = None):
+    """DSA top-k positions of each row of fp32 scores [B, W] (row b: scores[b, :row_len[b]]).
+
+    Returns (sel_idx int32 device tensor, sel_count host list): the form
+    mla_decode_latent_attn takes (rows with row_len <= top_k stay dense, -1)."""
+    if scores.dtype != torch.float32:
+        raise TypeError("scores must be float32")
+    if scores.dim() == 1:
+        scores = scores.view(1, -1)
+    if scores.dim() != 2 or scores.stride(1) != 1:
+        raise ValueError("scores must be [B, W] with a unit feature stride")
+    lens = _host_list(row_len)
+    b = scores.shape[0]
+    if len(lens) != b:
+        raise ValueError("row_len needs one entry per score row")
+    total = sum(int(top_k) for n in lens if n > top_k)
+    if sel_idx is None:
+        sel_idx = torch.empty(max(total, 1), dtype=torch.int32, device=scores.device)
+    elif sel_idx.dtype != torch.int32 or sel_idx.numel() < total:
+        raise ValueError("sel_idx must be int32 with room for every selected index")
+    counts = i32_array([0] * b)
+    check(lib.mla_dsa_topk_select(_ptr(scores), scores.stride(0), b, i32_array(lens), int(top_k), _ptr(sel_idx),
+                                  counts, _stream(scores)), "mla_dsa_topk_select")
+    return sel_idx[:total], [int(c) for c in counts]

@@ -90,6 +90,21 @@ struct CombineParams {
 };
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 
+// ------------------------------------------------------------------ DSA top-k
+constexpr int kTopkRowsPerLaunch = 128;
+
+struct TopkParams {
+  const float* scores;    // row b at scores + b * stride
+  int64_t stride;
+  int32_t* sel_idx;       // concatenated output
+  int32_t rows;           // selected rows in this launch
+  int32_t top_k;
+  int32_t row[kTopkRowsPerLaunch];
+  int32_t len[kTopkRowsPerLaunch];
+  int32_t out_off[kTopkRowsPerLaunch];
+};
+hipError_t launch_dsa_topk(const TopkParams& p, hipStream_t stream);
+
 // ------------------------------------------------------------------ prefill
 struct PrefillParams {
   int32_t dtype;

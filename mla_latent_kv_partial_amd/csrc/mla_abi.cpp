@@ -240,6 +240,47 @@ int mla_decode_latent_attn(int32_t dtype, const void* q_lat, const void* q_rope,
   return ok();
 }
 
+int mla_dsa_topk_select(const float* scores, int64_t score_stride, int32_t batch, const int32_t* row_len,
+                        int32_t top_k, int32_t* sel_idx, int32_t* sel_count, hipStream_t stream) {
+  if (batch < 0) return fail(MLA_ERR_ARG, "dsa_topk: batch must be >= 0");
+  if (top_k < 1) return fail(MLA_ERR_ARG, "dsa_topk: top_k must be >= 1");
+  if (batch == 0) return ok();
+  if (!scores || !row_len || !sel_count) return fail(MLA_ERR_ARG, "dsa_topk: NULL pointer");
+  int64_t total = 0;
+  for (int b = 0; b < batch; ++b) {
+    if (row_len[b] < 1 || row_len[b] > (1 << 30))
+      return fail(MLA_ERR_SHAPE, "dsa_topk: row_len[%d] = %d outside [1, 2^30]", b, row_len[b]);
+    if (batch > 1 && row_len[b] > score_stride)
+      return fail(MLA_ERR_SHAPE, "dsa_topk: row_len[%d] = %d exceeds the score row stride %lld", b, row_len[b],
+                  static_cast<long long>(score_stride));
+    if (row_len[b] > top_k) total += top_k;
+  }
+  if (total > 0x7fffffffLL) return fail(MLA_ERR_UNSUPPORTED, "dsa_topk: more than 2^31-1 selected indices");
+  if (total > 0 && !sel_idx) return fail(MLA_ERR_ARG, "dsa_topk: sel_idx is NULL but rows are selected");
+  for (int b = 0; b < batch; ++b) sel_count[b] = row_len[b] > top_k ? top_k : -1;
+  mla::TopkParams p{};
+  p.scores = scores;
+  p.stride = score_stride;
+  p.sel_idx = sel_idx;
+  p.top_k = top_k;
+  int64_t off = 0;
+  for (int b = 0; b < batch; ++b) {
+    if (row_len[b] <= top_k) continue;
+    p.row[p.rows] = b;
+    p.len[p.rows] = row_len[b];
+    p.out_off[p.rows] = static_cast<int32_t>(off);
+    off += top_k;
+    if (++p.rows == mla::kTopkRowsPerLaunch) {
+      hipError_t e = mla::launch_dsa_topk(p, stream);
+      if (e != hipSuccess) return device(e, "dsa_topk launch");
+      p.rows = 0;
+    }
+  }
+  hipError_t e = mla::launch_dsa_topk(p, stream);
+  if (e != hipSuccess) return device(e, "dsa_topk launch");
+  return ok();
+}
+
 int mla_decode_combine(const float* part_o, const float* part_lse, int32_t batch, int32_t heads, int32_t kv_lora_rank,
                        int32_t s_max, const int32_t* n_splits, float* o_lat, float* lse, hipStream_t stream) {
   if (batch < 0 || heads < 1 || kv_lora_rank < 1 || s_max < 1)

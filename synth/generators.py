@@ -29,6 +29,7 @@ T_C_Q = 8
 T_W_QB = 9
 T_K_ROPE_RAW = 10
 T_MISC = 11
+T_DSA_SCORES = 12
 
 BF16_QUIET_NAN = np.uint16(0x7FC0)
 

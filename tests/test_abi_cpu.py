@@ -119,3 +119,26 @@ def test_prefill_workspace_query_and_rejections():
     assert _prefill(dn=250)[0] == UNSUP
     assert _prefill(ws=ctypes.c_void_p(0x10000), size=need, offs=[-1])[0] == ROPE
     assert _prefill(ws=ctypes.c_void_p(0x10000), size=need, pad=[17])[0] == SHAPE
+
+
+def _topk(batch=2, lens=(10, 3), top_k=4, stride=16, scores=FAKE, sel=FAKE):
+    counts = i32_array([7] * max(batch, 1))
+    code = lib.mla_dsa_topk_select(scores, stride, batch, i32_array(list(lens)), top_k, sel, counts, None)
+    return code, [counts[i] for i in range(max(batch, 1))]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), ARG), (dict(top_k=0), ARG), (dict(scores=None), ARG),
+    (dict(lens=(0, 3)), SHAPE), (dict(lens=(2 ** 30 + 1, 3)), SHAPE), (dict(lens=(17, 3)), SHAPE),
+    (dict(sel=None), ARG),
+])
+def test_dsa_topk_rejections(kw, code):
+    assert _topk(**kw)[0] == code
+    assert lib.mla_last_error() != b""
+
+
+def test_dsa_topk_all_dense_rows_launch_nothing():
+    # every row is not longer than top_k: counts -1, nothing enqueued, sel_idx may be NULL
+    code, counts = _topk(lens=(4, 3), top_k=4, sel=None)
+    assert code == OK and counts == [-1, -1]
+    assert _topk(batch=0)[0] == OK
