@@ -21,7 +21,8 @@ back), HIP events around the replays.  traffic = HBM bytes per launch from the
 FETCH_SIZE / WRITE_SIZE counter runs recorded in the committed profile, only
 while the kernel sources still hash to the recorded digest.  cpu_baseline = the CPU
 oracle's reconstructed decode on a bounded sample of the same rows.  extra =
-the dense (chained and layer-stacked), DSA and prefill workloads.
+the dense (chained and layer-stacked), DSA (chain and top-k selection) and prefill
+workloads.
 """
 
 from __future__ import annotations
@@ -347,6 +348,18 @@ def main():
                                 "gathered_GBps": gb / (ms_dsa_attn * 1e-3) / 1e9}
         del sl
         torch.cuda.empty_cache()
+        # DSA top-k selection over the 131072-token context (synthetic fp32 scores)
+        import numpy as np
+        from synth import generators as gen
+        n_ctx, k_sel = scfg.tokens, scfg.selected
+        scores = torch.from_numpy(gen.normal_f32(scfg.config_id, gen.T_DSA_SCORES, (args.layers, n_ctx))).to(dev)
+        sel_buf = torch.empty(args.layers * k_sel, dtype=torch.int32, device=dev)
+        ms_sel = time_graph(torch, lambda: mla.mla_dsa_topk_select(scores, [n_ctx] * args.layers, k_sel,
+                                                                   sel_idx=sel_buf), args.steps, args.warmup)[0]
+        extra["dsa_topk"] = {"rows": args.layers, "context": n_ctx, "top_k": k_sel, "ms_per_launch": ms_sel,
+                             "us_per_row": ms_sel * 1e3 / args.layers,
+                             "scores_GBps": args.layers * n_ctx * 4 / (ms_sel * 1e-3) / 1e9}
+        del scores, sel_buf
         extra["prefill"] = prefill_leg(torch, mla, cf, dev)
         result["extra"] = extra
 

@@ -17,8 +17,8 @@
 //                               streamed through LDS, fp32 context out.
 // Both contractions run on v_mfma_f32_16x16x32_bf16.  Operand tiles move
 // HBM -> LDS with global_load_lds_dwordx4 into rows padded to an odd number of
-// 16-byte chunks, so the fragment reads of 16 consecutive rows are free of
-// bank conflicts.
+// 32-byte units, which makes the 16-byte fragment reads of 16 consecutive rows
+// free of bank conflicts (measured with the LDS bank-conflict counter).
 #include <math.h>
 
 #include "cdna4.hpp"
@@ -45,14 +45,14 @@ constexpr int kBatchPerLaunch = 128;    // per-row tables travel in the kernel a
 // two K steps ahead.
 constexpr int kGT = 128;
 constexpr int kGK = 64;
-constexpr int kGRowChunks = kGK / 8 + 1;            // eight data chunks + one pad
-constexpr int kGRowBytes = kGRowChunks * 16;        // 144
-constexpr int kGOpChunks = kGT * kGRowChunks;       // 1152 per operand tile
-constexpr int kGOpDma = kGOpChunks / 64;            // 18 copies of 1 KB
+constexpr int kGRowChunks = kGK / 8 + 2;            // eight data chunks + two pad
+constexpr int kGRowBytes = kGRowChunks * 16;        // 160
+constexpr int kGOpChunks = kGT * kGRowChunks;       // 1280 per operand tile
+constexpr int kGOpDma = kGOpChunks / 64;            // 20 copies of 1 KB
 constexpr int kGOpBytes = kGOpChunks * 16;
 constexpr int kGStageBytes = 2 * kGOpBytes;         // A tile then B tile
 constexpr int kGStages = 3;
-constexpr int kGMaxDma = (kGOpDma + 3) / 4;         // copies per wave per operand (5 or 4)
+constexpr int kGMaxDma = (kGOpDma + 3) / 4;         // copies per wave per operand
 
 __shared__ __attribute__((aligned(1024))) char g_gemm[kGStages * kGStageBytes];
 
@@ -87,8 +87,8 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(GemmNT p) {
   const int n0 = (tile / p.m_tiles) * kGT;
 
   // copy plan: copy j of this wave moves chunk q = 64 (wave + 4 j) + lane of
-  // an operand tile: row q / 9, chunk q % 9 (chunk 8 is padding and re-reads
-  // chunk 0); rows past the matrix edge re-read its last row.
+  // an operand tile: row q / 10, chunk q % 10 (chunks 8 and 9 are padding and
+  // re-read chunk 0); rows past the matrix edge re-read its last row.
   const int n_dma = (kGOpDma - wave + 3) / 4;
   const uint16_t* asrc[kGMaxDma];
   const uint16_t* bsrc[kGMaxDma];
@@ -200,12 +200,12 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(GemmNT p) {
 // softmax in exp2 with a lazily moved reference max, and O^T[dim, query] +=
 // V^T . P^T (V^T fragments by ds_read_b64_tr_b16, each shared by the two
 // query blocks).  The layout tricks are those of the latent decode kernel: key
-// row m of a 16-key block holds key sigma(m), and a key row is 41 chunks
-// (k_nope 16, v 16, rope 8, pad 1), an odd count.
+// row m of a 16-key block holds key sigma(m), and a key row is 42 chunks
+// (k_nope 16, v 16, rope 8, pad 2), an odd number of 32-byte units.
 constexpr int kAQ = 128;
 constexpr int kAK = 32;
-constexpr int kARowChunks = 41;
-constexpr int kARowBytes = kARowChunks * 16;                 // 656
+constexpr int kARowChunks = 42;
+constexpr int kARowBytes = kARowChunks * 16;                 // 672
 constexpr int kATileDma = (kAK * kARowChunks + 63) / 64;      // 21
 constexpr int kAStageBytes = kATileDma * 1024;
 constexpr int kAStages = 3;
@@ -225,8 +225,7 @@ struct AttnMfma {
 };
 
 __device__ __forceinline__ int sigma(int m) {
-  const int g = m >> 2, j = m & 3;
-  return 2 * j + 8 * (g & 1) + (g >> 1);
+  return 2 * (m & 3) + ((m >> 2) & 1) + 8 * ((m >> 3) & 1);
 }
 
 __global__ __launch_bounds__(256, 2) void flash_attn_kernel(AttnMfma p) {
@@ -247,8 +246,8 @@ __global__ __launch_bounds__(256, 2) void flash_attn_kernel(AttnMfma p) {
   const int nt = k_last >= k_first ? (k_last - k_first) / kAK + 1 : 0;
 
   // ---- copy plan (same for every tile): chunk q = 64 (wave + 4 j) + lane is
-  // chunk c of key row q / 41; c < 32 from the KV workspace row of head h,
-  // c < 40 from the rope row, c = 40 padding (re-reads chunk 0)
+  // chunk c of key row q / 42; c < 32 from the KV workspace row of head h,
+  // c < 40 from the rope row, c = 40, 41 padding (re-read chunk 0)
   const int n_dma = (kATileDma - wave + 3) / 4;
   int c_row[kAMaxDma];
   int c_off[kAMaxDma];   // byte offset in the KV head slice, or rope row (sign bit set)
