@@ -56,6 +56,8 @@ constexpr int kQSteps = kR / 32 + kDR / 32;                 // 18 k-steps of the
 constexpr int kDimBlocks = kR / 16;                         // 32 output blocks of 16 dims
 constexpr float kRescaleSlack = 8.f;                        // log2 units
 constexpr int kMaxHeadGroups = 4;                           // 16-head groups per workgroup
+static_assert(kStages * kStageBytes >= kMaxHeadGroups * (16 * kMaxHeadGroups) * (kR * 4 / kMaxHeadGroups + 32),
+              "the epilogue regions of the context waves must fit in the stage ring");
 
 __shared__ __attribute__((aligned(1024))) char g_stage[kStages * kStageBytes];
 __shared__ __attribute__((aligned(16))) char g_p[2][kMaxHeadGroups][kWave * 16];   // P operands, by tile parity
@@ -121,8 +123,6 @@ struct Decode {
     return ok ? pad + idx : p.width - 1;   // masked tokens read a valid row, weighted by zero
   }
 
-  __device__ __forceinline__ int dense_index(int tile) const { return sel_base + tile * kNT + lane; }
-
   __device__ __forceinline__ static char* stage(int s) { return g_stage + s * kStageBytes; }
   __device__ __forceinline__ static int* idx_area(int s) { return reinterpret_cast<int*>(stage(s) + kTileBytes); }
 
@@ -137,6 +137,35 @@ struct Decode {
       const char* src = off >= 0 ? lat_base + v * lat_st + off : rope_base + v * rope_st + (off & 0x7fff);
       dma16(src, dst + (wave + kWaves * i) * 1024);
     }
+  }
+
+  // Dense rows: row r of tile `tile` is slot pad + sel_base + 32 tile + r while
+  // inside the split; past its end the copy reads the valid slot width - 1
+  // (those tokens are masked).  No lane exchange needed.
+  __device__ __forceinline__ void issue_tile_dense(int s, int tile) const {
+    const uint32_t dst = lds_addr(stage(s));
+    const int first = tile * kNT;
+    const int base = pad + sel_base + first;
+#pragma unroll
+    for (int i = 0; i < kMaxDma; ++i) {
+      if (i == kMaxDma - 1 && n_dma != kMaxDma) break;
+      const int r = dma_src[i] >> 2;
+      const int slot = first + r < n_tok ? base + r : p.width - 1;
+      const int off = dma_off[i];
+      if (PACKED) {
+        dma16_off(lat_base, static_cast<uint32_t>(slot) * static_cast<uint32_t>(lat_st) + static_cast<uint32_t>(off),
+                  dst + (wave + kWaves * i) * 1024);
+      } else {
+        const char* src = off >= 0 ? lat_base + slot * lat_st + off : rope_base + slot * rope_st + (off & 0x7fff);
+        dma16(src, dst + (wave + kWaves * i) * 1024);
+      }
+    }
+  }
+
+  // Validity of the tokens of tile `tile` of a dense row (bit t: token t).
+  __device__ __forceinline__ uint32_t dense_mask(int tile) const {
+    const int cnt = n_tok - tile * kNT;
+    return cnt >= kNT ? 0xffffffffu : (cnt <= 0 ? 0u : (1u << cnt) - 1u);
   }
 
   // Copy one tile into stage s.  slot_v: lane t < 32 holds token t's row slot.
@@ -305,23 +334,25 @@ struct Decode {
 #pragma unroll
         for (int e = 0; e < 8; ++e) qrraw[ks][e] = static_cast<short>(qr[8 * g + 32 * ks + e]);
     }
-    int idx0v, idx1v;
+    // Tile 1 is copied even for single-tile splits (all of its tokens are
+    // then masked and read a valid row), which keeps the wait counts fixed.
     if (GATHER && gather_row) {
-      idx0v = lane < kNT ? p.sel[sel_base + min(lane, n_tok - 1)] : 0;
-      idx1v = lane < kNT ? p.sel[sel_base + min(kNT + lane, n_tok - 1)] : 0;
-    } else {
-      idx0v = dense_index(0);
-      idx1v = dense_index(1);
-    }
-    if (SC && GATHER) convert_queries(qraw, qrraw);
-    {
+      const int idx0v = lane < kNT ? p.sel[sel_base + min(lane, n_tok - 1)] : 0;
+      const int idx1v = lane < kNT ? p.sel[sel_base + min(kNT + lane, n_tok - 1)] : 0;
+      if (SC) convert_queries(qraw, qrraw);
       const int slot0 = slot_of<SC>(0, idx0v, mask0);
       issue_tile(0, slot0);
-      if (GATHER && gather_row && nt > 2) issue_idx(2, 2);
-      // Tile 1 is copied even for single-tile splits (all of its tokens are
-      // then masked and read a valid row), which keeps the wait counts fixed.
+      if (nt > 2) issue_idx(2, 2);
       const int slot1 = slot_of<SC>(1, idx1v, mask1);
       issue_tile(1, slot1);
+    } else {
+      issue_tile_dense(0, 0);
+      issue_tile_dense(1, 1);
+      if (SC) {
+        mask0 = dense_mask(0);
+        mask1 = dense_mask(1);
+        if (GATHER) convert_queries(qraw, qrraw);
+      }
     }
     if (SC && !GATHER) convert_queries(qraw, qrraw);
     if (!SC) {
@@ -342,15 +373,15 @@ struct Decode {
       if (i < nt) wait_vm_upto<kMaxDma>(ops_after(i));
       lds_barrier();
       if (i + 2 < nt) {
-        int idx;
         if (GATHER && gather_row) {
-          idx = lane < kNT ? idx_area((i + 2) % kStages)[lane] : 0;
+          const int idx = lane < kNT ? idx_area((i + 2) % kStages)[lane] : 0;
           if (i + 3 < nt) issue_idx((i + 3) % kStages, i + 3);
+          const int slot = slot_of<SC>(i + 2, idx, mask2);
+          issue_tile((i + 2) % kStages, slot);
         } else {
-          idx = dense_index(i + 2);
+          issue_tile_dense((i + 2) % kStages, i + 2);
+          if (SC) mask2 = dense_mask(i + 2);
         }
-        const int slot = slot_of<SC>(i + 2, idx, mask2);
-        issue_tile((i + 2) % kStages, slot);
       }
       if (SC) {
         if (i < nt) score(i % kStages, i & 1, mask0);
@@ -371,19 +402,30 @@ struct Decode {
         p.part_lse[ps] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
       }
     }
-    lds_barrier();
+    lds_barrier();   // every wave is past the loop and its copies: the stages are free
     if (!SC) {
+      // O^T leaves through LDS so that every store instruction writes two
+      // whole 512-byte partial rows: the wave's region holds its dims of every
+      // head, one row per head padded to an odd number of 32-byte units.
+      constexpr int kEpiDims = kR / NW;
+      constexpr int kEpiRow = kEpiDims * 4 + 32;
+      constexpr int kChunksPerRow = kEpiDims / 4;
+      char* region = g_stage + hw * (16 * NW * kEpiRow);
 #pragma unroll
-      for (int hb = 0; hb < NW; ++hb) {
-        const float l_tot = g_l[hb][h];
+      for (int hb = 0; hb < NW; ++hb)
+#pragma unroll
+        for (int db = 0; db < kCtxBlocks; ++db)
+          *reinterpret_cast<f32x4*>(region + (16 * hb + h) * kEpiRow + (16 * db + 4 * g) * 4) = reg[db * NW + hb];
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave reads back its own writes
+#pragma unroll 4
+      for (int k = 0; k < 16 * NW * kChunksPerRow / kWave; ++k) {
+        const int q = k * kWave + lane;
+        const int row = q / kChunksPerRow, c = q - row * kChunksPerRow;
+        const float l_tot = g_l[row >> 4][row & 15];
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        const int64_t ps = (static_cast<int64_t>(b) * p.heads + head0 + 16 * hb + h) * p.s_max + s;
-        float* out = p.part_o + ps * kR + 16 * kCtxBlocks * hw + 4 * g;
-#pragma unroll
-        for (int db = 0; db < kCtxBlocks; ++db) {
-          const f32x4 v = reg[db * NW + hb] * inv;
-          *reinterpret_cast<float4*>(out + 16 * db) = make_float4(v[0], v[1], v[2], v[3]);
-        }
+        const f32x4 v = *reinterpret_cast<const f32x4*>(region + row * kEpiRow + c * 16) * inv;
+        const int64_t ps = (static_cast<int64_t>(b) * p.heads + head0 + row) * p.s_max + s;
+        *reinterpret_cast<float4*>(p.part_o + ps * kR + kEpiDims * hw + 4 * c) = make_float4(v[0], v[1], v[2], v[3]);
       }
     }
   }
