@@ -1,0 +1,58 @@
+"""Pins of the fused-append oracle (page "mlx-bun 0.0.11 -> 0.0.13",
+glm52-mla.ts: rmsNormF32Mlx and the kv_a split of Glm52Mla.project)."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "rms_norm_hand_example.json")
+
+
+def test_rms_norm_hand_example():
+    with open(GOLDEN) as f:
+        fix = json.load(f)
+    for c in fix["cases"]:
+        got = oracle.rms_norm(np.array(c["x"]), np.array(c["weight"]), c["eps"])
+        assert np.allclose(got, c["expected"], rtol=1e-14, atol=0)
+
+
+def test_rms_norm_unit_rms_and_scale_invariance():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((5, 64))
+    y = oracle.rms_norm(x, np.ones(64), 0.0)
+    assert np.allclose(np.sqrt((y * y).mean(axis=-1)), 1.0, rtol=1e-13)
+    assert np.allclose(oracle.rms_norm(-7.5 * x, np.ones(64), 0.0), -y, rtol=1e-12)
+
+
+def test_rms_norm_brute_force_loop():
+    rng = np.random.default_rng(4)
+    x, w = rng.standard_normal(9), rng.standard_normal(9)
+    s = 0.0
+    for v in x:
+        s += v * v
+    inv = 1.0 / (s / 9 + 1e-3) ** 0.5
+    assert np.allclose(oracle.rms_norm(x, w, 1e-3), [x[i] * inv * w[i] for i in range(9)], rtol=1e-13)
+
+
+def test_append_splits_latent_and_rope():
+    rng = np.random.default_rng(5)
+    r, dr = 16, 8
+    kv_a = rng.standard_normal((2, 3, r + dr))
+    w = rng.standard_normal(r)
+    lat, rope = oracle.append_compressed(kv_a, w, 1e-6, [5, 0], 10000.0, r, dr)
+    assert np.allclose(lat, oracle.rms_norm(kv_a[..., :r], w, 1e-6))
+    # row 1 starts at position 0: token 0 is the plain de-interleave of its pairs
+    assert np.array_equal(rope[1, 0], np.concatenate([kv_a[1, 0, r::2], kv_a[1, 0, r + 1::2]]))
+    # pair norms are preserved at every position
+    a, b = kv_a[..., r::2], kv_a[..., r + 1::2]
+    assert np.allclose(a * a + b * b, rope[..., :dr // 2] ** 2 + rope[..., dr // 2:] ** 2)
+
+
+@pytest.mark.parametrize("eps", [-1.0, float("nan"), float("inf")])
+def test_rms_norm_rejects_bad_epsilon(eps):
+    with pytest.raises(oracle.OracleError):
+        oracle.rms_norm(np.ones(4), np.ones(4), eps)
