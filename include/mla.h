@@ -191,6 +191,35 @@ int mla_absorb_v(int32_t dtype, const float* o_lat, const void* w_kv_b, float* c
                  hipStream_t stream);
 
 /*
+ * Fused cache append.  [P1] Glm52Mla.project: the kv_a_proj_with_mqa output
+ * of a token splits into the latent part (first kv_lora_rank features) and
+ * the rope part (last rope_dim); the latent goes through rmsNormF32Mlx with
+ * the kv_a_layernorm weight, the rope part through partialInterleavedRopeMlx
+ * at the token's position; Glm52Mla.forward appends both to the cache.
+ *
+ *   latent[b, slot + t, :] = x * rsqrt(mean(x^2) + eps) * norm_weight,
+ *                            x = kv_a[b, t, 0 .. kv_lora_rank)
+ *   rope[b, slot + t, :]   = RoPE(kv_a[b, t, kv_lora_rank ..), positions[b] + t)
+ *
+ * In the right-aligned cache of mla_decode_latent_attn every row appends at
+ * the same slot (the width before the append: slot = width) while each row's
+ * RoPE position is its own length ([P2] glm52-cache.ts).
+ * kv_a [batch, tokens, kv_lora_rank + rope_dim] of `dtype`, strides
+ * (kv_a_stride_b, kv_a_stride_t, 1); norm_weight [kv_lora_rank] of `dtype`;
+ * positions [host] int64[batch]; latent / rope: the cache arrays as in
+ * mla_decode_latent_attn (the caller guarantees slot + tokens fits the
+ * buffer).  The mean square is accumulated in fp32, the rotation in double;
+ * each output is rounded once to `dtype`.
+ * Errors: MLA_ERR_ARG (eps negative or not finite, NULL, bad strides),
+ * MLA_ERR_ROPE (odd rope_dim, theta, negative positions).
+ */
+int mla_append_compressed(int32_t dtype, const void* kv_a, int64_t kv_a_stride_b, int64_t kv_a_stride_t,
+                          int32_t batch, int32_t tokens, int32_t kv_lora_rank, int32_t rope_dim,
+                          const void* norm_weight, float eps, const int64_t* positions, double theta,
+                          void* latent, int64_t latent_stride_b, int64_t latent_stride_t, void* rope,
+                          int64_t rope_stride_b, int64_t rope_stride_t, int32_t slot, hipStream_t stream);
+
+/*
  * DSA top-k position selection.  [P3] selectGlm52DsaDevice, with the dense
  * fallback of the page's indexer (a context not longer than top_k is
  * attended densely).  For row b with n = row_len[b] > top_k, over the fp32

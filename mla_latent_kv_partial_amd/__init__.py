@@ -20,7 +20,7 @@ from ._lib import (EXPORTS, LIB_PATH, MLA_DTYPE_BF16, MLA_DTYPE_F32, MlaError, c
 __all__ = [
     "MlaError", "LIB_PATH", "EXPORTS", "mla_rope_partial_interleaved", "mla_absorb_q", "mla_decode_latent_attn",
     "mla_decode_combine", "mla_absorb_v", "mla_prefill_reconstructed", "mla_version", "split_count",
-    "plan_chunk_len", "prefill_workspace_bytes", "mla_dsa_topk_select",
+    "plan_chunk_len", "prefill_workspace_bytes", "mla_dsa_topk_select", "mla_append_compressed",
 ]
 
 
@@ -271,3 +271,27 @@ def mla_dsa_topk_select(scores: torch.Tensor, row_len, top_k: int, sel_idx: torc
     check(lib.mla_dsa_topk_select(_ptr(scores), scores.stride(0), b, i32_array(lens), int(top_k), _ptr(sel_idx),
                                   counts, _stream(scores)), "mla_dsa_topk_select")
     return sel_idx[:total], [int(c) for c in counts]
+
+
+def mla_append_compressed(kv_a: torch.Tensor, norm_weight: torch.Tensor, eps: float, positions, theta: float,
+                          latent: torch.Tensor, rope: torch.Tensor, slot: int) -> None:
+    """RMSNorm(kv_a[..., :r]) and RoPE(kv_a[..., r:]) written to latent[:, slot:slot+T] / rope[:, slot:slot+T].
+
+    kv_a [B, T, r + dr]; latent [B, W, r] and rope [B, W, dr] are cache views
+    (feature stride 1); positions: host sequence, RoPE position of token 0 per row."""
+    b, t, width = kv_a.shape
+    r, dr = latent.shape[2], rope.shape[2]
+    if width != r + dr:
+        raise ValueError("kv_a must hold kv_lora_rank + rope_dim features")
+    if not (kv_a.dtype == norm_weight.dtype == latent.dtype == rope.dtype):
+        raise TypeError("kv_a, norm_weight and the cache must share a dtype")
+    if kv_a.stride(2) != 1 or latent.stride(2) != 1 or rope.stride(2) != 1 or not norm_weight.is_contiguous():
+        raise ValueError("feature axes must have stride 1")
+    if slot < 0 or slot + t > latent.shape[1] or slot + t > rope.shape[1]:
+        raise ValueError("slot + tokens must fit the cache")
+    check(lib.mla_append_compressed(
+        _dtype_code(kv_a), _ptr(kv_a), kv_a.stride(0), kv_a.stride(1), b, t, r, dr, _ptr(norm_weight),
+        float(eps), i64_array(_host_list(positions)), float(theta), _ptr(latent), latent.stride(0),
+        latent.stride(1), _ptr(rope), rope.stride(0), rope.stride(1), int(slot), _stream(kv_a)),
+        "mla_append_compressed")
+

@@ -22,6 +22,7 @@ STATUS_NAMES = {
 EXPORTS = (
     "mla_last_error", "mla_version", "mla_rope_partial_interleaved", "mla_absorb_q", "mla_decode_latent_attn",
     "mla_decode_combine", "mla_absorb_v", "mla_prefill_reconstructed", "mla_dsa_topk_select",
+    "mla_append_compressed",
 )
 
 _p = ctypes.c_void_p
@@ -45,6 +46,8 @@ _SIGNATURES = {
     "mla_decode_combine": (ctypes.c_int, [_p, _p, _i32, _i32, _i32, _i32, _pi32, _p, _p, _p]),
     "mla_absorb_v": (ctypes.c_int, [_i32, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _p]),
     "mla_dsa_topk_select": (ctypes.c_int, [_p, _i64, _i32, _pi32, _i32, _p, _pi32, _p]),
+    "mla_append_compressed": (ctypes.c_int, [
+        _i32, _p, _i64, _i64, _i32, _i32, _i32, _i32, _p, _f32, _pi64, _f64, _p, _i64, _i64, _p, _i64, _i64, _i32, _p]),
     "mla_prefill_reconstructed": (ctypes.c_int, [
         _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _pi64, _f64, _pi32, _f32,
         _p, _psz, _p, _p]),

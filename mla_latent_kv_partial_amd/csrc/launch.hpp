@@ -90,6 +90,22 @@ struct CombineParams {
 };
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 
+// ------------------------------------------------------------------ cache append
+struct AppendParams {
+  const void* kv_a;       // [rows, T, r + dr] strided (element strides kb, kt)
+  int64_t kb, kt;
+  const void* w;          // [r] RMSNorm weight
+  void* latent;           // cache, element strides lb, lt
+  int64_t lb, lt;
+  void* rope;
+  int64_t rb, rt;
+  int32_t rows, tokens, r, dr, slot;
+  float eps;
+  int64_t off[kRopeRowsPerLaunch];   // RoPE position of token 0, per row
+  float inv[kRopeMaxPairs];
+};
+hipError_t launch_append(int32_t dtype, const AppendParams& p, hipStream_t stream);
+
 // ------------------------------------------------------------------ DSA top-k
 constexpr int kTopkRowsPerLaunch = 128;
 

@@ -240,6 +240,55 @@ int mla_decode_latent_attn(int32_t dtype, const void* q_lat, const void* q_rope,
   return ok();
 }
 
+int mla_append_compressed(int32_t dtype, const void* kv_a, int64_t kv_a_stride_b, int64_t kv_a_stride_t,
+                          int32_t batch, int32_t tokens, int32_t kv_lora_rank, int32_t rope_dim,
+                          const void* norm_weight, float eps, const int64_t* positions, double theta,
+                          void* latent, int64_t latent_stride_b, int64_t latent_stride_t, void* rope,
+                          int64_t rope_stride_b, int64_t rope_stride_t, int32_t slot, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return fail(MLA_ERR_ARG, "append: unknown dtype %d", dtype);
+  if (batch < 0 || tokens < 0 || kv_lora_rank < 1 || rope_dim < 1 || slot < 0)
+    return fail(MLA_ERR_ARG, "append: batch, tokens, slot >= 0 and positive kv_lora_rank, rope_dim required");
+  if (!isfinite(eps) || eps < 0.f) return fail(MLA_ERR_ARG, "RMSNorm epsilon must be non-negative");
+  if (rope_dim & 1) return fail(MLA_ERR_ROPE, "RoPE dimensions must be positive, even, and fit the feature axis");
+  if (!(theta > 0.0) || !isfinite(theta)) return fail(MLA_ERR_ROPE, "RoPE theta must be positive");
+  if (rope_dim > 2 * mla::kRopeMaxPairs || kv_lora_rank > 65536)
+    return fail(MLA_ERR_UNSUPPORTED, "append: rope_dim <= %d and kv_lora_rank <= 65536 supported", 2 * mla::kRopeMaxPairs);
+  if (batch == 0 || tokens == 0) return ok();
+  if (!kv_a || !norm_weight || !positions || !latent || !rope) return fail(MLA_ERR_ARG, "append: NULL pointer");
+  if (kv_a_stride_b < 0 || kv_a_stride_t < 0 || latent_stride_b < 0 || latent_stride_t < 1 || rope_stride_b < 0 ||
+      rope_stride_t < 1)
+    return fail(MLA_ERR_ARG, "append: bad stride");
+  for (int b = 0; b < batch; ++b) {
+    if (positions[b] < 0) return fail(MLA_ERR_ROPE, "RoPE position offset must be a non-negative integer");
+    if (static_cast<double>(positions[b]) + tokens > kMaxPosition)
+      return fail(MLA_ERR_UNSUPPORTED, "append: position + tokens exceeds 2^53");
+  }
+  mla::AppendParams p{};
+  p.kb = kv_a_stride_b;
+  p.kt = kv_a_stride_t;
+  p.w = norm_weight;
+  p.lb = latent_stride_b;
+  p.lt = latent_stride_t;
+  p.rb = rope_stride_b;
+  p.rt = rope_stride_t;
+  p.tokens = tokens;
+  p.r = kv_lora_rank;
+  p.dr = rope_dim;
+  p.slot = slot;
+  p.eps = eps;
+  mla::rope_inverse_frequencies(rope_dim, theta, p.inv);
+  for (int b0 = 0; b0 < batch; b0 += mla::kRopeRowsPerLaunch) {
+    p.rows = std::min(batch - b0, mla::kRopeRowsPerLaunch);
+    p.kv_a = advance(kv_a, b0 * kv_a_stride_b, dtype);
+    p.latent = const_cast<void*>(advance(latent, b0 * latent_stride_b, dtype));
+    p.rope = const_cast<void*>(advance(rope, b0 * rope_stride_b, dtype));
+    for (int i = 0; i < p.rows; ++i) p.off[i] = positions[b0 + i];
+    hipError_t e = mla::launch_append(dtype, p, stream);
+    if (e != hipSuccess) return device(e, "append launch");
+  }
+  return ok();
+}
+
 int mla_dsa_topk_select(const float* scores, int64_t score_stride, int32_t batch, const int32_t* row_len,
                         int32_t top_k, int32_t* sel_idx, int32_t* sel_count, hipStream_t stream) {
   if (batch < 0) return fail(MLA_ERR_ARG, "dsa_topk: batch must be >= 0");

@@ -142,3 +142,27 @@ def test_dsa_topk_all_dense_rows_launch_nothing():
     code, counts = _topk(lens=(4, 3), top_k=4, sel=None)
     assert code == OK and counts == [-1, -1]
     assert _topk(batch=0)[0] == OK
+
+
+def _append(**kw):
+    a = dict(dtype=1, batch=2, tokens=1, r=512, dr=64, eps=1e-6, pos=[3, 4], theta=1e4, slot=0, lt=576, rt=576,
+             kv=FAKE, w=FAKE)
+    a.update(kw)
+    return lib.mla_append_compressed(a["dtype"], a["kv"], 576, 576, a["batch"], a["tokens"], a["r"], a["dr"], a["w"],
+                                     a["eps"], i64_array(a["pos"]), a["theta"], FAKE, 576 * 8, a["lt"], FAKE,
+                                     576 * 8, a["rt"], a["slot"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), ARG), (dict(eps=-1.0), ARG), (dict(eps=float("inf")), ARG), (dict(slot=-1), ARG),
+    (dict(dr=63), ROPE), (dict(theta=0.0), ROPE), (dict(pos=[-1, 0]), ROPE), (dict(kv=None), ARG),
+    (dict(lt=0), ARG), (dict(dr=1024), UNSUP),
+])
+def test_append_rejections(kw, code):
+    assert _append(**kw) == code
+    assert lib.mla_last_error() != b""
+
+
+def test_append_empty_is_a_no_op():
+    assert _append(batch=0, pos=[0]) == OK
+    assert _append(tokens=0) == OK
