@@ -40,3 +40,14 @@ def append_compressed(kv_a: np.ndarray, weight: np.ndarray, eps: float, position
     latent = rms_norm(kv_a[..., :kv_lora_rank], weight, eps)
     rope = rope_partial_interleaved(kv_a[..., kv_lora_rank:], [int(p) for p in positions], rope_dim, theta)
     return latent, rope
+
+
+def o_proj(ctx: np.ndarray, w_o: np.ndarray) -> np.ndarray:
+    """Page "mlx-bun 0.0.11 -> 0.0.13", glm52-mla.ts, the o_proj linear after
+    attendReconstructed / attendAbsorbed: out[m, :] = ctx[m, :] . w_o^T with
+    w_o stored [hidden, heads * v_head] (out features, in features)."""
+    ctx = np.asarray(ctx, dtype=np.float64)
+    w_o = np.asarray(w_o, dtype=np.float64)
+    if ctx.shape[-1] != w_o.shape[1]:
+        raise OracleError("o_proj: context width != weight input width")
+    return ctx @ w_o.T

@@ -56,3 +56,16 @@ def test_append_splits_latent_and_rope():
 def test_rms_norm_rejects_bad_epsilon(eps):
     with pytest.raises(oracle.OracleError):
         oracle.rms_norm(np.ones(4), np.ones(4), eps)
+
+
+def test_o_proj_brute_force_and_unit_rows():
+    rng = np.random.default_rng(6)
+    ctx, w = rng.standard_normal((3, 7)), rng.standard_normal((5, 7))
+    ref = [[sum(ctx[m, k] * w[n, k] for k in range(7)) for n in range(5)] for m in range(3)]
+    assert np.allclose(oracle.o_proj(ctx, w), ref, rtol=1e-13)
+    # a unit context row selects a column of w_o (an input feature across outputs)
+    e = np.zeros((1, 7))
+    e[0, 4] = 1.0
+    assert np.array_equal(oracle.o_proj(e, w)[0], w[:, 4])
+    with pytest.raises(oracle.OracleError):
+        oracle.o_proj(ctx, w[:, :6])
