@@ -220,6 +220,27 @@ int mla_append_compressed(int32_t dtype, const void* kv_a, int64_t kv_a_stride_b
                           int64_t rope_stride_b, int64_t rope_stride_t, int32_t slot, hipStream_t stream);
 
 /*
+ * o_proj linear after the attention.  [P1] the o_proj of
+ * Glm52Mla.attendReconstructed / attendAbsorbed: the per-head contexts
+ * concatenated [rows, heads*v_head] times the o_proj weight, stored
+ * [hidden, heads*v_head] (out features, in features):
+ *
+ *   out[m, n] = sum_k ctx[m, k] * w_o[n, k]
+ *
+ * ctx fp32 [rows, in_features] contiguous (the ctx of mla_absorb_v or of
+ * mla_prefill_reconstructed); w_o [hidden, in_features] of `dtype`,
+ * contiguous; out fp32 [rows, hidden].  bf16 weights: up to 64 rows stream
+ * the weight once on MFMA with the fp32 context split into two bf16 parts;
+ * more rows round the context to bf16 once (in the workspace) and run an MFMA
+ * GEMM.  The workspace size depends on the shapes only:
+ * mla_o_proj_workspace_bytes writes it (0 when none is needed, and then
+ * workspace may be NULL).  Errors: MLA_ERR_ARG, MLA_ERR_WORKSPACE.
+ */
+int mla_o_proj_workspace_bytes(int32_t dtype, int64_t rows, int32_t in_features, int32_t hidden, size_t* bytes);
+int mla_o_proj(int32_t dtype, const float* ctx, int64_t rows, int32_t in_features, const void* w_o, int32_t hidden,
+               float* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * DSA top-k position selection.  [P3] selectGlm52DsaDevice, with the dense
  * fallback of the page's indexer (a context not longer than top_k is
  * attended densely).  For row b with n = row_len[b] > top_k, over the fp32

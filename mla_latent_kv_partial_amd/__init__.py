@@ -21,6 +21,7 @@ __all__ = [
     "MlaError", "LIB_PATH", "EXPORTS", "mla_rope_partial_interleaved", "mla_absorb_q", "mla_decode_latent_attn",
     "mla_decode_combine", "mla_absorb_v", "mla_prefill_reconstructed", "mla_version", "split_count",
     "plan_chunk_len", "prefill_workspace_bytes", "mla_dsa_topk_select", "mla_append_compressed",
+    "mla_o_proj",
 ]
 
 
@@ -294,4 +295,26 @@ def mla_append_compressed(kv_a: torch.Tensor, norm_weight: torch.Tensor, eps: fl
         float(eps), i64_array(_host_list(positions)), float(theta), _ptr(latent), latent.stride(0),
         latent.stride(1), _ptr(rope), rope.stride(0), rope.stride(1), int(slot), _stream(kv_a)),
         "mla_append_compressed")
+
+
+def mla_o_proj(ctx: torch.Tensor, w_o: torch.Tensor, out: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """ctx fp32 [..., in] (contiguous), w_o [hidden, in] -> out fp32 [..., hidden]."""
+    if ctx.dtype != torch.float32 or not ctx.is_contiguous() or not w_o.is_contiguous():
+        raise ValueError("ctx must be contiguous fp32 and w_o contiguous")
+    hidden, width = w_o.shape
+    if ctx.shape[-1] != width:
+        raise ValueError("ctx width != w_o input width")
+    rows = ctx.numel() // width
+    if out is None:
+        out = torch.empty((*ctx.shape[:-1], hidden), dtype=torch.float32, device=ctx.device)
+    need = ctypes.c_size_t(0)
+    check(lib.mla_o_proj_workspace_bytes(_dtype_code(w_o), rows, width, hidden, ctypes.byref(need)),
+          "mla_o_proj_workspace_bytes")
+    if need.value and (workspace is None or workspace.numel() * workspace.element_size() < need.value):
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=ctx.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib.mla_o_proj(_dtype_code(w_o), _ptr(ctx), rows, width, _ptr(w_o), hidden, _ptr(out), _ptr(workspace),
+                         nbytes, _stream(ctx)), "mla_o_proj")
+    return out
 

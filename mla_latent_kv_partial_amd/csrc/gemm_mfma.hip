@@ -1,0 +1,213 @@
+// MFMA NT GEMM for bf16 operands (both K-contiguous), fp32 accumulation,
+// bf16 or fp32 result.  Serves the prefill projections of page "mlx-bun
+// 0.0.11 -> 0.0.13", glm52-mla.ts (q_b_proj with the q RoPE of
+// Glm52Mla.project as an epilogue; the kv_b_proj expansion of
+// attendReconstructed) and the o_proj linear after the attention.
+#include <math.h>
+
+#include "cdna4.hpp"
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mla {
+namespace {
+
+constexpr int kDn = 128, kDr = 64;      // RoPE epilogue geometry: 128 no-PE + 64 rope columns per head
+constexpr int kQk = kDn + kDr;
+
+// ------------------------------------------------------------------ NT GEMM
+// C[m, n] = sum_k A[m, k] B[n, k]: both operands K-contiguous, bf16; fp32
+// accumulation; bf16 result (round to nearest even) or fp32.  Workgroup tile 128 x 128,
+// K step 64, 4 waves of 64 x 64 (4 x 4 MFMA blocks), 3-stage LDS ring filled
+// two K steps ahead.
+constexpr int kGT = 128;
+constexpr int kGK = 64;
+constexpr int kGRowChunks = kGK / 8 + 2;            // eight data chunks + two pad
+constexpr int kGRowBytes = kGRowChunks * 16;        // 160
+constexpr int kGOpChunks = kGT * kGRowChunks;       // 1280 per operand tile
+constexpr int kGOpDma = kGOpChunks / 64;            // 20 copies of 1 KB
+constexpr int kGOpBytes = kGOpChunks * 16;
+constexpr int kGStageBytes = 2 * kGOpBytes;         // A tile then B tile
+constexpr int kGStages = 3;
+constexpr int kGMaxDma = (kGOpDma + 3) / 4;         // copies per wave per operand
+
+__shared__ __attribute__((aligned(1024))) char g_gemm[kGStages * kGStageBytes];
+
+template <bool ROPE, bool OUT_F32>
+__global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(GemmNT p) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Tile order: workgroup ids go round-robin over the 8 XCDs; give each XCD
+  // a contiguous run of tiles, M fastest, so the workgroups that share an
+  // XCD's L2 also share B tiles.
+  const int tiles = p.m_tiles * p.n_tiles;
+  const int per_xcd = (tiles + 7) / 8;
+  int tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (tiles % 8 != 0) tile = blockIdx.x;   // uneven split: plain order
+  const int m0 = (tile % p.m_tiles) * kGT;
+  const int n0 = (tile / p.m_tiles) * kGT;
+
+  // copy plan: copy j of this wave moves chunk q = 64 (wave + 4 j) + lane of
+  // an operand tile: row q / 10, chunk q % 10 (chunks 8 and 9 are padding and
+  // re-read chunk 0); rows past the matrix edge re-read its last row.
+  const int n_dma = (kGOpDma - wave + 3) / 4;
+  const uint16_t* asrc[kGMaxDma];
+  const uint16_t* bsrc[kGMaxDma];
+#pragma unroll
+  for (int j = 0; j < kGMaxDma; ++j) {
+    const int q = 64 * (wave + 4 * j) + lane;
+    const int row = q / kGRowChunks;
+    int c = q - row * kGRowChunks;
+    c = c < 8 ? c : 0;
+    asrc[j] = p.a + static_cast<int64_t>(min(m0 + row, p.m - 1)) * p.lda + 8 * c;
+    bsrc[j] = p.b + static_cast<int64_t>(min(n0 + row, p.n - 1)) * p.ldb + 8 * c;
+  }
+  auto issue = [&](int s, int k0) {
+    const uint32_t da = lds_addr(g_gemm + s * kGStageBytes);
+    const uint32_t db = da + kGOpBytes;
+#pragma unroll
+    for (int j = 0; j < kGMaxDma - 1; ++j) {
+      dma16(asrc[j] + k0, da + (wave + 4 * j) * 1024);
+      dma16(bsrc[j] + k0, db + (wave + 4 * j) * 1024);
+    }
+    if (n_dma == kGMaxDma) {
+      dma16(asrc[kGMaxDma - 1] + k0, da + (wave + 4 * (kGMaxDma - 1)) * 1024);
+      dma16(bsrc[kGMaxDma - 1] + k0, db + (wave + 4 * (kGMaxDma - 1)) * 1024);
+    }
+  };
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int i16 = lane & 15, g = lane >> 4;
+  const uint32_t a_frag = (64 * wm + i16) * kGRowBytes + g * 16;
+  const uint32_t b_frag = kGOpBytes + (64 * wn + i16) * kGRowBytes + g * 16;
+
+  const int nk = p.k / kGK;
+  issue(0, 0);
+  if (nk > 1) issue(1, kGK);
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn) acc[bm][bn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int i = 0; i < nk; ++i) {
+    // tile i's copies done; those of tile i + 1 (issued one step ago) may fly
+    if (i + 1 < nk)
+      wait_vm_upto<2 * kGMaxDma>(2 * n_dma);
+    else
+      wait_vm<0>();
+    lds_barrier();
+    if (i + 2 < nk) issue((i + 2) % kGStages, (i + 2) * kGK);
+    const char* st = g_gemm + (i % kGStages) * kGStageBytes;
+#pragma unroll
+    for (int ks = 0; ks < kGK / 32; ++ks) {
+      bf16x8 af[4], bfr[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        af[t] = *reinterpret_cast<const bf16x8*>(st + a_frag + t * 16 * kGRowBytes + ks * 64);
+        bfr[t] = *reinterpret_cast<const bf16x8*>(st + b_frag + t * 16 * kGRowBytes + ks * 64);
+      }
+      // D^T blocks: lane (column m = i16, group g) receives C[m][n + 4g + (0..3)]
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+        for (int bn = 0; bn < 4; ++bn) acc[bm][bn] = mfma16x16x32(bfr[bn], af[bm], acc[bm][bn]);
+    }
+  }
+
+  // ---- epilogue: 4 consecutive columns per lane and block
+#pragma unroll
+  for (int bm = 0; bm < 4; ++bm) {
+    const int m = m0 + 64 * wm + 16 * bm + i16;
+    if (m >= p.m) continue;
+    uint16_t* crow = static_cast<uint16_t*>(p.c) + static_cast<int64_t>(m) * p.ldc;
+    float* frow = static_cast<float*>(p.c) + static_cast<int64_t>(m) * p.ldc;
+    double pos = 0.0;
+    if (ROPE) pos = static_cast<double>(p.off[m / p.tokens] + m % p.tokens);
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn) {
+      const int n = n0 + 64 * wn + 16 * bn + 4 * g;
+      if (n >= p.n) continue;
+      const f32x4 v = acc[bm][bn];
+      const int d = ROPE ? n % kQk : 0;
+      if (ROPE && d >= kDn) {
+        // pairs (v0, v1) and (v2, v3) are rope pairs q0 and q0 + 1 of the head
+        const int q0 = (d - kDn) >> 1;
+        uint16_t* head = crow + (n - d) + kDn;
+        uint16_t re[2], im[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float ang = static_cast<float>(pos * static_cast<double>(p.inv[q0 + e]));
+          double s, c;
+          sincos(static_cast<double>(ang), &s, &c);
+          const double a = v[2 * e], b = v[2 * e + 1];
+          re[e] = f64_to_bf16(a * c - b * s);
+          im[e] = f64_to_bf16(b * c + a * s);
+        }
+        *reinterpret_cast<uint32_t*>(head + q0) = re[0] | (static_cast<uint32_t>(re[1]) << 16);
+        *reinterpret_cast<uint32_t*>(head + kDr / 2 + q0) = im[0] | (static_cast<uint32_t>(im[1]) << 16);
+      } else if (OUT_F32) {
+        *reinterpret_cast<float4*>(frow + n) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+        const uint32_t lo = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+        const uint32_t hi = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+        *reinterpret_cast<uint2*>(crow + n) = make_uint2(lo, hi);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+bool gemm_nt_mfma_ok(const void* a, int64_t lda, const void* b, int64_t ldb, const void* c, int64_t ldc, int64_t m,
+                     int64_t n, int64_t k) {
+  auto al = [](const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15) == 0; };
+  return al(a) && al(b) && al(c) && k % kGK == 0 && k > 0 && lda % 8 == 0 && ldb % 8 == 0 && ldc % 4 == 0 &&
+         n % 4 == 0 && m > 0 && n > 0 && (m + kGT - 1) / kGT * ((n + kGT - 1) / kGT) < 0x7fffffffLL;
+}
+
+hipError_t launch_gemm_nt_mfma(const GemmNT& p0, bool rope, bool out_f32, hipStream_t stream) {
+  GemmNT p = p0;
+  p.m_tiles = (p.m + kGT - 1) / kGT;
+  p.n_tiles = (p.n + kGT - 1) / kGT;
+  const dim3 grid(p.m_tiles * p.n_tiles);
+  if (rope)
+    hipLaunchKernelGGL((gemm_nt_mfma_kernel<true, false>), grid, dim3(256), 0, stream, p);
+  else if (out_f32)
+    hipLaunchKernelGGL((gemm_nt_mfma_kernel<false, true>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((gemm_nt_mfma_kernel<false, false>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace mla
+
+namespace mla {
+namespace {
+
+// fp32 -> bf16 (round to nearest even), 4 elements per thread per step.
+__global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restrict__ x, uint16_t* __restrict__ y,
+                                                          int64_t n) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x * 4;
+  for (int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
+    if (i + 4 <= n) {
+      const float4 v = *reinterpret_cast<const float4*>(x + i);
+      const uint32_t lo = f32_to_bf16(v.x) | (static_cast<uint32_t>(f32_to_bf16(v.y)) << 16);
+      const uint32_t hi = f32_to_bf16(v.z) | (static_cast<uint32_t>(f32_to_bf16(v.w)) << 16);
+      *reinterpret_cast<uint2*>(y + i) = make_uint2(lo, hi);
+    } else {
+      for (int64_t j = i; j < n; ++j) y[j] = f32_to_bf16(x[j]);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_f32_to_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 1023) / 1024, 4096);
+  hipLaunchKernelGGL(f32_to_bf16_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream, x, y, n);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -121,6 +121,31 @@ struct TopkParams {
 };
 hipError_t launch_dsa_topk(const TopkParams& p, hipStream_t stream);
 
+// ------------------------------------------------------------------ GEMM (MFMA, bf16 operands)
+constexpr int kGemmRowsPerLaunch = 128;
+
+// C[m, n] = sum_k A[m, k] B[n, k], both operands bf16 and K-contiguous.
+struct GemmNT {
+  const uint16_t* a;
+  int64_t lda;
+  const uint16_t* b;
+  int64_t ldb;
+  void* c;                // bf16 or fp32, row stride ldc
+  int64_t ldc;
+  int32_t m, n, k;
+  int32_t m_tiles, n_tiles;   // filled by the launcher
+  // RoPE epilogue (q projection, heads of 128 no-PE + 64 rope columns): row m
+  // is token m % tokens of batch row m / tokens, rotated at off[row] + token.
+  int32_t tokens;
+  int64_t off[kGemmRowsPerLaunch];
+  float inv[32];
+};
+bool gemm_nt_mfma_ok(const void* a, int64_t lda, const void* b, int64_t ldb, const void* c, int64_t ldc, int64_t m,
+                     int64_t n, int64_t k);
+hipError_t launch_gemm_nt_mfma(const GemmNT& p, bool rope, bool out_f32, hipStream_t stream);
+// x (fp32, 16-byte aligned) -> y (bf16), round to nearest even.
+hipError_t launch_f32_to_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t stream);
+
 // ------------------------------------------------------------------ prefill
 struct PrefillParams {
   int32_t dtype;

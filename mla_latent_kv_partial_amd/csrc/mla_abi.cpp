@@ -240,6 +240,70 @@ int mla_decode_latent_attn(int32_t dtype, const void* q_lat, const void* q_rope,
   return ok();
 }
 
+namespace {
+
+// o_proj: the MFMA GEMM path (rows > 64) stages the context in bf16 in the
+// workspace; its size depends on the shapes only.
+bool o_proj_gemm_shape(int32_t dtype, int64_t rows, int32_t in_features, int32_t hidden) {
+  return dtype == MLA_DTYPE_BF16 && rows > 64 && in_features % 64 == 0 && in_features % 8 == 0 && hidden % 4 == 0;
+}
+
+size_t o_proj_need(int32_t dtype, int64_t rows, int32_t in_features, int32_t hidden) {
+  return o_proj_gemm_shape(dtype, rows, in_features, hidden)
+             ? (static_cast<size_t>(rows) * in_features * 2 + 255) / 256 * 256
+             : 0;
+}
+
+}  // namespace
+
+int mla_o_proj_workspace_bytes(int32_t dtype, int64_t rows, int32_t in_features, int32_t hidden, size_t* bytes) {
+  if (!valid_dtype(dtype)) return fail(MLA_ERR_ARG, "o_proj: unknown dtype %d", dtype);
+  if (rows < 0 || in_features < 1 || hidden < 1) return fail(MLA_ERR_ARG, "o_proj: rows >= 0, positive widths required");
+  if (!bytes) return fail(MLA_ERR_ARG, "o_proj: bytes is NULL");
+  *bytes = o_proj_need(dtype, rows, in_features, hidden);
+  return ok();
+}
+
+int mla_o_proj(int32_t dtype, const float* ctx, int64_t rows, int32_t in_features, const void* w_o, int32_t hidden,
+               float* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return fail(MLA_ERR_ARG, "o_proj: unknown dtype %d", dtype);
+  if (rows < 0 || in_features < 1 || hidden < 1) return fail(MLA_ERR_ARG, "o_proj: rows >= 0, positive widths required");
+  if (rows > 0x7fffffffLL) return fail(MLA_ERR_UNSUPPORTED, "o_proj: rows > 2^31-1");
+  if (rows == 0) return ok();
+  if (!ctx || !w_o || !out) return fail(MLA_ERR_ARG, "o_proj: NULL pointer");
+  const size_t need = o_proj_need(dtype, rows, in_features, hidden);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(MLA_ERR_WORKSPACE, "o_proj: workspace of %zu bytes required", need);
+  if (need > 0 && reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(MLA_ERR_WORKSPACE, "o_proj: workspace not 256-byte aligned");
+  mla::AbsorbVParams v{ctx, w_o, out, static_cast<int32_t>(rows), 1, 0, hidden, in_features};
+  hipError_t e;
+  if (need > 0 && (reinterpret_cast<uintptr_t>(ctx) & 15) == 0 &&
+      mla::gemm_nt_mfma_ok(workspace, in_features, w_o, in_features, out, hidden, rows, hidden, in_features)) {
+    uint16_t* a = static_cast<uint16_t*>(workspace);
+    e = mla::launch_f32_to_bf16(ctx, a, rows * in_features, stream);
+    if (e == hipSuccess) {
+      mla::GemmNT g{};
+      g.a = a;
+      g.lda = in_features;
+      g.b = static_cast<const uint16_t*>(w_o);
+      g.ldb = in_features;
+      g.c = out;
+      g.ldc = hidden;
+      g.m = static_cast<int32_t>(rows);
+      g.n = hidden;
+      g.k = in_features;
+      e = mla::launch_gemm_nt_mfma(g, false, true, stream);
+    }
+  } else {
+    // weight-streaming contraction of absorb_v with a single "head" (MFMA for
+    // bf16 weights of a suitable shape, generic kernel otherwise)
+    e = mla::launch_absorb_v(dtype, v, stream);
+  }
+  if (e != hipSuccess) return device(e, "o_proj launch");
+  return ok();
+}
+
 int mla_append_compressed(int32_t dtype, const void* kv_a, int64_t kv_a_stride_b, int64_t kv_a_stride_t,
                           int32_t batch, int32_t tokens, int32_t kv_lora_rank, int32_t rope_dim,
                           const void* norm_weight, float eps, const int64_t* positions, double theta,

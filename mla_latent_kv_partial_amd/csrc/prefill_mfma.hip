@@ -7,18 +7,19 @@
 // glm52-mla.ts: keys before the row's left pad are masked.
 //
 // Three kernels over a bf16 workspace:
-//   gemm_nt_mfma_kernel<true>   Q  [rows*T, H*192] = c_q . w_q_b^T, with the
-//                               RoPE of each head's last 64 columns applied to
-//                               the fp32 accumulators before rounding;
-//   gemm_nt_mfma_kernel<false>  KV [rows*K, H*256] = latent . w_kv_b^T (per head
+//   NT GEMM with RoPE epilogue  Q  [rows*T, H*192] = c_q . w_q_b^T, the RoPE of
+//                               each head's last 64 columns applied to the
+//                               fp32 accumulators before rounding;
+//   NT GEMM                     KV [rows*K, H*256] = latent . w_kv_b^T (per head
 //                               k_nope then v);
 //   flash_attn_kernel           one workgroup per (head, 128 queries): causal
 //                               online-softmax attention, K/V tiles of 32 keys
 //                               streamed through LDS, fp32 context out.
-// Both contractions run on v_mfma_f32_16x16x32_bf16.  Operand tiles move
-// HBM -> LDS with global_load_lds_dwordx4 into rows padded to an odd number of
-// 32-byte units, which makes the 16-byte fragment reads of 16 consecutive rows
-// free of bank conflicts (measured with the LDS bank-conflict counter).
+// The GEMMs live in gemm_mfma.hip.  The attention runs on
+// v_mfma_f32_16x16x32_bf16; K/V tiles move HBM -> LDS with
+// global_load_lds_dwordx4 into rows padded to an odd number of 32-byte units,
+// which makes the 16-byte fragment reads of 16 consecutive rows free of bank
+// conflicts (measured with the LDS bank-conflict counter).
 #include <math.h>
 
 #include "cdna4.hpp"
@@ -36,162 +37,7 @@ namespace {
 constexpr int kDn = 128, kDr = 64, kDv = 128;
 constexpr int kQk = kDn + kDr;          // 192
 constexpr int kKvw = kDn + kDv;         // 256
-constexpr int kBatchPerLaunch = 128;    // per-row tables travel in the kernel arguments
-
-// ------------------------------------------------------------------ NT GEMM
-// C[m, n] = sum_k A[m, k] B[n, k]: both operands K-contiguous, bf16; fp32
-// accumulation; bf16 result (round to nearest even).  Workgroup tile 128 x 128,
-// K step 64, 4 waves of 64 x 64 (4 x 4 MFMA blocks), 3-stage LDS ring filled
-// two K steps ahead.
-constexpr int kGT = 128;
-constexpr int kGK = 64;
-constexpr int kGRowChunks = kGK / 8 + 2;            // eight data chunks + two pad
-constexpr int kGRowBytes = kGRowChunks * 16;        // 160
-constexpr int kGOpChunks = kGT * kGRowChunks;       // 1280 per operand tile
-constexpr int kGOpDma = kGOpChunks / 64;            // 20 copies of 1 KB
-constexpr int kGOpBytes = kGOpChunks * 16;
-constexpr int kGStageBytes = 2 * kGOpBytes;         // A tile then B tile
-constexpr int kGStages = 3;
-constexpr int kGMaxDma = (kGOpDma + 3) / 4;         // copies per wave per operand
-
-__shared__ __attribute__((aligned(1024))) char g_gemm[kGStages * kGStageBytes];
-
-struct GemmNT {
-  const uint16_t* a;
-  int64_t lda;
-  const uint16_t* b;
-  int64_t ldb;
-  uint16_t* c;
-  int64_t ldc;
-  int32_t m, n, k;
-  int32_t m_tiles, n_tiles;
-  // RoPE epilogue: row m is token m % tokens of batch row m / tokens; columns
-  // d = n % 192 >= 128 of a head hold its interleaved rope pairs.
-  int32_t tokens;
-  int64_t off[kBatchPerLaunch];
-  float inv[kDr / 2];
-};
-
-template <bool ROPE>
-__global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(GemmNT p) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // Tile order: workgroup ids go round-robin over the 8 XCDs; give each XCD
-  // a contiguous run of tiles, M fastest, so the workgroups that share an
-  // XCD's L2 also share B tiles.
-  const int tiles = p.m_tiles * p.n_tiles;
-  const int per_xcd = (tiles + 7) / 8;
-  int tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (tiles % 8 != 0) tile = blockIdx.x;   // uneven split: plain order
-  const int m0 = (tile % p.m_tiles) * kGT;
-  const int n0 = (tile / p.m_tiles) * kGT;
-
-  // copy plan: copy j of this wave moves chunk q = 64 (wave + 4 j) + lane of
-  // an operand tile: row q / 10, chunk q % 10 (chunks 8 and 9 are padding and
-  // re-read chunk 0); rows past the matrix edge re-read its last row.
-  const int n_dma = (kGOpDma - wave + 3) / 4;
-  const uint16_t* asrc[kGMaxDma];
-  const uint16_t* bsrc[kGMaxDma];
-#pragma unroll
-  for (int j = 0; j < kGMaxDma; ++j) {
-    const int q = 64 * (wave + 4 * j) + lane;
-    const int row = q / kGRowChunks;
-    int c = q - row * kGRowChunks;
-    c = c < 8 ? c : 0;
-    asrc[j] = p.a + static_cast<int64_t>(min(m0 + row, p.m - 1)) * p.lda + 8 * c;
-    bsrc[j] = p.b + static_cast<int64_t>(min(n0 + row, p.n - 1)) * p.ldb + 8 * c;
-  }
-  auto issue = [&](int s, int k0) {
-    const uint32_t da = lds_addr(g_gemm + s * kGStageBytes);
-    const uint32_t db = da + kGOpBytes;
-#pragma unroll
-    for (int j = 0; j < kGMaxDma - 1; ++j) {
-      dma16(asrc[j] + k0, da + (wave + 4 * j) * 1024);
-      dma16(bsrc[j] + k0, db + (wave + 4 * j) * 1024);
-    }
-    if (n_dma == kGMaxDma) {
-      dma16(asrc[kGMaxDma - 1] + k0, da + (wave + 4 * (kGMaxDma - 1)) * 1024);
-      dma16(bsrc[kGMaxDma - 1] + k0, db + (wave + 4 * (kGMaxDma - 1)) * 1024);
-    }
-  };
-
-  const int wm = wave >> 1, wn = wave & 1;
-  const int i16 = lane & 15, g = lane >> 4;
-  const uint32_t a_frag = (64 * wm + i16) * kGRowBytes + g * 16;
-  const uint32_t b_frag = kGOpBytes + (64 * wn + i16) * kGRowBytes + g * 16;
-
-  const int nk = p.k / kGK;
-  issue(0, 0);
-  if (nk > 1) issue(1, kGK);
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int bm = 0; bm < 4; ++bm)
-#pragma unroll
-    for (int bn = 0; bn < 4; ++bn) acc[bm][bn] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int i = 0; i < nk; ++i) {
-    // tile i's copies done; those of tile i + 1 (issued one step ago) may fly
-    if (i + 1 < nk)
-      wait_vm_upto<2 * kGMaxDma>(2 * n_dma);
-    else
-      wait_vm<0>();
-    lds_barrier();
-    if (i + 2 < nk) issue((i + 2) % kGStages, (i + 2) * kGK);
-    const char* st = g_gemm + (i % kGStages) * kGStageBytes;
-#pragma unroll
-    for (int ks = 0; ks < kGK / 32; ++ks) {
-      bf16x8 af[4], bfr[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        af[t] = *reinterpret_cast<const bf16x8*>(st + a_frag + t * 16 * kGRowBytes + ks * 64);
-        bfr[t] = *reinterpret_cast<const bf16x8*>(st + b_frag + t * 16 * kGRowBytes + ks * 64);
-      }
-      // D^T blocks: lane (column m = i16, group g) receives C[m][n + 4g + (0..3)]
-#pragma unroll
-      for (int bm = 0; bm < 4; ++bm)
-#pragma unroll
-        for (int bn = 0; bn < 4; ++bn) acc[bm][bn] = mfma16x16x32(bfr[bn], af[bm], acc[bm][bn]);
-    }
-  }
-
-  // ---- epilogue: 4 consecutive columns per lane and block
-#pragma unroll
-  for (int bm = 0; bm < 4; ++bm) {
-    const int m = m0 + 64 * wm + 16 * bm + i16;
-    if (m >= p.m) continue;
-    uint16_t* crow = p.c + static_cast<int64_t>(m) * p.ldc;
-    double pos = 0.0;
-    if (ROPE) pos = static_cast<double>(p.off[m / p.tokens] + m % p.tokens);
-#pragma unroll
-    for (int bn = 0; bn < 4; ++bn) {
-      const int n = n0 + 64 * wn + 16 * bn + 4 * g;
-      if (n >= p.n) continue;
-      const f32x4 v = acc[bm][bn];
-      const int d = ROPE ? n % kQk : 0;
-      if (ROPE && d >= kDn) {
-        // pairs (v0, v1) and (v2, v3) are rope pairs q0 and q0 + 1 of the head
-        const int q0 = (d - kDn) >> 1;
-        uint16_t* head = crow + (n - d) + kDn;
-        uint16_t re[2], im[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const float ang = static_cast<float>(pos * static_cast<double>(p.inv[q0 + e]));
-          double s, c;
-          sincos(static_cast<double>(ang), &s, &c);
-          const double a = v[2 * e], b = v[2 * e + 1];
-          re[e] = f64_to_bf16(a * c - b * s);
-          im[e] = f64_to_bf16(b * c + a * s);
-        }
-        *reinterpret_cast<uint32_t*>(head + q0) = re[0] | (static_cast<uint32_t>(re[1]) << 16);
-        *reinterpret_cast<uint32_t*>(head + kDr / 2 + q0) = im[0] | (static_cast<uint32_t>(im[1]) << 16);
-      } else {
-        const uint32_t lo = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-        const uint32_t hi = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
-        *reinterpret_cast<uint2*>(crow + n) = make_uint2(lo, hi);
-      }
-    }
-  }
-}
+constexpr int kBatchPerLaunch = kGemmRowsPerLaunch;   // per-row tables travel in the kernel arguments
 
 // ------------------------------------------------------------------ attention
 // Workgroup = (head, 128 consecutive queries, batch row); wave w owns queries
@@ -391,7 +237,8 @@ size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 
 bool prefill_mfma_supported(const PrefillParams& p) {
   auto al = [](const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15) == 0; };
-  return p.dtype == kBF16 && p.dn == kDn && p.dr == kDr && p.dv == kDv && p.ql % kGK == 0 && p.r % kGK == 0 &&
+  // 64: the K step of the GEMMs
+  return p.dtype == kBF16 && p.dn == kDn && p.dr == kDr && p.dv == kDv && p.ql % 64 == 0 && p.r % 64 == 0 &&
          al(p.q_c) && al(p.w_qb) && al(p.latent) && al(p.rope) && al(p.w_kvb) && al(p.ctx) && p.heads <= 65535;
 }
 
@@ -423,13 +270,10 @@ hipError_t launch_prefill_mfma(const PrefillParams& p, hipStream_t stream) {
     gq.m = rows * p.tokens;
     gq.n = p.heads * kQk;
     gq.k = p.ql;
-    gq.m_tiles = (gq.m + kGT - 1) / kGT;
-    gq.n_tiles = (gq.n + kGT - 1) / kGT;
     gq.tokens = p.tokens;
     for (int i = 0; i < rows; ++i) gq.off[i] = p.q_offsets[b0 + i];
     for (int i = 0; i < kDr / 2; ++i) gq.inv[i] = inv[i];
-    hipLaunchKernelGGL(gemm_nt_mfma_kernel<true>, dim3(gq.m_tiles * gq.n_tiles), dim3(256), 0, stream, gq);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_gemm_nt_mfma(gq, true, false, stream);
     if (e != hipSuccess) return e;
     // KV expansion
     GemmNT gk{};
@@ -442,16 +286,13 @@ hipError_t launch_prefill_mfma(const PrefillParams& p, hipStream_t stream) {
     gk.m = rows * p.keys;
     gk.n = p.heads * kKvw;
     gk.k = p.r;
-    gk.m_tiles = (gk.m + kGT - 1) / kGT;
-    gk.n_tiles = (gk.n + kGT - 1) / kGT;
     gk.tokens = p.keys;
-    hipLaunchKernelGGL(gemm_nt_mfma_kernel<false>, dim3(gk.m_tiles * gk.n_tiles), dim3(256), 0, stream, gk);
-    e = hipGetLastError();
+    e = launch_gemm_nt_mfma(gk, false, false, stream);
     if (e != hipSuccess) return e;
     // attention
     AttnMfma ap{};
-    ap.q = gq.c;
-    ap.kv = gk.c;
+    ap.q = static_cast<const uint16_t*>(gq.c);
+    ap.kv = static_cast<const uint16_t*>(gk.c);
     ap.rope = rope + static_cast<int64_t>(b0) * p.keys * kDr;
     ap.ctx = p.ctx + static_cast<int64_t>(b0) * p.tokens * p.heads * kDv;
     ap.tokens = p.tokens;

@@ -166,3 +166,18 @@ def test_append_rejections(kw, code):
 def test_append_empty_is_a_no_op():
     assert _append(batch=0, pos=[0]) == OK
     assert _append(tokens=0) == OK
+
+
+def test_o_proj_workspace_query_and_rejections():
+    need = ctypes.c_size_t(7)
+    assert lib.mla_o_proj_workspace_bytes(1, 8, 8192, 6144, ctypes.byref(need)) == OK and need.value == 0
+    assert lib.mla_o_proj_workspace_bytes(1, 4096, 8192, 6144, ctypes.byref(need)) == OK
+    assert need.value == 4096 * 8192 * 2
+    assert lib.mla_o_proj_workspace_bytes(0, 4096, 8192, 6144, ctypes.byref(need)) == OK and need.value == 0
+    assert lib.mla_o_proj_workspace_bytes(3, 8, 8, 8, ctypes.byref(need)) == ARG
+    assert lib.mla_o_proj(1, FAKE, -1, 8, FAKE, 8, FAKE, None, 0, None) == ARG
+    assert lib.mla_o_proj(1, None, 8, 8, FAKE, 8, FAKE, None, 0, None) == ARG
+    # the GEMM path needs its workspace
+    assert lib.mla_o_proj(1, FAKE, 4096, 8192, FAKE, 6144, FAKE, None, 0, None) == WS
+    assert lib.mla_o_proj(1, FAKE, 4096, 8192, FAKE, 6144, FAKE, FAKE, 100, None) == WS
+    assert lib.mla_o_proj(1, FAKE, 0, 8192, FAKE, 6144, FAKE, None, 0, None) == OK

@@ -15,7 +15,7 @@ from conftest import build_module
 
 B = build_module()
 
-SRC = ["decode_mfma.hip", "absorb_mfma.hip"]
+SRC = ["decode_mfma.hip", "absorb_mfma.hip", "gemm_mfma.hip", "prefill_mfma.hip"]
 
 
 def _asm(name, tmp_path):
@@ -45,5 +45,5 @@ def test_no_spills(name, tmp_path):
     text = _asm(name, tmp_path)
     spills = [int(v) for v in re.findall(r"\.vgpr_spill_count:\s+(\d+)", text)]
     names = re.findall(r"\.name:\s+(\S+)", text)
-    hot = [s for n, s in zip(names, spills) if "ILi4E" in n or "absorb" in n]
+    hot = [s for n, s in zip(names, spills) if any(k in n for k in ("ILi4E", "absorb", "gemm", "flash"))]
     assert hot and max(hot) == 0, list(zip(names, spills))
