@@ -65,11 +65,13 @@ def parse():
 class DecodeLayer:
     """Device tensors of one layer instance of a decode workload, packed cache [B, W, 576]."""
 
-    def __init__(self, cfg, layer, torch, cf, dev, batch=None):
+    def __init__(self, cfg, layer, torch, cf, dev, batch=None, spare_slots=0):
         inp = cf.decode_inputs(cfg, layer=layer, batch=batch)
         self.inp = inp
         import numpy as np
         cache = np.concatenate([inp.latent, inp.rope], axis=-1)
+        if spare_slots:   # room to append the step's token at slot = width
+            cache = np.concatenate([cache, np.zeros((cache.shape[0], spare_slots, cache.shape[2]), cache.dtype)], 1)
         self.cache = torch.from_numpy(cache.view(np.int16)).to(dev).view(torch.bfloat16)
         del cache
         self.latent = self.cache[..., : cfg.kv_lora_rank]
@@ -90,6 +92,7 @@ class DecodeLayer:
         self.lse = torch.empty((b, cfg.heads), dtype=torch.float32, device=dev)
         self.ctx = torch.empty((b, cfg.heads * cfg.v_head), dtype=torch.float32, device=dev)
         self.cfg = cfg
+        self.layer_id = layer
         # drop the host copies of the large arrays
         inp.latent = inp.rope = None
 
@@ -117,6 +120,40 @@ class DecodeLayer:
         self.attn(mla)
         mla.mla_decode_combine(self.part_o, self.part_lse, self.n_splits, o_lat=self.o_lat, lse=self.lse)
         mla.mla_absorb_v(self.o_lat, self.w, c.qk_nope, c.v_head, ctx=self.ctx)
+
+    def full_layer_setup(self, torch, cf, dev, hidden):
+        """Tensors of the whole layer around the hot path: the kv_a output of the
+        step's token (appended at slot = width, each row at its own RoPE
+        position) and the o_proj weight (synthetic hidden size)."""
+        import numpy as np
+        from synth import generators as gen
+        c = self.cfg
+        b = len(self.kv_len)
+        r, dr = c.kv_lora_rank, c.qk_rope
+        t = lambda x: torch.from_numpy(cf.store(x, cf.BF16).view(np.int16)).to(dev).view(torch.bfloat16)
+        self.kv_a = t(gen.normal_f32(c.config_id, gen.T_MISC, (b, 1, r + dr), layer=500 + self.layer_id))
+        self.norm_w = t(np.float32(1) + gen.normal_f32(c.config_id, gen.T_MISC, (r,), std=0.1, layer=600))
+        self.w_o = t(gen.normal_f32(c.config_id, gen.T_MISC, (hidden, c.heads * c.v_head),
+                                    std=(c.heads * c.v_head) ** -0.5, layer=700 + self.layer_id))
+        self.out = torch.empty((b, hidden), dtype=torch.float32, device=dev)
+        self.slot = self.cache.shape[1] - 1
+        self.kv_len_new = [n + 1 for n in self.kv_len]
+
+    def full_step(self, mla):
+        """append -> RoPE(q) -> absorb_q -> attention over kv_len + 1 -> combine -> absorb_v -> o_proj."""
+        c = self.cfg
+        b = len(self.kv_len)
+        mla.mla_append_compressed(self.kv_a, self.norm_w, 1e-6, self.offsets, c.theta, self.latent, self.rope,
+                                  self.slot)
+        mla.mla_rope_partial_interleaved(self.q_rope_raw.view(b, 1, c.heads, c.qk_rope), self.offsets, c.qk_rope,
+                                         c.theta, out=self.q_rope.view(b, 1, c.heads, c.qk_rope))
+        mla.mla_absorb_q(self.q_nope, self.w, c.v_head, q_lat=self.q_lat)
+        mla.mla_decode_latent_attn(self.q_lat, self.q_rope, self.latent, self.rope, self.kv_len_new,
+                                   c.softmax_scale, self.chunk, part_o=self.part_o, part_lse=self.part_lse,
+                                   s_max=self.s_max)
+        mla.mla_decode_combine(self.part_o, self.part_lse, self.n_splits, o_lat=self.o_lat, lse=self.lse)
+        mla.mla_absorb_v(self.o_lat, self.w, c.qk_nope, c.v_head, ctx=self.ctx)
+        mla.mla_o_proj(self.ctx, self.w_o, out=self.out)
 
     @property
     def cache_bytes(self):
@@ -205,11 +242,13 @@ def cpu_baseline(cf, oracle, layer0, budget_s=12.0):
     }
 
 
-def prefill_leg(torch, mla, cf, dev):
-    """The 4096-token reconstructed causal prefill: ms per call and algorithmic TFLOP/s."""
+def prefill_leg(torch, mla, cf, dev, tokens=None, left_pad=0):
+    """Reconstructed causal prefill over 4096 keys: ms per call and algorithmic TFLOP/s.
+    tokens < 4096: the last `tokens` queries over a cached prefix of 4096 - tokens
+    keys (chunked prefill); left_pad: keys before it are masked (padded row)."""
     pcfg = cf.PREFILL_BF16
     import numpy as np
-    pin = cf.prefill_inputs(pcfg)
+    pin = cf.prefill_inputs(pcfg, tokens=tokens or pcfg.tokens, keys=pcfg.keys)
     t = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
     c_q, w_qb, latent, w_kvb = t(pin.c_q), t(pin.w_qb), t(pin.latent), t(pin.w_kvb)
     rope = t(pin.k_rope_raw)
@@ -217,21 +256,40 @@ def prefill_leg(torch, mla, cf, dev):
     need = mla.prefill_workspace_bytes(torch.bfloat16, 1, pcfg.tokens, pcfg.keys, pcfg.heads, pcfg.q_lora_rank,
                                        pcfg.kv_lora_rank, pcfg.qk_nope, pcfg.qk_rope, pcfg.v_head)
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
-    ctx = torch.empty((1, pcfg.tokens, pcfg.heads * pcfg.v_head), dtype=torch.float32, device=dev)
+    tt, kk, h = pin.c_q.shape[1], pin.latent.shape[1], pcfg.heads
+    ctx = torch.empty((1, tt, pcfg.heads * pcfg.v_head), dtype=torch.float32, device=dev)
+    offs = [int(o) for o in pin.q_offsets]
     run = lambda: mla.mla_prefill_reconstructed(c_q, w_qb, latent, rope, w_kvb, pcfg.heads, pcfg.qk_nope,
-                                                pcfg.qk_rope, pcfg.v_head, [0], pcfg.theta, workspace=ws,
-                                                ctx=ctx)
+                                                pcfg.qk_rope, pcfg.v_head, offs, pcfg.theta, workspace=ws,
+                                                ctx=ctx, left_pad=[left_pad] if left_pad else None)
     ms_p = time_graph(torch, run, 3, 1)[0]
-    tt, kk, h = pcfg.tokens, pcfg.keys, pcfg.heads
+    prefix = kk - tt
+    visible = sum(max(0, prefix + t + 1 - left_pad) for t in range(tt))   # causal pairs past the pad
     flops = (2 * tt * pcfg.q_lora_rank * h * (pcfg.qk_nope + pcfg.qk_rope)
              + 2 * kk * pcfg.kv_lora_rank * h * (pcfg.qk_nope + pcfg.v_head)
-             + 2 * h * (tt * (tt + 1) // 2) * (pcfg.qk_nope + pcfg.qk_rope + pcfg.v_head))
-    out = {"tokens": tt, "ms": ms_p, "algorithmic_GFLOP": flops / 1e9,
+             + 2 * h * visible * (pcfg.qk_nope + pcfg.qk_rope + pcfg.v_head))
+    out = {"tokens": tt, "keys": kk, "left_pad": left_pad, "ms": ms_p, "algorithmic_GFLOP": flops / 1e9,
            "TFLOPs": flops / (ms_p * 1e-3) / 1e12,
            "frac_bf16_mfma": flops / (ms_p * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
     del c_q, w_qb, latent, w_kvb, rope, ws, ctx
     torch.cuda.empty_cache()
     return out
+
+
+def o_proj_prefill_leg(torch, mla, cf, dev, rows=4096, hidden=6144):
+    """o_proj after a 4096-token prefill (hidden size synthetic): TFLOP/s."""
+    import numpy as np
+    from synth import generators as gen
+    width = 64 * 128
+    ctx = torch.from_numpy(gen.normal_f32(5, gen.T_MISC, (rows, width))).to(dev)
+    w = torch.from_numpy(cf.store(gen.normal_f32(5, gen.T_MISC, (hidden, width), std=width ** -0.5, layer=1),
+                                  cf.BF16).view(np.int16)).to(dev).view(torch.bfloat16)
+    out = torch.empty((rows, hidden), dtype=torch.float32, device=dev)
+    ws = torch.empty(rows * width * 2, dtype=torch.uint8, device=dev)
+    ms = time_graph(torch, lambda: mla.mla_o_proj(ctx, w, out=out, workspace=ws), 3, 1)[0]
+    flops = 2 * rows * width * hidden
+    return {"rows": rows, "in": width, "hidden": hidden, "ms": ms, "TFLOPs": flops / (ms * 1e-3) / 1e12,
+            "frac_bf16_mfma": flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
 
 
 def main():
@@ -361,6 +419,26 @@ def main():
                              "scores_GBps": args.layers * n_ctx * 4 / (ms_sel * 1e-3) / 1e9}
         del scores, sel_buf
         extra["prefill"] = prefill_leg(torch, mla, cf, dev)
+        # the whole layer around the hot path: append + chain + o_proj (hidden 6144, synthetic)
+        fl = [DecodeLayer(cfg, l, torch, cf, dev, spare_slots=1) for l in range(args.layers)]
+        for ly in fl:
+            ly.n_att = [n + 1 for n in ly.n_att]   # attention covers kv_len + 1 tokens
+            ly.plan(mla, slots, torch, dev)
+            ly.full_layer_setup(torch, cf, dev, hidden=6144)
+        ms_full, _ = time_graph(torch, lambda: [ly.full_step(mla) for ly in fl], args.steps, args.warmup)
+        ms_oproj = time_graph(torch, lambda: [mla.mla_o_proj(ly.ctx, ly.w_o, out=ly.out) for ly in fl],
+                              args.steps, args.warmup)[0] / len(fl)
+        extra["decode_full_layer"] = {
+            "layers": len(fl), "hidden": 6144, "ms_per_step": ms_full,
+            "rows_layers_per_s": rows * len(fl) / (ms_full * 1e-3),
+            "chain": "append -> rope -> absorb_q -> latent_attn -> combine -> absorb_v -> o_proj",
+            "o_proj_us": ms_oproj * 1e3,
+            "o_proj_weight_GBps": 6144 * cfg.heads * cfg.v_head * 2 / (ms_oproj * 1e-3) / 1e9}
+        del fl
+        torch.cuda.empty_cache()
+        extra["prefill_chunked"] = prefill_leg(torch, mla, cf, dev, tokens=1024, left_pad=0)
+        extra["prefill_left_padded"] = prefill_leg(torch, mla, cf, dev, tokens=4096, left_pad=1024)
+        extra["o_proj_prefill"] = o_proj_prefill_leg(torch, mla, cf, dev)
         result["extra"] = extra
 
     if args.copy_calibration:

@@ -29,7 +29,7 @@ constexpr int kVCols = 32;      // absorb_v output columns per workgroup
 __device__ __forceinline__ int swz(int d) { return ((d & 3) << 1) ^ (((d >> 3) & 1) << 3); }
 
 __shared__ __attribute__((aligned(1024))) char g_wtile[256 * kQCols * 2];   // up to dn = 256 rows
-__shared__ float g_vsum[4][16][kVCols + 1];
+__shared__ float g_vsum[8][16][kVCols + 1];   // per wave, up to 8 waves
 
 __global__ __launch_bounds__(256) void absorb_q_mfma_kernel(AbsorbQParams p) {
   const int lane = threadIdx.x & 63;
@@ -85,19 +85,23 @@ __global__ __launch_bounds__(256) void absorb_q_mfma_kernel(AbsorbQParams p) {
   }
 }
 
-__global__ __launch_bounds__(256) void absorb_v_mfma_kernel(AbsorbVParams p) {
+// NB 16-column blocks per workgroup, NWV waves splitting the latent axis.
+template <int NB, int NWV>
+__global__ __launch_bounds__(NWV * 64) void absorb_v_mfma_kernel(AbsorbVParams p) {
+  constexpr int kCols = 16 * NB;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int v0 = blockIdx.x * kVCols;
+  const int v0 = blockIdx.x * kCols;
   const int h = blockIdx.y;
   const int m = lane & 15, g = lane >> 4;
-  const int kq = p.r / 4;                   // latent range of this wave
+  const int kq = p.r / NWV;                 // latent range of this wave (a multiple of 32)
   const uint16_t* w = static_cast<const uint16_t*>(p.w) +
                       (static_cast<int64_t>(h) * (p.dn + p.dv) + p.dn + v0) * p.r + wave * kq;
   for (int b0 = 0; b0 < p.batch; b0 += 16) {
     const int b = b0 + m;
     const float* o = p.o_lat + (static_cast<int64_t>(b) * p.heads + h) * p.r + wave * kq;
-    f32x4 acc[2] = {};
+    f32x4 acc[NB] = {};
+#pragma unroll 4
     for (int ks = 0; ks < kq / 32; ++ks) {
       bf16x8 hi = bf16x8{}, lo = bf16x8{};
       if (b < p.batch) {
@@ -111,7 +115,7 @@ __global__ __launch_bounds__(256) void absorb_v_mfma_kernel(AbsorbVParams p) {
         lo = to_bf16x8(ru, rv);
       }
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+      for (int nb = 0; nb < NB; ++nb) {
         // B[k = latent 32ks + 8g .. +8][n = value column 16nb + m]
         const bf16x8 bw = *reinterpret_cast<const bf16x8*>(w + static_cast<int64_t>(16 * nb + m) * p.r + 32 * ks + 8 * g);
         acc[nb] = mfma16x16x32(hi, bw, acc[nb]);
@@ -120,15 +124,17 @@ __global__ __launch_bounds__(256) void absorb_v_mfma_kernel(AbsorbVParams p) {
     }
     // partial sums of this wave: lane (column m, group g) holds rows 4g + i
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) g_vsum[wave][4 * g + i][16 * nb + m] = acc[nb][i];
     __syncthreads();
-    for (int e = threadIdx.x; e < 16 * kVCols; e += 256) {
-      const int row = e / kVCols, col = e % kVCols;
+    for (int e = threadIdx.x; e < 16 * kCols; e += NWV * 64) {
+      const int row = e / kCols, col = e % kCols;
       const int bb = b0 + row;
       if (bb < p.batch) {
-        const float sum = g_vsum[0][row][col] + g_vsum[1][row][col] + g_vsum[2][row][col] + g_vsum[3][row][col];
+        float sum = 0.f;
+#pragma unroll
+        for (int wv = 0; wv < NWV; ++wv) sum += g_vsum[wv][row][col];
         p.ctx[static_cast<int64_t>(bb) * p.heads * p.dv + static_cast<int64_t>(h) * p.dv + v0 + col] = sum;
       }
     }
@@ -155,7 +161,12 @@ hipError_t launch_absorb_q_mfma(const AbsorbQParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_absorb_v_mfma(const AbsorbVParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(absorb_v_mfma_kernel, dim3(p.dv / kVCols, p.heads), dim3(256), 0, stream, p);
+  // 32 columns and 4 waves per workgroup while that fills the CUs; otherwise
+  // 16 columns and 8 waves (a long latent axis over few heads, as in o_proj).
+  if (static_cast<int64_t>(p.dv / kVCols) * p.heads >= 256 || p.r % (8 * 32) != 0)
+    hipLaunchKernelGGL((absorb_v_mfma_kernel<2, 4>), dim3(p.dv / kVCols, p.heads), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((absorb_v_mfma_kernel<1, 8>), dim3(p.dv / 16, p.heads), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -9,16 +9,20 @@
 //               ascending, then the other selected positions, ascending.
 //
 // One workgroup of 1024 threads per selected row, no workspace:
-//   1. radix select, 8 bits per pass from the top: a 256-bin LDS histogram of
-//      the keys that match the prefix found so far locates the byte of the
-//      top_k-th smallest key K*; at the end, m = how many of the keys equal
-//      to K* are selected (the first m by position);
-//   2. one pass counts n0 = selected positions strictly above the threshold
-//      (keys below K* whose score is > the score of K*; the threshold is the
-//      score with key K*, which is the minimum selected score);
-//   3. one ordered pass over the positions in chunks of 1024: block-wide
-//      exclusive scans (wave ballots + per-wave totals in LDS) of the tie and
-//      class flags give every selected position its output slot.
+//   1. radix select with digits of 12, 12 and 8 bits from the top, over
+//      coalesced chunks of the row: an LDS histogram of the keys that match
+//      the prefix found so far locates the digit of the top_k-th smallest key
+//      K*; at the end, m = how many of the keys equal to K* are selected (the
+//      first m by position);
+//   2. wave w owns a contiguous run of positions, swept 64 at a time: a first
+//      sweep counts the class-0 positions (key < K* and score > threshold; the
+//      threshold is the score with key K*, the minimum selected score), the
+//      other positions below K*, and the ties (key == K*); the 16 wave counts
+//      give each wave its starting ranks; a second sweep writes: class 0 at
+//      its class-0 rank, class 1 after all n0 class-0 positions at (lower
+//      class-1 positions before it) + min(ties before it, m), since the
+//      selected ties are the first m.  Ranks inside 64 positions come from
+//      ballots.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -27,6 +31,7 @@ namespace {
 
 constexpr int kTT = 1024;
 constexpr int kTW = kTT / kWave;   // 16 waves
+constexpr int kU = 32;             // scores per thread loaded together in every pass (128 KB in flight per CU)
 
 __device__ __forceinline__ uint32_t rank_key(float f) {
   const uint32_t u = __float_as_uint(f);
@@ -44,65 +49,51 @@ __device__ __forceinline__ int lanes_below(uint64_t ballot) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(ballot), 0u));
 }
 
-// Exclusive block scan of three flags; returns the block totals in tot[].
-// Contains two barriers; every thread of the block must call it.
-__device__ __forceinline__ void block_scan3(const bool f[3], int ex[3], int tot[3], int (*s_tot)[kTW]) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  uint64_t b[3];
-#pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    b[k] = __ballot(f[k]);
-    ex[k] = lanes_below(b[k]);
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int k = 0; k < 3; ++k) s_tot[k][wave] = __popcll(b[k]);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    int below = 0, all = 0;
-    for (int w = 0; w < kTW; ++w) {
-      const int t = s_tot[k][w];
-      below += w < wave ? t : 0;
-      all += t;
-    }
-    ex[k] += below;
-    tot[k] = all;
-  }
-  __syncthreads();
-}
-
 __global__ __launch_bounds__(kTT) void dsa_topk_kernel(TopkParams p) {
   const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
   const int row = p.row[blockIdx.x];
   const int n = p.len[blockIdx.x];
   const float* sc = p.scores + static_cast<int64_t>(row) * p.stride;
   int32_t* out = p.sel_idx + p.out_off[blockIdx.x];
   const uint32_t k = static_cast<uint32_t>(p.top_k);
 
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[4096];
   __shared__ uint32_t s_prefix, s_rank;
   __shared__ int s_tot[3][kTW];
 
-  // ---- 1. radix select of the k-th smallest key
+  // ---- 1. radix select of the k-th smallest key: digits of 12, 12 and 8 bits
+  // from the top (12-bit digits spread the sign-and-exponent-heavy top bits
+  // of the keys over enough bins that the histogram atomics rarely collide)
   uint32_t prefix = 0, mask = 0, rank = k;   // rank: 1-based, among keys matching the prefix
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += kTT) hist[i] = 0;
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int bits = pass < 2 ? 12 : 8;
+    const int shift = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
+    const int nb = 1 << bits;
+    const uint32_t digit = static_cast<uint32_t>(nb - 1);
+    for (int i = tid; i < nb; i += kTT) hist[i] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += kTT) {
-      const uint32_t key = rank_key(sc[i]);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    for (int base = 0; base < n; base += kTT * kU) {
+      float v[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int i = base + u * kTT + tid;
+        v[u] = i < n ? sc[i] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const uint32_t key = rank_key(v[u]);
+        if (base + u * kTT + tid < n && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & digit], 1u);
+      }
     }
     __syncthreads();
     if (tid < kWave) {
-      // lane l owns bins 4l .. 4l+3
-      uint32_t c[4], sum = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        c[j] = hist[4 * tid + j];
-        sum += c[j];
-      }
+      // lane l owns the per = nb / 64 consecutive bins from l * per
+      const int per = nb / kWave;
+      uint32_t sum = 0;
+      for (int j = 0; j < per; ++j) sum += hist[tid * per + j];
       uint32_t incl = sum;   // inclusive scan of the lane sums
 #pragma unroll
       for (int off = 1; off < kWave; off <<= 1) {
@@ -113,14 +104,14 @@ __global__ __launch_bounds__(kTT) void dsa_topk_kernel(TopkParams p) {
       // the lane whose range holds the rank-th key: before < rank <= incl
       if (before < rank && rank <= incl) {
         uint32_t cum = before;
-        int bin = 4 * tid;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (cum + c[j] >= rank) {
-            bin = 4 * tid + j;
+        int bin = tid * per;
+        for (int j = 0; j < per; ++j) {
+          const uint32_t c = hist[tid * per + j];
+          if (cum + c >= rank) {
+            bin = tid * per + j;
             break;
           }
-          cum += c[j];
+          cum += c;
         }
         s_prefix = prefix | (static_cast<uint32_t>(bin) << shift);
         s_rank = rank - cum;
@@ -129,56 +120,72 @@ __global__ __launch_bounds__(kTT) void dsa_topk_kernel(TopkParams p) {
     __syncthreads();
     prefix = s_prefix;
     rank = s_rank;
-    mask |= 0xFFu << shift;
+    mask |= digit << shift;
     __syncthreads();
   }
   const uint32_t kstar = prefix;
-  const int ties_taken = static_cast<int>(rank);   // first `rank` keys equal to K* are selected
+  const int m = static_cast<int>(rank);   // the first m keys equal to K* are selected
   const float thr = key_score(kstar);
 
-  // ---- 2. n0 = selected positions strictly above the threshold
-  int cnt = 0;
-  for (int i = tid; i < n; i += kTT) {
-    const float v = sc[i];
-    cnt += (rank_key(v) < kstar && v > thr) ? 1 : 0;
-  }
+  // ---- 2. wave runs: count, exchange, write
+  const int per_wave = ((n + kTW - 1) / kTW + kWave - 1) / kWave * kWave;
+  const int w_lo = min(n, wave * per_wave), w_hi = min(n, w_lo + per_wave);
+  int c0 = 0, c1 = 0, ct = 0;   // wave-uniform: class 0, other keys below K*, ties
+  for (int base = w_lo; base < w_hi; base += kWave * kU) {
+    float v[kU];
 #pragma unroll
-  for (int off = kWave / 2; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, kWave);
-  if ((tid & (kWave - 1)) == 0) s_tot[0][tid / kWave] = cnt;
-  __syncthreads();
-  int n0 = 0;
-  for (int w = 0; w < kTW; ++w) n0 += s_tot[0][w];
-  __syncthreads();
-
-  // ---- 3. ordered write
-  int ties_before = 0, w0 = 0, w1 = 0;
-  for (int base = 0; base < n; base += kTT) {
-    const int i = base + tid;
-    bool lt = false, tie = false;
-    float v = 0.f;
-    if (i < n) {
-      v = sc[i];
-      const uint32_t key = rank_key(v);
-      lt = key < kstar;
-      tie = key == kstar;
+    for (int u = 0; u < kU; ++u) {
+      const int i = base + u * kWave + lane;
+      v[u] = i < w_hi ? sc[i] : 0.f;
     }
-    bool f[3] = {tie, false, false};
-    int ex[3], tot[3];
-    // first scan: tie ranks decide which ties are selected
-    block_scan3(f, ex, tot, s_tot);
-    const bool sel = lt || (tie && ties_before + ex[0] < ties_taken);
-    const bool c0 = sel && v > thr;
-    const bool c1 = sel && !c0;
-    const int tie_total = tot[0];
-    f[0] = c0;
-    f[1] = c1;
-    block_scan3(f, ex, tot, s_tot);
-    if (c0) out[w0 + ex[0]] = i;
-    if (c1) out[n0 + w1 + ex[1]] = i;
-    ties_before += tie_total;
-    w0 += tot[0];
-    w1 += tot[1];
-    if (w0 + w1 >= static_cast<int>(k)) break;   // uniform: every selected position is written
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const bool ok = base + u * kWave + lane < w_hi;
+      const uint32_t key = rank_key(v[u]);
+      c0 += __popcll(__ballot(ok && key < kstar && v[u] > thr));
+      c1 += __popcll(__ballot(ok && key < kstar && !(v[u] > thr)));
+      ct += __popcll(__ballot(ok && key == kstar));
+    }
+  }
+  if (lane == 0) {
+    s_tot[0][wave] = c0;
+    s_tot[1][wave] = c1;
+    s_tot[2][wave] = ct;
+  }
+  __syncthreads();
+  int r0 = 0, r1 = 0, rt = 0, n0 = 0;
+  for (int w = 0; w < kTW; ++w) {
+    if (w < wave) {
+      r0 += s_tot[0][w];
+      r1 += s_tot[1][w];
+      rt += s_tot[2][w];
+    }
+    n0 += s_tot[0][w];
+  }
+  for (int base = w_lo; base < w_hi; base += kWave * kU) {
+    float v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = base + u * kWave + lane;
+      v[u] = i < w_hi ? sc[i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = base + u * kWave + lane;
+      const bool ok = i < w_hi;
+      const uint32_t key = rank_key(v[u]);
+      const bool f0 = ok && key < kstar && v[u] > thr;
+      const bool f1 = ok && key < kstar && !(v[u] > thr);
+      const bool ft = ok && key == kstar;
+      const uint64_t b0 = __ballot(f0), b1 = __ballot(f1), bt = __ballot(ft);
+      const int t_before = rt + lanes_below(bt);
+      if (f0) out[r0 + lanes_below(b0)] = i;
+      if (f1) out[n0 + r1 + lanes_below(b1) + min(t_before, m)] = i;
+      if (ft && t_before < m) out[n0 + r1 + lanes_below(b1) + t_before] = i;
+      r0 += __popcll(b0);
+      r1 += __popcll(b1);
+      rt += __popcll(bt);
+    }
   }
 }
 
