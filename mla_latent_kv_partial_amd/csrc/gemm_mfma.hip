@@ -18,8 +18,8 @@ constexpr int kQk = kDn + kDr;
 // ------------------------------------------------------------------ NT GEMM
 // C[m, n] = sum_k A[m, k] B[n, k]: both operands K-contiguous, bf16; fp32
 // accumulation; bf16 result (round to nearest even) or fp32.  Workgroup tile 128 x 128,
-// K step 64, 4 waves of 64 x 64 (4 x 4 MFMA blocks), 3-stage LDS ring filled
-// two K steps ahead.
+// K step 64, 4 waves of 64 x 64 (4 x 4 MFMA blocks), 2-stage LDS ring filled
+// one K step ahead; two workgroups per CU hide each other's waits.
 constexpr int kGT = 128;
 constexpr int kGK = 64;
 constexpr int kGRowChunks = kGK / 8 + 2;            // eight data chunks + two pad
@@ -28,7 +28,7 @@ constexpr int kGOpChunks = kGT * kGRowChunks;       // 1280 per operand tile
 constexpr int kGOpDma = kGOpChunks / 64;            // 20 copies of 1 KB
 constexpr int kGOpBytes = kGOpChunks * 16;
 constexpr int kGStageBytes = 2 * kGOpBytes;         // A tile then B tile
-constexpr int kGStages = 3;
+constexpr int kGStages = 2;   // 80 KB of LDS: two workgroups share a CU (measured faster than 3 or 4 stages)
 constexpr int kGMaxDma = (kGOpDma + 3) / 4;         // copies per wave per operand
 
 __shared__ __attribute__((aligned(1024))) char g_gemm[kGStages * kGStageBytes];
@@ -82,8 +82,8 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(GemmNT p) {
   const uint32_t b_frag = kGOpBytes + (64 * wn + i16) * kGRowBytes + g * 16;
 
   const int nk = p.k / kGK;
-  issue(0, 0);
-  if (nk > 1) issue(1, kGK);
+  // the ring runs kGStages - 1 K steps ahead
+  for (int t = 0; t < kGStages - 1 && t < nk; ++t) issue(t, t * kGK);
   f32x4 acc[4][4];
 #pragma unroll
   for (int bm = 0; bm < 4; ++bm)
@@ -91,13 +91,11 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(GemmNT p) {
     for (int bn = 0; bn < 4; ++bn) acc[bm][bn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int i = 0; i < nk; ++i) {
-    // tile i's copies done; those of tile i + 1 (issued one step ago) may fly
-    if (i + 1 < nk)
-      wait_vm_upto<2 * kGMaxDma>(2 * n_dma);
-    else
-      wait_vm<0>();
+    // tile i's copies done; those of the following tiles issued so far may fly
+    const int later = min(nk - 1 - i, kGStages - 2);
+    wait_vm_upto<2 * kGMaxDma * (kGStages - 2)>(2 * n_dma * later);
     lds_barrier();
-    if (i + 2 < nk) issue((i + 2) % kGStages, (i + 2) * kGK);
+    if (i + kGStages - 1 < nk) issue((i + kGStages - 1) % kGStages, (i + kGStages - 1) * kGK);
     const char* st = g_gemm + (i % kGStages) * kGStageBytes;
 #pragma unroll
     for (int ks = 0; ks < kGK / 32; ++ks) {
