@@ -58,6 +58,8 @@ __global__ __launch_bounds__(kTT) void dsa_topk_kernel(TopkParams p) {
   const float* sc = p.scores + static_cast<int64_t>(row) * p.stride;
   int32_t* out = p.sel_idx + p.out_off[blockIdx.x];
   const uint32_t k = static_cast<uint32_t>(p.top_k);
+  // whole 16-byte groups: an aligned row whose length is a multiple of 4
+  const bool vec4 = (reinterpret_cast<uintptr_t>(sc) & 15) == 0 && (n & 3) == 0;
 
   __shared__ uint32_t hist[4096];
   __shared__ uint32_t s_prefix, s_rank;
@@ -75,17 +77,39 @@ __global__ __launch_bounds__(kTT) void dsa_topk_kernel(TopkParams p) {
     const uint32_t digit = static_cast<uint32_t>(nb - 1);
     for (int i = tid; i < nb; i += kTT) hist[i] = 0;
     __syncthreads();
-    for (int base = 0; base < n; base += kTT * kU) {
-      float v[kU];
+    if (vec4) {
+      // 16-byte loads: thread t covers positions base + 4 (u kTT + t) .. +3
+      for (int base = 0; base < n; base += kTT * kU) {
+        float4 v[kU / 4];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int i = base + u * kTT + tid;
-        v[u] = i < n ? sc[i] : 0.f;
+        for (int u = 0; u < kU / 4; ++u) {
+          const int i = base + 4 * (u * kTT + tid);
+          v[u] = i < n ? *reinterpret_cast<const float4*>(sc + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < kU / 4; ++u) {
+          const int i = base + 4 * (u * kTT + tid);
+          const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t key = rank_key(e[q]);
+            if (i < n && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & digit], 1u);
+          }
+        }
       }
+    } else {
+      for (int base = 0; base < n; base += kTT * kU) {
+        float v[kU];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const uint32_t key = rank_key(v[u]);
-        if (base + u * kTT + tid < n && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & digit], 1u);
+        for (int u = 0; u < kU; ++u) {
+          const int i = base + u * kTT + tid;
+          v[u] = i < n ? sc[i] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const uint32_t key = rank_key(v[u]);
+          if (base + u * kTT + tid < n && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & digit], 1u);
+        }
       }
     }
     __syncthreads();
