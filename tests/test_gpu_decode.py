@@ -260,3 +260,29 @@ def test_absorb_unit_query_selects_weight_row_exactly():
     q_lat = _mla().mla_absorb_q(dev(cf.store(q, cf.BF16)), dev(w), dv)
     wt = dev(w).float().view(h, dn + dv, r)
     assert torch.equal(q_lat[0], wt[:, 5]) and torch.equal(q_lat[1], wt[:, 127])
+
+
+@pytest.mark.parametrize("heads", [16, 32, 128])
+@pytest.mark.parametrize("packed", [True, False])
+def test_head_counts_match_oracle(heads, packed):
+    """The MFMA kernel's head-group variants (16, 32, 64 x 2 heads per launch)
+    on ragged rows, packed and separate latent / rope caches."""
+    cfg = cf.with_shape(cf.RAGGED_BF16, heads=heads)
+    inp = cf.decode_inputs(cfg, layer=heads, lengths=(300, 1, 77))
+    say(f"heads={heads} packed={packed}")
+    got = Step(inp, packed=packed).run(64)
+    ref = _oracle(inp)
+    assert_close(host_values(got["ctx"]), ref["ctx"], cfg.dtype, "ctx")
+    assert_close(host_values(got["lse"]), ref["lse"], cfg.dtype, "lse")
+
+
+@pytest.mark.parametrize("heads", [16, 32, 128])
+def test_head_counts_gathered_match_oracle(heads):
+    cfg = cf.with_shape(cf.DSA_BF16, heads=heads, tokens=4096, selected=300)
+    inp = cf.decode_inputs(cfg, layer=heads)
+    say(f"gathered heads={heads}")
+    step = Step(inp)
+    got = step.run(64)
+    assert int(step.err.item()) == 0
+    ref = _oracle(inp)
+    assert_close(host_values(got["ctx"]), ref["ctx"], cfg.dtype, "ctx")
