@@ -54,7 +54,12 @@ constexpr int kARowChunks = 42;
 constexpr int kARowBytes = kARowChunks * 16;                 // 672
 constexpr int kATileDma = (kAK * kARowChunks + 63) / 64;      // 21
 constexpr int kAStageBytes = kATileDma * 1024;
-constexpr int kAStages = 3;
+// Two ring stages (43 KB of LDS) and at most 168 VGPRs let three workgroups
+// share a CU; at 4096 tokens that ran faster than a third stage at two
+// workgroups per CU (483 against 582 us).  With two stages each tile's copies
+// are waited for in full before the next tile is issued.
+constexpr int kAStages = 2;
+constexpr int kAWavesPerEu = 3;
 constexpr int kAMaxDma = (kATileDma + 3) / 4;                 // 6 (wave 0) or 5
 constexpr float kSlack = 8.f;
 
@@ -74,7 +79,7 @@ __device__ __forceinline__ int sigma(int m) {
   return 2 * (m & 3) + ((m >> 2) & 1) + 8 * ((m >> 3) & 1);
 }
 
-__global__ __launch_bounds__(256, 2) void flash_attn_kernel(AttnMfma p) {
+__global__ __launch_bounds__(256, kAWavesPerEu) void flash_attn_kernel(AttnMfma p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = blockIdx.x;
@@ -131,8 +136,7 @@ __global__ __launch_bounds__(256, 2) void flash_attn_kernel(AttnMfma p) {
 #pragma unroll
     for (int ks = 0; ks < kQk / 32; ++ks) qreg[qb][ks] = *reinterpret_cast<const f32x4*>(qrow + 32 * ks);
   }
-  if (nt > 0) issue(0, 0);
-  if (nt > 1) issue(1, 1);
+  for (int t = 0; t < kAStages - 1 && t < nt; ++t) issue(t, t);
 
   const uint32_t k_frag = sigma(m) * kARowBytes + g * 16;
   const uint32_t v_frag = sigma(4 * g + (m >> 2)) * kARowBytes + kDn * 2 + ((m & 3) >> 1) * 16 + (m & 1) * 8;
@@ -146,12 +150,10 @@ __global__ __launch_bounds__(256, 2) void flash_attn_kernel(AttnMfma p) {
   const int t_q[2] = {t_lo + m, t_lo + 16 + m};
 
   for (int i = 0; i < nt; ++i) {
-    if (i + 1 < nt)
-      wait_vm_upto<kAMaxDma>(n_dma);
-    else
-      wait_vm<0>();
+    // tile i's copies done; those of the later tiles issued so far may fly
+    wait_vm_upto<kAMaxDma * (kAStages - 2)>(n_dma * min(nt - 1 - i, kAStages - 2));
     lds_barrier();
-    if (i + 2 < nt) issue((i + 2) % kAStages, i + 2);
+    if (i + kAStages - 1 < nt) issue((i + kAStages - 1) % kAStages, i + kAStages - 1);
     const int k0 = k_first + i * kAK;
     // tiles past every query of this wave contribute nothing
     if (k0 > P + t_lo + 31 || k0 + kAK - 1 < pad) continue;
@@ -220,9 +222,11 @@ __global__ __launch_bounds__(256, 2) void flash_attn_kernel(AttnMfma p) {
     float l = l_run[qb] + __shfl_xor(l_run[qb], 16, kWave);
     l += __shfl_xor(l, 32, kWave);
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int t = t_q[qb];
+    // lane-derived values recomputed here rather than kept live across the loop
+    const int ln = threadIdx.x & 63;
+    const int t = t0 + 32 * wave + 16 * qb + (ln & 15);
     if (t >= p.tokens) continue;
-    float* out = p.ctx + (static_cast<int64_t>(b) * p.tokens + t) * p.heads * kDv + h * kDv + 4 * g;
+    float* out = p.ctx + (static_cast<int64_t>(b) * p.tokens + t) * p.heads * kDv + h * kDv + 4 * (ln >> 4);
 #pragma unroll
     for (int db = 0; db < kDv / 16; ++db) {
       const f32x4 v = o[qb][db] * inv;
