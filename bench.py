@@ -160,6 +160,19 @@ class DecodeLayer:
         return sum(self.n_att) * TOKEN_BYTES
 
 
+def share_partials(layers, torch, dev):
+    """One split-partial workspace for every layer instance, as a decode engine
+    keeps one: the partials are scratch that the combine consumes within the
+    same layer, so the layers need not hold them apart."""
+    s_max = max(ly.s_max for ly in layers)
+    b = max(len(ly.kv_len) for ly in layers)
+    c = layers[0].cfg
+    po = torch.empty((b, c.heads, s_max, c.kv_lora_rank), dtype=torch.float32, device=dev)
+    pl = torch.empty((b, c.heads, s_max), dtype=torch.float32, device=dev)
+    for ly in layers:
+        ly.part_o, ly.part_lse, ly.s_max = po, pl, s_max
+
+
 def time_graph(torch, fn, steps, warmup):
     """Capture fn() in a HIP graph; mean ms per replay over `steps` replays."""
     s = torch.cuda.Stream()
@@ -316,6 +329,7 @@ def main():
         layers.append(DecodeLayer(cfg, l, torch, cf, dev))
         layers[-1].plan(mla, slots, torch, dev)
         log(f"layer {l}: rows {layers[-1].kv_len} chunk {layers[-1].chunk} splits {sum(layers[-1].n_splits)}")
+    share_partials(layers, torch, dev)
     rows = len(layers[0].kv_len)
 
     def step():
@@ -371,6 +385,7 @@ def main():
         dl = [DecodeLayer(dcfg, l, torch, cf, dev) for l in range(n_dense)]
         for ly in dl:
             ly.plan(mla, slots, torch, dev)
+        share_partials(dl, torch, dev)
         ms_d, _ = time_graph(torch, lambda: [ly.step(mla) for ly in dl], args.steps, args.warmup)
         extra["dense_chained"] = {"layers": n_dense, "ms_per_step": ms_d,
                                   "rows_layers_per_s": n_dense / (ms_d * 1e-3),
@@ -397,6 +412,7 @@ def main():
         sl = [DecodeLayer(scfg, l, torch, cf, dev) for l in range(args.layers)]
         for ly in sl:
             ly.plan(mla, slots, torch, dev)
+        share_partials(sl, torch, dev)
         ms_dsa, _ = time_graph(torch, lambda: [ly.step(mla) for ly in sl], args.steps, args.warmup)
         ms_dsa_attn = time_graph(torch, lambda: [ly.attn(mla) for ly in sl], args.steps, args.warmup)[0] / len(sl)
         gb = scfg.selected * TOKEN_BYTES
@@ -425,6 +441,7 @@ def main():
             ly.n_att = [n + 1 for n in ly.n_att]   # attention covers kv_len + 1 tokens
             ly.plan(mla, slots, torch, dev)
             ly.full_layer_setup(torch, cf, dev, hidden=6144)
+        share_partials(fl, torch, dev)
         ms_full, _ = time_graph(torch, lambda: [ly.full_step(mla) for ly in fl], args.steps, args.warmup)
         ms_oproj = time_graph(torch, lambda: [mla.mla_o_proj(ly.ctx, ly.w_o, out=ly.out) for ly in fl],
                               args.steps, args.warmup)[0] / len(fl)

@@ -286,3 +286,40 @@ def test_head_counts_gathered_match_oracle(heads):
     assert int(step.err.item()) == 0
     ref = _oracle(inp)
     assert_close(host_values(got["ctx"]), ref["ctx"], cfg.dtype, "ctx")
+
+
+@pytest.mark.parametrize("heads,r,n_splits,s_max,misalign", [
+    (3, 512, (1, 7, 33, 600, 700), 700, False),   # several load batches, > 512 splits
+    (2, 36, (40, 3), 40, False),                  # 16-byte path with a short feature axis
+    (2, 30, (9, 1), 10, False),                   # scalar path: r not a multiple of 4
+    (2, 512, (5, 70), 70, True),                  # scalar path: misaligned partials
+    (1, 8, (5000,), 5000, False),                 # split lse beyond the LDS copy
+])
+def test_combine_direct_partials(heads, r, n_splits, s_max, misalign):
+    """The merge on given partials against the oracle's merge, with empty
+    splits (lse = -inf) whose partials hold NaN: such splits add nothing, and a
+    (row, head) with no non-empty split gives o = 0 and lse = -inf."""
+    mla = _mla()
+    b = len(n_splits)
+    say(f"combine heads={heads} r={r} n_splits={n_splits} s_max={s_max} misalign={misalign}")
+    po = gen.normal_f32(96, 1, (b, heads, s_max, r))
+    pl = 3.0 * gen.normal_f32(96, 2, (b, heads, s_max))
+    rng = np.random.default_rng(7)
+    empty = rng.random((b, heads, s_max)) < 0.2
+    empty[0, 0, :] = True                           # a (row, head) with no split
+    pl[empty] = -np.inf
+    po_gpu = po.copy()
+    po_gpu[empty] = np.nan
+    flat = torch.empty(po.size + 1, dtype=torch.float32, device="cuda")
+    view = (flat[1:] if misalign else flat[:-1]).view(b, heads, s_max, r)
+    view.copy_(torch.from_numpy(po_gpu))
+    o, lse = mla.mla_decode_combine(view, dev(pl), list(n_splits))
+    po_ref = np.where(empty[..., None], 0.0, po)
+    o_ref, lse_ref = oracle.combine_partials(po_ref, pl, n_splits)
+    o_h, lse_h = host_values(o), host_values(lse)
+    assert not np.isnan(o_h).any()
+    assert np.array_equal(o_h[0, 0], np.zeros(r)) and lse_h[0, 0] == -np.inf
+    assert_close(o_h, o_ref, cf.F32, "combined o_lat", tol=1e-5)
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(lse_h), fin)
+    assert np.allclose(lse_h[fin], lse_ref[fin], rtol=0, atol=1e-5)
