@@ -8,8 +8,9 @@ qk_nope=128, qk_rope=64, v_head=128, kv_lora_rank=512, per-row cache lengths
 drawn from U{1024..32768}, bf16 cache, fp32 accumulation) over L distinct layer
 instances (default 8, about 1.25 GB of caches, beyond the 256 MB last-level
 cache).  Per layer the step runs the whole chain through the C ABI:
-  partial interleaved RoPE of q_rope -> absorb_q -> latent attention (split-T
-  partials) -> combine -> absorb_v.
+  decode query (absorb_q and the RoPE of q_rope in one launch) -> latent
+  attention (split-T partials) -> combine -> absorb_v.  The split partials are
+  one workspace shared by the layers, as an engine keeps them.
 The step is captured once in a HIP graph and replayed; W warmup replays, then
 K timed replays between synchronisations.
 
@@ -113,10 +114,8 @@ class DecodeLayer:
 
     def step(self, mla):
         c = self.cfg
-        b = len(self.kv_len)
-        mla.mla_rope_partial_interleaved(self.q_rope_raw.view(b, 1, c.heads, c.qk_rope), self.offsets, c.qk_rope,
-                                         c.theta, out=self.q_rope.view(b, 1, c.heads, c.qk_rope))
-        mla.mla_absorb_q(self.q_nope, self.w, c.v_head, q_lat=self.q_lat)
+        mla.mla_decode_query(self.q_nope, self.q_rope_raw, self.w, c.v_head, self.offsets, c.theta, q_lat=self.q_lat,
+                             q_rope_out=self.q_rope)
         self.attn(mla)
         mla.mla_decode_combine(self.part_o, self.part_lse, self.n_splits, o_lat=self.o_lat, lse=self.lse)
         mla.mla_absorb_v(self.o_lat, self.w, c.qk_nope, c.v_head, ctx=self.ctx)
@@ -140,14 +139,12 @@ class DecodeLayer:
         self.kv_len_new = [n + 1 for n in self.kv_len]
 
     def full_step(self, mla):
-        """append -> RoPE(q) -> absorb_q -> attention over kv_len + 1 -> combine -> absorb_v -> o_proj."""
+        """append -> query (absorb_q + RoPE) -> attention over kv_len + 1 -> combine -> absorb_v -> o_proj."""
         c = self.cfg
-        b = len(self.kv_len)
         mla.mla_append_compressed(self.kv_a, self.norm_w, 1e-6, self.offsets, c.theta, self.latent, self.rope,
                                   self.slot)
-        mla.mla_rope_partial_interleaved(self.q_rope_raw.view(b, 1, c.heads, c.qk_rope), self.offsets, c.qk_rope,
-                                         c.theta, out=self.q_rope.view(b, 1, c.heads, c.qk_rope))
-        mla.mla_absorb_q(self.q_nope, self.w, c.v_head, q_lat=self.q_lat)
+        mla.mla_decode_query(self.q_nope, self.q_rope_raw, self.w, c.v_head, self.offsets, c.theta, q_lat=self.q_lat,
+                             q_rope_out=self.q_rope)
         mla.mla_decode_latent_attn(self.q_lat, self.q_rope, self.latent, self.rope, self.kv_len_new,
                                    c.softmax_scale, self.chunk, part_o=self.part_o, part_lse=self.part_lse,
                                    s_max=self.s_max)
@@ -365,7 +362,8 @@ def main():
                         "lengths U{1024..32768}, 1 query token, bf16 cache, fp32 accumulate",
             "layers": len(layers), "rows": rows, "cache_MB_per_step": cache_bytes / 1e6,
             "step_GBps_cache": cache_bytes / (ms_step * 1e-3) / 1e9,
-            "chain": "rope -> absorb_q -> latent_attn -> combine -> absorb_v per layer, HIP graph",
+            "chain": "decode_query (absorb_q + q RoPE, one launch) -> latent_attn -> combine -> absorb_v "
+                     "per layer, HIP graph",
         },
         "roofline": {
             "kernel": "mla_decode_latent_attn (decode_mfma_kernel)",
@@ -448,7 +446,7 @@ def main():
         extra["decode_full_layer"] = {
             "layers": len(fl), "hidden": 6144, "ms_per_step": ms_full,
             "rows_layers_per_s": rows * len(fl) / (ms_full * 1e-3),
-            "chain": "append -> rope -> absorb_q -> latent_attn -> combine -> absorb_v -> o_proj",
+            "chain": "append -> decode_query -> latent_attn -> combine -> absorb_v -> o_proj",
             "o_proj_us": ms_oproj * 1e3,
             "o_proj_weight_GBps": 6144 * cfg.heads * cfg.v_head * 2 / (ms_oproj * 1e-3) / 1e9}
         del fl

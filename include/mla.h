@@ -11,6 +11,7 @@
  * A decode step is the chain
  *   mla_rope_partial_interleaved (q rope part)  ->  mla_absorb_q  ->
  *   mla_decode_latent_attn  ->  mla_decode_combine  ->  mla_absorb_v
+ * (mla_decode_query does the first two in one call)
  * and a prefill block is one call of mla_prefill_reconstructed.
  *
  * Conventions shared by every entry point
@@ -111,6 +112,34 @@ int mla_absorb_q(int32_t dtype, const void* q_nope, int64_t q_stride_b, int64_t 
                  const void* w_kv_b, void* q_lat,
                  int32_t batch, int32_t heads, int32_t qk_nope, int32_t v_head, int32_t kv_lora_rank,
                  hipStream_t stream);
+
+/*
+ * The decode query in one call: the page's query split into its no-PE part,
+ * absorbed as in mla_absorb_q, and its rope part, rotated as in
+ * mla_rope_partial_interleaved ([P1] Glm52Mla.project and attendAbsorbed:
+ * q_pe takes RoPE at the row's position before the scores).  The results are
+ * those of the two entries:
+ *   q_lat      = mla_absorb_q(q_nope)
+ *   q_rope_out = mla_rope_partial_interleaved(q_rope_in) with tokens = 1,
+ *                inner = heads, feat = rotary_dims = qk_rope, offsets = positions
+ * computed in one launch where the bf16 MFMA absorb applies (the rotation runs
+ * while the weight tiles are in flight), else in two launches.
+ *
+ * q_nope:     [batch, heads, qk_nope] of `dtype`, strides (qn_stride_b, qn_stride_h, 1).
+ * q_rope_in:  [batch, heads, qk_rope] of `dtype`, strides (qr_stride_b, qr_stride_h, 1);
+ * q_rope_out: same strides; may equal q_rope_in (in place), else must not overlap it.
+ * w_kv_b, q_lat as in mla_absorb_q.
+ * positions [host] int64[batch]: the RoPE position of each row's query token.
+ * Errors as in the two entries (MLA_ERR_ROPE: odd or non-positive qk_rope,
+ * negative position, theta not finite and > 0; MLA_ERR_UNSUPPORTED: qk_rope > 512,
+ * position >= 2^53).  batch may be 0 (nothing is enqueued).
+ */
+int mla_decode_query(int32_t dtype, const void* q_nope, int64_t qn_stride_b, int64_t qn_stride_h,
+                     const void* q_rope_in, void* q_rope_out, int64_t qr_stride_b, int64_t qr_stride_h,
+                     const void* w_kv_b, void* q_lat,
+                     int32_t batch, int32_t heads, int32_t qk_nope, int32_t qk_rope, int32_t v_head,
+                     int32_t kv_lora_rank, const int64_t* positions, double theta,
+                     hipStream_t stream);
 
 /*
  * Latent decode attention, split-T partials.  [P1] Glm52Mla.attendAbsorbed

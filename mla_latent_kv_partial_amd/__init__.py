@@ -21,7 +21,7 @@ __all__ = [
     "MlaError", "LIB_PATH", "EXPORTS", "mla_rope_partial_interleaved", "mla_absorb_q", "mla_decode_latent_attn",
     "mla_decode_combine", "mla_absorb_v", "mla_prefill_reconstructed", "mla_version", "split_count",
     "plan_chunk_len", "prefill_workspace_bytes", "mla_dsa_topk_select", "mla_append_compressed",
-    "mla_o_proj",
+    "mla_o_proj", "mla_decode_query",
 ]
 
 
@@ -143,6 +143,39 @@ def mla_absorb_q(q_nope: torch.Tensor, w_kv_b: torch.Tensor, v_head: int,
     check(lib.mla_absorb_q(_dtype_code(q_nope), _ptr(q_nope), q_nope.stride(0), q_nope.stride(1), _ptr(w_kv_b),
                            _ptr(q_lat), b, h, dn, int(v_head), r, _stream(q_nope)), "mla_absorb_q")
     return q_lat
+
+
+def mla_decode_query(q_nope: torch.Tensor, q_rope: torch.Tensor, w_kv_b: torch.Tensor, v_head: int, positions,
+                     theta: float, q_lat: torch.Tensor | None = None,
+                     q_rope_out: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """The decode query in one call: q_nope [B,H,dn] -> q_lat [B,H,r] (as mla_absorb_q) and
+    q_rope [B,H,dr] -> q_rope_out rotated at positions[b] (as mla_rope_partial_interleaved over the
+    whole rope part).  q_rope_out=q_rope rotates in place; otherwise it must match q_rope's strides."""
+    b, h, dn = q_nope.shape
+    r = w_kv_b.shape[1]
+    if q_nope.dtype != w_kv_b.dtype or q_rope.dtype != q_nope.dtype:
+        raise TypeError("q_nope, q_rope and w_kv_b must share a dtype")
+    if q_rope.dim() != 3 or tuple(q_rope.shape[:2]) != (b, h):
+        raise ValueError("q_rope must be [B,H,dr] with q_nope's B and H")
+    if q_nope.stride(2) != 1 or q_rope.stride(2) != 1 or not w_kv_b.is_contiguous():
+        raise ValueError("q_nope and q_rope need feature stride 1 and w_kv_b must be contiguous")
+    if q_lat is None:
+        q_lat = torch.empty((b, h, r), dtype=q_nope.dtype, device=q_nope.device)
+    if q_lat.dtype != q_nope.dtype or not q_lat.is_contiguous() or tuple(q_lat.shape) != (b, h, r):
+        raise ValueError("q_lat must be a contiguous [B,H,r] tensor of q_nope's dtype")
+    if q_rope_out is None:   # the same strides as q_rope (the ABI takes one stride pair for both)
+        q_rope_out = torch.empty_strided(q_rope.shape, q_rope.stride(), dtype=q_rope.dtype, device=q_rope.device)
+    if (q_rope_out.shape != q_rope.shape or q_rope_out.stride() != q_rope.stride()
+            or q_rope_out.dtype != q_rope.dtype):
+        raise ValueError("q_rope_out must match q_rope in shape, strides and dtype")
+    pos = _host_list(positions)
+    if len(pos) != b:
+        raise ValueError("one position per row is required")
+    check(lib.mla_decode_query(_dtype_code(q_nope), _ptr(q_nope), q_nope.stride(0), q_nope.stride(1), _ptr(q_rope),
+                               _ptr(q_rope_out), q_rope.stride(0), q_rope.stride(1), _ptr(w_kv_b), _ptr(q_lat), b, h,
+                               dn, q_rope.shape[2], int(v_head), r, i64_array(pos), float(theta), _stream(q_nope)),
+          "mla_decode_query")
+    return q_lat, q_rope_out
 
 
 def mla_decode_latent_attn(q_lat: torch.Tensor, q_rope: torch.Tensor, latent: torch.Tensor, rope: torch.Tensor,

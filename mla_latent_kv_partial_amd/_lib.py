@@ -22,7 +22,7 @@ STATUS_NAMES = {
 EXPORTS = (
     "mla_last_error", "mla_version", "mla_rope_partial_interleaved", "mla_absorb_q", "mla_decode_latent_attn",
     "mla_decode_combine", "mla_absorb_v", "mla_prefill_reconstructed", "mla_dsa_topk_select",
-    "mla_append_compressed", "mla_o_proj_workspace_bytes", "mla_o_proj",
+    "mla_append_compressed", "mla_o_proj_workspace_bytes", "mla_o_proj", "mla_decode_query",
 )
 
 _p = ctypes.c_void_p
@@ -40,6 +40,8 @@ _SIGNATURES = {
     "mla_rope_partial_interleaved": (ctypes.c_int, [
         _i32, _p, _p, _i32, _i32, _i32, _i32, _i64, _i64, _i64, _i32, _f64, _pi64, _i32, _p]),
     "mla_absorb_q": (ctypes.c_int, [_i32, _p, _i64, _i64, _p, _p, _i32, _i32, _i32, _i32, _i32, _p]),
+    "mla_decode_query": (ctypes.c_int, [
+        _i32, _p, _i64, _i64, _p, _p, _i64, _i64, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _pi64, _f64, _p]),
     "mla_decode_latent_attn": (ctypes.c_int, [
         _i32, _p, _p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
         _pi32, _p, _pi32, _f32, _i32, _p, _p, _i32, _p, _p]),

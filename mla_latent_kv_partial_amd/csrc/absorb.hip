@@ -64,6 +64,7 @@ __global__ __launch_bounds__(256) void absorb_v_kernel(AbsorbVParams p) {
 bool absorb_q_mfma_ok(const AbsorbQParams& p);
 bool absorb_v_mfma_ok(const AbsorbVParams& p);
 hipError_t launch_absorb_q_mfma(const AbsorbQParams& p, hipStream_t stream);
+hipError_t launch_absorb_q_rope_mfma(const AbsorbQParams& p, const RopeParams& rp, hipStream_t stream);
 hipError_t launch_absorb_v_mfma(const AbsorbVParams& p, hipStream_t stream);
 
 hipError_t launch_absorb_q(int32_t dtype, const AbsorbQParams& p, hipStream_t stream) {
@@ -75,6 +76,13 @@ hipError_t launch_absorb_q(int32_t dtype, const AbsorbQParams& p, hipStream_t st
   else
     hipLaunchKernelGGL(absorb_q_kernel<float>, grid, dim3(256), 0, stream, p);
   return hipGetLastError();
+}
+
+hipError_t launch_absorb_q_rope(int32_t dtype, const AbsorbQParams& p, const RopeParams& rp, hipStream_t stream) {
+  if (p.batch == 0) return hipSuccess;
+  if (dtype == kBF16 && absorb_q_mfma_ok(p)) return launch_absorb_q_rope_mfma(p, rp, stream);
+  const hipError_t e = launch_rope(dtype, rp, stream);
+  return e != hipSuccess ? e : launch_absorb_q(dtype, p, stream);
 }
 
 hipError_t launch_absorb_v(int32_t dtype, const AbsorbVParams& p, hipStream_t stream) {

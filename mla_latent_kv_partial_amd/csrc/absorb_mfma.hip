@@ -10,7 +10,8 @@
 //   d-packed MFMA operand is read with ds_read_b64_tr_b16.  Chunks of a tile
 //   row are XOR-swizzled (f(d) below) so those reads are bank-conflict free.
 //   q_nope rows (bf16) are the other operand, straight from global memory;
-//   q_lat is stored in bf16 (round to nearest even).
+//   q_lat is stored in bf16 (round to nearest even).  A variant also applies
+//   the query's RoPE in the same launch (the decode query in one kernel).
 // absorb_v: workgroup = (32-column block of dv, head).  The contraction runs
 //   along the contiguous latent axis of both o_lat and W_UV, so both operands
 //   load directly; the latent axis is split over the 4 waves and the partial
@@ -19,6 +20,7 @@
 #include "cdna4.hpp"
 #include "common.hpp"
 #include "launch.hpp"
+#include "rope_dev.hpp"
 
 namespace mla {
 namespace {
@@ -31,7 +33,11 @@ __device__ __forceinline__ int swz(int d) { return ((d & 3) << 1) ^ (((d >> 3) &
 __shared__ __attribute__((aligned(1024))) char g_wtile[256 * kQCols * 2];   // up to dn = 256 rows
 __shared__ float g_vsum[8][16][kVCols + 1];   // per wave, up to 8 waves
 
-__global__ __launch_bounds__(256) void absorb_q_mfma_kernel(AbsorbQParams p) {
+// ROPE: the workgroups' waves also rotate the query's rope part (one wave per
+// (row, head) vector, rope_vector), between issuing the weight-tile copies and
+// waiting for them, so the rotation hides under the copy latency.
+template <bool ROPE>
+__global__ __launch_bounds__(256) void absorb_q_mfma_kernel(AbsorbQParams p, RopeParams rp) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c0 = blockIdx.x * kQCols;
@@ -45,6 +51,12 @@ __global__ __launch_bounds__(256) void absorb_q_mfma_kernel(AbsorbQParams p) {
     const int k = 64 * n + lane;
     const int d = k >> 4, s = k & 15;
     dma16(w + static_cast<int64_t>(d) * p.r + 8 * (s ^ swz(d)), dst + n * 1024);
+  }
+  if (ROPE) {
+    const int64_t vecs = static_cast<int64_t>(rp.rows) * rp.tokens * rp.inner;
+    const int64_t waves = static_cast<int64_t>(gridDim.x) * gridDim.y * 4;
+    for (int64_t v = (static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x) * 4 + wave; v < vecs; v += waves)
+      rope_vector<uint16_t>(rp, v, lane);
   }
   wait_vm<0>();
   lds_barrier();
@@ -156,7 +168,13 @@ bool absorb_v_mfma_ok(const AbsorbVParams& p) {
 }
 
 hipError_t launch_absorb_q_mfma(const AbsorbQParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(absorb_q_mfma_kernel, dim3(p.r / kQCols, p.heads), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(absorb_q_mfma_kernel<false>, dim3(p.r / kQCols, p.heads), dim3(256), 0, stream, p,
+                     RopeParams{});
+  return hipGetLastError();
+}
+
+hipError_t launch_absorb_q_rope_mfma(const AbsorbQParams& p, const RopeParams& rp, hipStream_t stream) {
+  hipLaunchKernelGGL(absorb_q_mfma_kernel<true>, dim3(p.r / kQCols, p.heads), dim3(256), 0, stream, p, rp);
   return hipGetLastError();
 }
 

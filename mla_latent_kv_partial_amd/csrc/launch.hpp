@@ -42,6 +42,9 @@ struct AbsorbQParams {
   int32_t batch, heads, dn, dv, r;
 };
 hipError_t launch_absorb_q(int32_t dtype, const AbsorbQParams& p, hipStream_t stream);
+// absorb_q of p and the RoPE of rp (rows of rp = rows of p) in one launch where
+// the MFMA absorb applies, else the two launches in order.
+hipError_t launch_absorb_q_rope(int32_t dtype, const AbsorbQParams& p, const RopeParams& rp, hipStream_t stream);
 
 struct AbsorbVParams {
   const float* o_lat;     // [B,H,r]

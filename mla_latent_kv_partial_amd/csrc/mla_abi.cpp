@@ -137,6 +137,55 @@ int mla_absorb_q(int32_t dtype, const void* q_nope, int64_t q_stride_b, int64_t 
   return device(mla::launch_absorb_q(dtype, p, stream), "absorb_q launch");
 }
 
+int mla_decode_query(int32_t dtype, const void* q_nope, int64_t qn_stride_b, int64_t qn_stride_h,
+                     const void* q_rope_in, void* q_rope_out, int64_t qr_stride_b, int64_t qr_stride_h,
+                     const void* w_kv_b, void* q_lat, int32_t batch, int32_t heads, int32_t qk_nope,
+                     int32_t qk_rope, int32_t v_head, int32_t kv_lora_rank, const int64_t* positions, double theta,
+                     hipStream_t stream) {
+  if (!valid_dtype(dtype)) return fail(MLA_ERR_ARG, "decode_query: unknown dtype %d", dtype);
+  if (batch < 0 || heads < 1 || qk_nope < 1 || v_head < 1 || kv_lora_rank < 1)
+    return fail(MLA_ERR_ARG, "decode_query: batch >= 0 and positive heads, qk_nope, v_head, kv_lora_rank required");
+  if (qk_rope <= 0 || (qk_rope & 1)) return fail(MLA_ERR_ROPE, "RoPE dimensions must be positive and even");
+  if (qk_rope > 2 * mla::kRopeMaxPairs)
+    return fail(MLA_ERR_UNSUPPORTED, "decode_query: qk_rope %d > %d", qk_rope, 2 * mla::kRopeMaxPairs);
+  if (!(theta > 0.0) || !isfinite(theta)) return fail(MLA_ERR_ROPE, "RoPE theta must be positive");
+  if (batch == 0) return ok();
+  if (!q_nope || !q_rope_in || !q_rope_out || !w_kv_b || !q_lat || !positions)
+    return fail(MLA_ERR_ARG, "decode_query: NULL pointer");
+  if (qn_stride_b < 0 || qn_stride_h < 0 || qr_stride_b < 0 || qr_stride_h < 0)
+    return fail(MLA_ERR_ARG, "decode_query: negative stride");
+  if (batch > 65535 * 8) return fail(MLA_ERR_UNSUPPORTED, "decode_query: batch too large");
+  for (int b = 0; b < batch; ++b) {
+    if (positions[b] < 0) return fail(MLA_ERR_ROPE, "RoPE position offset must be a non-negative integer");
+    if (positions[b] >= (int64_t{1} << 53)) return fail(MLA_ERR_UNSUPPORTED, "decode_query: position >= 2^53");
+  }
+  mla::RopeParams rp{};
+  rp.tokens = 1;
+  rp.inner = heads;
+  rp.feat = qk_rope;
+  rp.sb = qr_stride_b;
+  rp.st = 0;
+  rp.si = qr_stride_h;
+  rp.rotary = qk_rope;
+  rp.per_row = 1;
+  rp.copy_tail = 0;   // the whole rope part rotates
+  mla::rope_inverse_frequencies(qk_rope, theta, rp.inv);
+  mla::AbsorbQParams p{nullptr, qn_stride_b, qn_stride_h, w_kv_b, nullptr, 0, heads, qk_nope, v_head, kv_lora_rank};
+  for (int b0 = 0; b0 < batch; b0 += mla::kRopeRowsPerLaunch) {
+    const int rows = std::min(batch - b0, mla::kRopeRowsPerLaunch);
+    rp.rows = rows;
+    rp.x = advance(q_rope_in, b0 * qr_stride_b, dtype);
+    rp.y = const_cast<void*>(advance(q_rope_out, b0 * qr_stride_b, dtype));
+    for (int i = 0; i < rows; ++i) rp.off[i] = positions[b0 + i];
+    p.q = advance(q_nope, b0 * qn_stride_b, dtype);
+    p.q_lat = const_cast<void*>(advance(q_lat, static_cast<int64_t>(b0) * heads * kv_lora_rank, dtype));
+    p.batch = rows;
+    hipError_t e = mla::launch_absorb_q_rope(dtype, p, rp, stream);
+    if (e != hipSuccess) return device(e, "decode_query launch");
+  }
+  return ok();
+}
+
 int mla_absorb_v(int32_t dtype, const float* o_lat, const void* w_kv_b, float* ctx, int32_t batch, int32_t heads,
                  int32_t qk_nope, int32_t v_head, int32_t kv_lora_rank, hipStream_t stream) {
   if (!valid_dtype(dtype)) return fail(MLA_ERR_ARG, "absorb_v: unknown dtype %d", dtype);

@@ -97,6 +97,29 @@ def test_absorb_rejections():
     assert lib.mla_absorb_v(0, FAKE, FAKE, FAKE, 0, 1, 1, 1, 1, None) == OK
 
 
+def _query(**kw):
+    a = dict(dtype=1, qn=FAKE, qr=FAKE, qo=FAKE, w=FAKE, ql=FAKE, b=2, h=4, dn=16, dr=8, dv=16, r=32, pos=[3, 0],
+             theta=1e4, sb=1, sh=1)
+    a.update(kw)
+    return lib.mla_decode_query(a["dtype"], a["qn"], a["sb"], a["sh"], a["qr"], a["qo"], 1, 1, a["w"], a["ql"],
+                                a["b"], a["h"], a["dn"], a["dr"], a["dv"], a["r"],
+                                None if a["pos"] is None else i64_array(a["pos"]), a["theta"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), ARG), (dict(h=0), ARG), (dict(qn=None), ARG), (dict(qo=None), ARG), (dict(pos=None), ARG),
+    (dict(sb=-1), ARG), (dict(dr=7), ROPE), (dict(dr=0), ROPE), (dict(theta=-1.0), ROPE),
+    (dict(theta=float("inf")), ROPE), (dict(pos=[3, -1]), ROPE), (dict(dr=514), UNSUP),
+    (dict(pos=[2 ** 53, 0]), UNSUP),
+])
+def test_decode_query_rejections(kw, code):
+    assert _query(**kw) == code
+
+
+def test_decode_query_empty_batch_is_ok():
+    assert _query(b=0, pos=[0]) == OK
+
+
 def _prefill(ws=None, size=0, **kw):
     a = dict(dtype=1, b=1, t=16, k=16, h=4, ql=32, r=32, dn=16, dr=8, dv=16, offs=[0], theta=1e4, pad=None)
     a.update(kw)
