@@ -9,7 +9,7 @@ drawn from U{1024..32768}, bf16 cache, fp32 accumulation) over L distinct layer
 instances (default 8, about 1.25 GB of caches, beyond the 256 MB last-level
 cache).  Per layer the step runs the whole chain through the C ABI:
   decode query (absorb_q and the RoPE of q_rope in one launch) -> latent
-  attention (split-T partials) -> combine -> absorb_v.  The split partials are
+  attention (split-T partials) -> combine and absorb_v (one launch).  The split partials are
   one workspace shared by the layers, as an engine keeps them.
 The step is captured once in a HIP graph and replayed; W warmup replays, then
 K timed replays between synchronisations.
@@ -117,8 +117,7 @@ class DecodeLayer:
         mla.mla_decode_query(self.q_nope, self.q_rope_raw, self.w, c.v_head, self.offsets, c.theta, q_lat=self.q_lat,
                              q_rope_out=self.q_rope)
         self.attn(mla)
-        mla.mla_decode_combine(self.part_o, self.part_lse, self.n_splits, o_lat=self.o_lat, lse=self.lse)
-        mla.mla_absorb_v(self.o_lat, self.w, c.qk_nope, c.v_head, ctx=self.ctx)
+        mla.mla_decode_combine_v(self.part_o, self.part_lse, self.n_splits, self.w, c.qk_nope, c.v_head, ctx=self.ctx)
 
     def full_layer_setup(self, torch, cf, dev, hidden):
         """Tensors of the whole layer around the hot path: the kv_a output of the
@@ -139,7 +138,7 @@ class DecodeLayer:
         self.kv_len_new = [n + 1 for n in self.kv_len]
 
     def full_step(self, mla):
-        """append -> query (absorb_q + RoPE) -> attention over kv_len + 1 -> combine -> absorb_v -> o_proj."""
+        """append -> query (absorb_q + RoPE) -> attention over kv_len + 1 -> combine + absorb_v -> o_proj."""
         c = self.cfg
         mla.mla_append_compressed(self.kv_a, self.norm_w, 1e-6, self.offsets, c.theta, self.latent, self.rope,
                                   self.slot)
@@ -148,8 +147,7 @@ class DecodeLayer:
         mla.mla_decode_latent_attn(self.q_lat, self.q_rope, self.latent, self.rope, self.kv_len_new,
                                    c.softmax_scale, self.chunk, part_o=self.part_o, part_lse=self.part_lse,
                                    s_max=self.s_max)
-        mla.mla_decode_combine(self.part_o, self.part_lse, self.n_splits, o_lat=self.o_lat, lse=self.lse)
-        mla.mla_absorb_v(self.o_lat, self.w, c.qk_nope, c.v_head, ctx=self.ctx)
+        mla.mla_decode_combine_v(self.part_o, self.part_lse, self.n_splits, self.w, c.qk_nope, c.v_head, ctx=self.ctx)
         mla.mla_o_proj(self.ctx, self.w_o, out=self.out)
 
     @property
@@ -362,8 +360,8 @@ def main():
                         "lengths U{1024..32768}, 1 query token, bf16 cache, fp32 accumulate",
             "layers": len(layers), "rows": rows, "cache_MB_per_step": cache_bytes / 1e6,
             "step_GBps_cache": cache_bytes / (ms_step * 1e-3) / 1e9,
-            "chain": "decode_query (absorb_q + q RoPE, one launch) -> latent_attn -> combine -> absorb_v "
-                     "per layer, HIP graph",
+            "chain": "decode_query (absorb_q + q RoPE, one launch) -> latent_attn -> combine_v (combine + "
+                     "absorb_v, one launch) per layer, HIP graph",
         },
         "roofline": {
             "kernel": "mla_decode_latent_attn (decode_mfma_kernel)",
@@ -446,7 +444,7 @@ def main():
         extra["decode_full_layer"] = {
             "layers": len(fl), "hidden": 6144, "ms_per_step": ms_full,
             "rows_layers_per_s": rows * len(fl) / (ms_full * 1e-3),
-            "chain": "append -> decode_query -> latent_attn -> combine -> absorb_v -> o_proj",
+            "chain": "append -> decode_query -> latent_attn -> combine_v -> o_proj",
             "o_proj_us": ms_oproj * 1e3,
             "o_proj_weight_GBps": 6144 * cfg.heads * cfg.v_head * 2 / (ms_oproj * 1e-3) / 1e9}
         del fl

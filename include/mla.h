@@ -11,7 +11,8 @@
  * A decode step is the chain
  *   mla_rope_partial_interleaved (q rope part)  ->  mla_absorb_q  ->
  *   mla_decode_latent_attn  ->  mla_decode_combine  ->  mla_absorb_v
- * (mla_decode_query does the first two in one call)
+ * (mla_decode_query does the first two in one call, mla_decode_combine_v the
+ * last two)
  * and a prefill block is one call of mla_prefill_reconstructed.
  *
  * Conventions shared by every entry point
@@ -205,6 +206,24 @@ int mla_decode_latent_attn(int32_t dtype, const void* q_lat,
 int mla_decode_combine(const float* part_o, const float* part_lse,
                        int32_t batch, int32_t heads, int32_t kv_lora_rank, int32_t s_max,
                        const int32_t* n_splits, float* o_lat, float* lse, hipStream_t stream);
+
+/*
+ * mla_decode_combine followed by mla_absorb_v in one launch: the merged latent
+ * context of each (row, head) stays on chip and is projected through the
+ * head's value block ([P1] attendAbsorbed: o_lat . W_UV[h]^T, heads
+ * concatenated).
+ *   ctx[b, h*dv + v] = sum_c o_lat[b,h,c] * w_kv_b[h*(dn+dv) + dn + v, c]
+ * with o_lat as defined for mla_decode_combine.  `dtype` is the dtype of
+ * w_kv_b (layout as in mla_absorb_q); the projection accumulates in fp32 over
+ * the fp32 o_lat.  part_o, part_lse, n_splits as in mla_decode_combine;
+ * ctx fp32 [batch, heads*v_head] contiguous.  o_lat [batch, heads, r] and
+ * lse [batch, heads] may be NULL; when given they receive the merge.
+ * Limits (MLA_ERR_UNSUPPORTED): kv_lora_rank <= 1024.
+ */
+int mla_decode_combine_v(int32_t dtype, const float* part_o, const float* part_lse,
+                         int32_t batch, int32_t heads, int32_t kv_lora_rank, int32_t s_max,
+                         const int32_t* n_splits, const void* w_kv_b, int32_t qk_nope, int32_t v_head,
+                         float* ctx, float* o_lat, float* lse, hipStream_t stream);
 
 /*
  * Project the latent context out through the value block.  [P1]

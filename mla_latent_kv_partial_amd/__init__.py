@@ -81,7 +81,7 @@ def plan_chunk_len(n_attended, slots: int, tile: int = 32) -> int:
     total = sum(n)
     if not n or total == 0:
         return tile
-    chunk = max(tile, -(-total // max(slots - len(n), 1)))
+    chunk = max(tile, -(-total // max(slots, 1)))
     chunk = -(-chunk // tile) * tile
     while sum(split_count(v, chunk) for v in n) > slots and chunk < max(n):
         chunk += tile
@@ -240,6 +240,22 @@ def mla_absorb_v(o_lat: torch.Tensor, w_kv_b: torch.Tensor, qk_nope: int, v_head
         raise ValueError("o_lat and w_kv_b must be contiguous")
     check(lib.mla_absorb_v(_dtype_code(w_kv_b), _ptr(o_lat), _ptr(w_kv_b), _ptr(ctx), b, h, int(qk_nope),
                            int(v_head), r, _stream(o_lat)), "mla_absorb_v")
+    return ctx
+
+
+def mla_decode_combine_v(part_o: torch.Tensor, part_lse: torch.Tensor, n_splits, w_kv_b: torch.Tensor, qk_nope: int,
+                         v_head: int, ctx: torch.Tensor | None = None, o_lat: torch.Tensor | None = None,
+                         lse: torch.Tensor | None = None):
+    """Merge partials and project through W_UV in one launch: ctx fp32 [B,H*dv]
+    (o_lat [B,H,r] and lse [B,H] are written too when given)."""
+    b, h, s_max, r = part_o.shape
+    if ctx is None:
+        ctx = torch.empty((b, h * v_head), dtype=torch.float32, device=part_o.device)
+    if not w_kv_b.is_contiguous():
+        raise ValueError("w_kv_b must be contiguous")
+    check(lib.mla_decode_combine_v(_dtype_code(w_kv_b), _ptr(part_o), _ptr(part_lse), b, h, r, s_max,
+                                   i32_array(_host_list(n_splits)), _ptr(w_kv_b), int(qk_nope), int(v_head), _ptr(ctx),
+                                   _ptr(o_lat), _ptr(lse), _stream(part_o)), "mla_decode_combine_v")
     return ctx
 
 

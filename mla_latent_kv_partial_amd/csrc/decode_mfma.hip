@@ -316,14 +316,17 @@ struct Decode {
 
   template <bool SC>
   __device__ __forceinline__ void pipeline(int b, int s) {
-    // ---- prologue.  Issue order: query loads (score waves), then the copies
-    // of tiles 0 and 1 (and the indices of tile 2); converting the queries then
-    // waits once for all of them, so the latencies overlap.  A launch with
-    // gathered rows first needs the indices of tiles 0 and 1 to address their
-    // copies; it converts the queries as soon as those indices are in, which
-    // costs no extra latency.
+    // ---- prologue.  Issue order for a dense row: the copies of tile 0, the
+    // query loads (score waves), the copies of tile 1; converting the queries
+    // then waits once for all of them, so the latencies overlap, and the HBM
+    // requests of tile 0 leave ahead of the (cache-resident) queries.  A row
+    // read through a selection first needs the indices of tiles 0 and 1 to
+    // address its copies: it loads the queries first and converts them as
+    // soon as those indices are in, which costs no extra latency.
     f32x4 qraw[kR / 32];   // 8 bf16 each
     short qrraw[kDR / 32][8];
+    const bool dense_row = !(GATHER && gather_row);
+    if (dense_row) issue_tile_dense(0, 0);
     if (SC) {
       const uint16_t* ql = static_cast<const uint16_t*>(p.q_lat) + (static_cast<int64_t>(b) * p.heads + head) * kR;
 #pragma unroll
@@ -346,7 +349,6 @@ struct Decode {
       const int slot1 = slot_of<SC>(1, idx1v, mask1);
       issue_tile(1, slot1);
     } else {
-      issue_tile_dense(0, 0);
       issue_tile_dense(1, 1);
       if (SC) {
         mask0 = dense_mask(0);

@@ -86,9 +86,13 @@ hipError_t launch_decode(int32_t dtype, const DecodeParams& p, hipStream_t strea
 struct CombineParams {
   const float* part_o;
   const float* part_lse;
-  float* o_lat;
+  float* o_lat;           // may be null when ctx is set
   float* lse;             // may be null
   int32_t rows, heads, r, s_max;
+  // value projection after the merge (ctx = o_lat . W_UV^T), when ctx is set
+  const void* w;          // [H*(dn+dv), r] of w_dtype
+  float* ctx;             // [rows, H*dv]
+  int32_t w_dtype, dn, dv;
   int32_t n_splits[kCombineRowsPerLaunch];
 };
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);

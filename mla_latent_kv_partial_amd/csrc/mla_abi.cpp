@@ -471,6 +471,43 @@ int mla_decode_combine(const float* part_o, const float* part_lse, int32_t batch
   return ok();
 }
 
+int mla_decode_combine_v(int32_t dtype, const float* part_o, const float* part_lse, int32_t batch, int32_t heads,
+                         int32_t kv_lora_rank, int32_t s_max, const int32_t* n_splits, const void* w_kv_b,
+                         int32_t qk_nope, int32_t v_head, float* ctx, float* o_lat, float* lse, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return fail(MLA_ERR_ARG, "combine_v: unknown dtype %d", dtype);
+  if (batch < 0 || heads < 1 || kv_lora_rank < 1 || s_max < 1 || qk_nope < 1 || v_head < 1)
+    return fail(MLA_ERR_ARG,
+                "combine_v: batch >= 0 and positive heads, kv_lora_rank, s_max, qk_nope, v_head required");
+  if (kv_lora_rank > 1024) return fail(MLA_ERR_UNSUPPORTED, "combine_v: kv_lora_rank <= 1024 supported");
+  if (batch == 0) return ok();
+  if (!part_o || !part_lse || !n_splits || !w_kv_b || !ctx) return fail(MLA_ERR_ARG, "combine_v: NULL pointer");
+  if (heads > 65535) return fail(MLA_ERR_UNSUPPORTED, "combine_v: heads > 65535");
+  for (int b = 0; b < batch; ++b)
+    if (n_splits[b] < 1 || n_splits[b] > s_max)
+      return fail(MLA_ERR_SHAPE, "combine_v: n_splits[%d] = %d outside [1, %d]", b, n_splits[b], s_max);
+  mla::CombineParams p{};
+  p.heads = heads;
+  p.r = kv_lora_rank;
+  p.s_max = s_max;
+  p.w = w_kv_b;
+  p.w_dtype = dtype;
+  p.dn = qk_nope;
+  p.dv = v_head;
+  for (int b0 = 0; b0 < batch; b0 += mla::kCombineRowsPerLaunch) {
+    p.rows = std::min(batch - b0, mla::kCombineRowsPerLaunch);
+    for (int i = 0; i < p.rows; ++i) p.n_splits[i] = n_splits[b0 + i];
+    const int64_t bh = static_cast<int64_t>(b0) * heads;
+    p.part_o = part_o + bh * s_max * kv_lora_rank;
+    p.part_lse = part_lse + bh * s_max;
+    p.o_lat = o_lat ? o_lat + bh * kv_lora_rank : nullptr;
+    p.lse = lse ? lse + bh : nullptr;
+    p.ctx = ctx + bh * v_head;
+    hipError_t e = mla::launch_combine(p, stream);
+    if (e != hipSuccess) return device(e, "combine_v launch");
+  }
+  return ok();
+}
+
 int mla_prefill_reconstructed(int32_t dtype, int32_t batch, int32_t tokens, int32_t keys, int32_t heads,
                               int32_t q_lora_rank, int32_t kv_lora_rank, int32_t qk_nope, int32_t qk_rope,
                               int32_t v_head, const void* q_c, const void* w_q_b, const void* latent,

@@ -90,6 +90,17 @@ def test_combine_rejections(ns, code):
     assert lib.mla_decode_combine(FAKE, FAKE, 2, 4, 8, 4, i32_array(ns), FAKE, None, None) == code
 
 
+def test_combine_v_rejections():
+    ns = i32_array([2, 1])
+    assert lib.mla_decode_combine_v(7, FAKE, FAKE, 2, 4, 8, 4, ns, FAKE, 4, 4, FAKE, None, None, None) == ARG
+    assert lib.mla_decode_combine_v(1, FAKE, FAKE, 2, 4, 8, 4, ns, FAKE, 4, 0, FAKE, None, None, None) == ARG
+    assert lib.mla_decode_combine_v(1, FAKE, FAKE, 2, 4, 8, 4, ns, FAKE, 4, 4, None, None, None, None) == ARG
+    assert lib.mla_decode_combine_v(1, FAKE, FAKE, 2, 4, 8, 4, i32_array([5, 1]), FAKE, 4, 4, FAKE, None, None,
+                                    None) == SHAPE
+    assert lib.mla_decode_combine_v(1, FAKE, FAKE, 2, 4, 2048, 4, ns, FAKE, 4, 4, FAKE, None, None, None) == UNSUP
+    assert lib.mla_decode_combine_v(1, FAKE, FAKE, 0, 4, 8, 4, ns, FAKE, 4, 4, FAKE, None, None, None) == OK
+
+
 def test_absorb_rejections():
     assert lib.mla_absorb_q(5, FAKE, 1, 1, FAKE, FAKE, 1, 1, 1, 1, 1, None) == ARG
     assert lib.mla_absorb_q(0, None, 1, 1, FAKE, FAKE, 1, 1, 1, 1, 1, None) == ARG

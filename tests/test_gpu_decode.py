@@ -55,8 +55,12 @@ class Step:
                                                 chunk, sel_idx=self.sel, sel_count=inp.sel_count, dev_err=self.err)
         o_lat, lse = mla.mla_decode_combine(po, pl, ns)
         ctx = mla.mla_absorb_v(o_lat, self.w, c.qk_nope, c.v_head)
+        # the same merge and projection in one launch
+        o_lat_v, lse_v = torch.empty_like(o_lat), torch.empty_like(lse)
+        ctx_v = mla.mla_decode_combine_v(po, pl, ns, self.w, c.qk_nope, c.v_head, o_lat=o_lat_v, lse=lse_v)
         torch.cuda.synchronize()
-        return dict(q_rope=q_rope, q_lat=q_lat, part_o=po, part_lse=pl, n_splits=ns, o_lat=o_lat, lse=lse, ctx=ctx)
+        return dict(q_rope=q_rope, q_lat=q_lat, part_o=po, part_lse=pl, n_splits=ns, o_lat=o_lat, lse=lse, ctx=ctx,
+                    o_lat_v=o_lat_v, lse_v=lse_v, ctx_v=ctx_v)
 
 
 def _selections(inp):
@@ -92,8 +96,12 @@ def test_decode_chain_matches_oracle(cfg):
     assert_close(host_values(got["o_lat"]), ref["o_lat"], cfg.dtype, "o_lat")
     assert_close(host_values(got["lse"]), ref["lse"], cfg.dtype, "lse")
     assert_close(host_values(got["ctx"]), ref["ctx"], cfg.dtype, "ctx vs absorbed oracle")
+    assert_close(host_values(got["ctx_v"]), ref["ctx"], cfg.dtype, "fused combine_v ctx vs absorbed oracle")
+    # the fused entry's merge is the combine's own code: identical o_lat and lse
+    assert bitwise_equal(got["o_lat_v"], got["o_lat"]) and bitwise_equal(got["lse_v"], got["lse"])
     if "ctx_rec" in ref:
         assert_close(host_values(got["ctx"]), ref["ctx_rec"], cfg.dtype, "ctx vs reconstructed oracle")
+        assert_close(host_values(got["ctx_v"]), ref["ctx_rec"], cfg.dtype, "fused ctx vs reconstructed oracle")
 
 
 def _small_ragged(lengths=(700, 1, 333), seed_layer=5):
@@ -323,3 +331,39 @@ def test_combine_direct_partials(heads, r, n_splits, s_max, misalign):
     fin = np.isfinite(lse_ref)
     assert np.array_equal(np.isfinite(lse_h), fin)
     assert np.allclose(lse_h[fin], lse_ref[fin], rtol=0, atol=1e-5)
+
+
+@pytest.mark.parametrize("wdt,heads,r,dn,dv,n_splits", [
+    (cf.BF16, 8, 512, 128, 128, (1, 9, 31, 40)),   # bf16 fast path (eight threads per column)
+    (cf.BF16, 3, 448, 32, 64, (5, 2)),              # fast path, r / 64 = 7, one pass of columns
+    (cf.BF16, 2, 1024, 16, 40, (3, 12)),            # r beyond the fast path: one thread per column
+    (cf.BF16, 2, 512, 128, 192, (4, 6)),            # dv beyond the fast path
+    (cf.F32, 4, 64, 32, 32, (4, 1)),                # fp32 weights
+    (cf.F32, 2, 30, 8, 12, (9, 1)),                 # scalar merge (r not a multiple of 4)
+])
+def test_combine_v_direct_partials(wdt, heads, r, dn, dv, n_splits):
+    """The fused merge + value projection on given partials (empty splits with
+    NaN partials, one (row, head) with no split at all) against the oracle's
+    merge followed by its absorb_v."""
+    mla = _mla()
+    b = len(n_splits)
+    s_max = max(n_splits)
+    say(f"combine_v {wdt} heads={heads} r={r} dn={dn} dv={dv} n_splits={n_splits}")
+    po = gen.normal_f32(97, 1, (b, heads, s_max, r))
+    pl = 3.0 * gen.normal_f32(97, 2, (b, heads, s_max))
+    empty = np.random.default_rng(11).random((b, heads, s_max)) < 0.2
+    empty[0, 0, :] = True
+    pl[empty] = -np.inf
+    po_gpu = po.copy()
+    po_gpu[empty] = np.nan
+    w = cf.store(gen.normal_f32(97, 3, (heads * (dn + dv), r), std=r ** -0.5), wdt)
+    o_lat = torch.empty((b, heads, r), dtype=torch.float32, device="cuda")
+    ctx = mla.mla_decode_combine_v(dev(po_gpu), dev(pl), list(n_splits), dev(w), dn, dv, o_lat=o_lat)
+    torch.cuda.synchronize()
+    o_ref, _ = oracle.combine_partials(np.where(empty[..., None], 0.0, po), pl, n_splits)
+    ctx_ref = oracle.absorb_v(o_ref, cf.values(w), dn, dv)
+    got = host_values(ctx)
+    assert not np.isnan(got).any()
+    assert np.array_equal(got[0, :dv], np.zeros(dv))   # row 0, head 0: no split, o = 0
+    assert_close(host_values(o_lat), o_ref, cf.F32, "fused merge o_lat", tol=1e-5)
+    assert_close(got, ctx_ref, cf.F32, "fused ctx", tol=1e-5)

@@ -15,7 +15,8 @@ from conftest import build_module
 
 B = build_module()
 
-SRC = ["decode_mfma.hip", "absorb_mfma.hip", "gemm_mfma.hip", "prefill_mfma.hip"]
+COPY_SRC = ["decode_mfma.hip", "absorb_mfma.hip", "gemm_mfma.hip", "prefill_mfma.hip"]   # HBM -> LDS copies
+SRC = COPY_SRC + ["combine.hip"]
 
 
 def _asm(name, tmp_path):
@@ -26,7 +27,7 @@ def _asm(name, tmp_path):
     return out.read_text()
 
 
-@pytest.mark.parametrize("name", SRC)
+@pytest.mark.parametrize("name", COPY_SRC)
 def test_m0_only_set_by_the_copy_sequences(name, tmp_path):
     text = _asm(name, tmp_path)
     lines = [ln.strip() for ln in text.splitlines() if re.search(r"\bm0\b", ln) and not ln.strip().startswith(";")]
@@ -45,5 +46,5 @@ def test_no_spills(name, tmp_path):
     text = _asm(name, tmp_path)
     spills = [int(v) for v in re.findall(r"\.vgpr_spill_count:\s+(\d+)", text)]
     names = re.findall(r"\.name:\s+(\S+)", text)
-    hot = [s for n, s in zip(names, spills) if any(k in n for k in ("ILi4E", "absorb", "gemm", "flash"))]
+    hot = [s for n, s in zip(names, spills) if any(k in n for k in ("ILi4E", "absorb", "gemm", "flash", "combine"))]
     assert hot and max(hot) == 0, list(zip(names, spills))
