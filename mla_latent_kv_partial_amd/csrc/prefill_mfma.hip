@@ -246,16 +246,23 @@ bool prefill_mfma_supported(const PrefillParams& p) {
          al(p.q_c) && al(p.w_qb) && al(p.latent) && al(p.rope) && al(p.w_kvb) && al(p.ctx) && p.heads <= 65535;
 }
 
+// q RoPE table of one launch: {cos, sin} (double) per query row and pair
+size_t rope_table_bytes(const PrefillParams& p) {
+  return static_cast<size_t>(min(p.batch, kBatchPerLaunch)) * p.tokens * 32 * sizeof(double2);
+}
+
 size_t prefill_mfma_workspace_bytes(const PrefillParams& p) {
   const size_t q = static_cast<size_t>(p.batch) * p.tokens * p.heads * kQk * 2;
   const size_t kv = static_cast<size_t>(p.batch) * p.keys * p.heads * kKvw * 2;
-  return up256(q) + up256(kv);
+  return up256(q) + up256(kv) + up256(rope_table_bytes(p));
 }
 
 hipError_t launch_prefill_mfma(const PrefillParams& p, hipStream_t stream) {
   uint16_t* q = static_cast<uint16_t*>(p.workspace);
   const size_t q_bytes = static_cast<size_t>(p.batch) * p.tokens * p.heads * kQk * 2;
+  const size_t kv_bytes = static_cast<size_t>(p.batch) * p.keys * p.heads * kKvw * 2;
   uint16_t* kv = reinterpret_cast<uint16_t*>(static_cast<char*>(p.workspace) + up256(q_bytes));
+  double2* cs = reinterpret_cast<double2*>(static_cast<char*>(p.workspace) + up256(q_bytes) + up256(kv_bytes));
   const uint16_t* q_c = static_cast<const uint16_t*>(p.q_c);
   const uint16_t* latent = static_cast<const uint16_t*>(p.latent);
   const uint16_t* rope = static_cast<const uint16_t*>(p.rope);
@@ -277,7 +284,10 @@ hipError_t launch_prefill_mfma(const PrefillParams& p, hipStream_t stream) {
     gq.tokens = p.tokens;
     for (int i = 0; i < rows; ++i) gq.off[i] = p.q_offsets[b0 + i];
     for (int i = 0; i < kDr / 2; ++i) gq.inv[i] = inv[i];
-    hipError_t e = launch_gemm_nt_mfma(gq, true, false, stream);
+    gq.cs = cs;
+    hipError_t e = launch_rope_table(gq, cs, stream);
+    if (e != hipSuccess) return e;
+    e = launch_gemm_nt_mfma(gq, true, false, stream);
     if (e != hipSuccess) return e;
     // KV expansion
     GemmNT gk{};

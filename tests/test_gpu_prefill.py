@@ -83,3 +83,13 @@ def test_prefill_full_size_sampled_rows():
     say("prefill full: oracle")
     ref = _oracle(inp, rows=rows)
     assert_close(got[:, rows], ref, cfg.dtype, "ctx sampled rows")
+
+
+def test_prefill_long_ragged_tiles_sampled_rows():
+    """2200 tokens: the projections run on 256 x 256 GEMM tiles with a partial
+    last row tile (2200 = 8 x 256 + 152); sampled rows against the oracle."""
+    cfg = cf.PREFILL_BF16
+    inp = cf.prefill_inputs(cfg, tokens=2200, keys=2200)
+    got = host_values(_gpu(inp))
+    rows = [0, 151, 152, 255, 256, 1500, 2047, 2048, 2199]
+    assert_close(got[:, rows], _oracle(inp, rows=rows), cfg.dtype, "ctx sampled rows")
