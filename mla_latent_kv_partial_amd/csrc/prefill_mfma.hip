@@ -48,7 +48,8 @@ constexpr int kBatchPerLaunch = kGemmRowsPerLaunch;   // per-row tables travel i
 // query blocks).  The layout tricks are those of the latent decode kernel: key
 // row m of a 16-key block holds key sigma(m), and a key row is 42 chunks
 // (k_nope 16, v 16, rope 8, pad 2), an odd number of 32-byte units.
-constexpr int kAQ = 128;
+constexpr int kAWaves = 4;                                   // waves per workgroup, 32 queries each
+constexpr int kAQ = 32 * kAWaves;
 constexpr int kAK = 32;
 constexpr int kARowChunks = 42;
 constexpr int kARowBytes = kARowChunks * 16;                 // 672
@@ -60,7 +61,7 @@ constexpr int kAStageBytes = kATileDma * 1024;
 // are waited for in full before the next tile is issued.
 constexpr int kAStages = 2;
 constexpr int kAWavesPerEu = 3;
-constexpr int kAMaxDma = (kATileDma + 3) / 4;                 // 6 (wave 0) or 5
+constexpr int kAMaxDma = (kATileDma + kAWaves - 1) / kAWaves;   // copies per wave (the first waves take one more)
 constexpr float kSlack = 8.f;
 
 __shared__ __attribute__((aligned(1024))) char g_attn[kAStages * kAStageBytes];
@@ -79,7 +80,7 @@ __device__ __forceinline__ int sigma(int m) {
   return 2 * (m & 3) + ((m >> 2) & 1) + 8 * ((m >> 3) & 1);
 }
 
-__global__ __launch_bounds__(256, kAWavesPerEu) void flash_attn_kernel(AttnMfma p) {
+__global__ __launch_bounds__(64 * kAWaves, kAWavesPerEu) void flash_attn_kernel(AttnMfma p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = blockIdx.x;
@@ -96,15 +97,15 @@ __global__ __launch_bounds__(256, kAWavesPerEu) void flash_attn_kernel(AttnMfma 
   const int k_last = min(p.keys - 1, P + min(t0 + kAQ, p.tokens) - 1);
   const int nt = k_last >= k_first ? (k_last - k_first) / kAK + 1 : 0;
 
-  // ---- copy plan (same for every tile): chunk q = 64 (wave + 4 j) + lane is
+  // ---- copy plan (same for every tile): chunk q = 64 (wave + kAWaves j) + lane is
   // chunk c of key row q / 42; c < 32 from the KV workspace row of head h,
   // c < 40 from the rope row, c = 40, 41 padding (re-read chunk 0)
-  const int n_dma = (kATileDma - wave + 3) / 4;
+  const int n_dma = (kATileDma - wave + kAWaves - 1) / kAWaves;
   int c_row[kAMaxDma];
   int c_off[kAMaxDma];   // byte offset in the KV head slice, or rope row (sign bit set)
 #pragma unroll
   for (int j = 0; j < kAMaxDma; ++j) {
-    const int q = 64 * (wave + 4 * j) + lane;
+    const int q = 64 * (wave + kAWaves * j) + lane;
     const int row = q / kARowChunks;
     const int c = q - row * kARowChunks;
     c_row[j] = min(row, kAK - 1);
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(256, kAWavesPerEu) void flash_attn_kernel(AttnMfma 
     const int key = min(k0 + c_row[j], p.keys - 1);
     const int off = c_off[j];
     const char* src = off >= 0 ? kv_base + key * kv_stride + off : rope_base + key * (kDr * 2) + (off & 0x7fff);
-    dma16(src, dst + (wave + 4 * j) * 1024);
+    dma16(src, dst + (wave + kAWaves * j) * 1024);
   };
   auto issue = [&](int s, int tile) {
     const uint32_t dst = lds_addr(g_attn + s * kAStageBytes);
@@ -315,7 +316,7 @@ hipError_t launch_prefill_mfma(const PrefillParams& p, hipStream_t stream) {
     ap.q_tiles = (p.tokens + kAQ - 1) / kAQ;
     ap.scale_log2 = p.scale * 1.4426950408889634f;
     for (int i = 0; i < rows; ++i) ap.pad[i] = p.left_pad ? p.left_pad[b0 + i] : 0;
-    hipLaunchKernelGGL(flash_attn_kernel, dim3(p.heads, ap.q_tiles, rows), dim3(256), 0, stream, ap);
+    hipLaunchKernelGGL(flash_attn_kernel, dim3(p.heads, ap.q_tiles, rows), dim3(64 * kAWaves), 0, stream, ap);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
