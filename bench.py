@@ -424,12 +424,19 @@ def main():
         n_ctx, k_sel = scfg.tokens, scfg.selected
         scores = torch.from_numpy(gen.normal_f32(scfg.config_id, gen.T_DSA_SCORES, (args.layers, n_ctx))).to(dev)
         sel_buf = torch.empty(args.layers * k_sel, dtype=torch.int32, device=dev)
-        ms_sel = time_graph(torch, lambda: mla.mla_dsa_topk_select(scores, [n_ctx] * args.layers, k_sel,
-                                                                   sel_idx=sel_buf), args.steps, args.warmup)[0]
-        extra["dsa_topk"] = {"rows": args.layers, "context": n_ctx, "top_k": k_sel, "ms_per_launch": ms_sel,
-                             "us_per_row": ms_sel * 1e3 / args.layers,
-                             "scores_GBps": args.layers * n_ctx * 4 / (ms_sel * 1e-3) / 1e9}
-        del scores, sel_buf
+        lens = [n_ctx] * args.layers
+        ws = torch.empty(max(mla.dsa_topk_workspace_bytes(lens, k_sel), 1), dtype=torch.uint8, device=dev)
+        topk = {}
+        for rows in (args.layers, 1):
+            for two in (True, False):
+                ms_sel = time_graph(torch, lambda: mla.mla_dsa_topk_select(
+                    scores[:rows], lens[:rows], k_sel, sel_idx=sel_buf, workspace=ws, two_stage=two),
+                    args.steps, args.warmup)[0]
+                topk[f"{rows}_rows_{'two_stage' if two else 'one_workgroup'}_us"] = ms_sel * 1e3
+        extra["dsa_topk"] = {"context": n_ctx, "top_k": k_sel, **topk,
+                             "scores_GBps_8_rows": args.layers * n_ctx * 4 /
+                             (topk[f"{args.layers}_rows_two_stage_us"] * 1e-6) / 1e9}
+        del scores, sel_buf, ws
         extra["prefill"] = prefill_leg(torch, mla, cf, dev)
         # the whole layer around the hot path: append + chain + o_proj (hidden 6144, synthetic)
         fl = [DecodeLayer(cfg, l, torch, cf, dev, spare_slots=1) for l in range(args.layers)]

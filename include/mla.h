@@ -311,11 +311,21 @@ int mla_o_proj(int32_t dtype, const float* ctx, int64_t rows, int32_t in_feature
  *         dense row (row_len[b] <= top_k), as mla_decode_latent_attn takes it.
  * sel_idx: device int32, written with top_k entries per selected row,
  *         concatenated in row order; may be NULL only if no row is selected.
+ * workspace / workspace_bytes: a row of 2 to 8 segments of 16384 scores
+ *         whose segments' candidates (segments x top_k) fit 16384 runs on one
+ *         workgroup per segment and then one for the row, in caller memory of
+ *         131328 bytes per such row (256-byte aligned).  workspace == NULL with
+ *         workspace_bytes != NULL writes the size needed (0 when no row
+ *         qualifies) and returns MLA_OK without launching.  workspace_bytes
+ *         == NULL: every row runs on one workgroup.  Both ways give the same
+ *         positions.
  * Errors: MLA_ERR_ARG (NULL pointers, top_k < 1, batch < 0), MLA_ERR_SHAPE
- * (row_len out of range or above score_stride).
+ * (row_len out of range or above score_stride), MLA_ERR_WORKSPACE (too small
+ * or misaligned).
  */
 int mla_dsa_topk_select(const float* scores, int64_t score_stride, int32_t batch, const int32_t* row_len,
-                        int32_t top_k, int32_t* sel_idx, int32_t* sel_count, hipStream_t stream);
+                        int32_t top_k, int32_t* sel_idx, int32_t* sel_count, void* workspace,
+                        size_t* workspace_bytes, hipStream_t stream);
 
 /*
  * Reconstructed causal prefill.  [P1] Glm52Mla.project (q_b_proj of the

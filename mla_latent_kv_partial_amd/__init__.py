@@ -300,11 +300,26 @@ def mla_prefill_reconstructed(q_c: torch.Tensor, w_q_b: torch.Tensor, latent: to
     return ctx
 
 
-def mla_dsa_topk_select(scores: torch.Tensor, row_len, top_k: int, sel_idx: torch.Tensor | None = None):
+def dsa_topk_workspace_bytes(row_len, top_k: int) -> int:
+    """Workspace bytes mla_dsa_topk_select needs for rows of these lengths (0
+    when every row runs on one workgroup)."""
+    lens = _host_list(row_len)
+    size = ctypes.c_size_t(0)
+    counts = i32_array([0] * max(len(lens), 1))
+    stride = max(lens) if lens else 1
+    check(lib.mla_dsa_topk_select(ctypes.c_void_p(16), stride, len(lens), i32_array(lens), int(top_k), None, counts,
+                                  None, ctypes.byref(size), None), "mla_dsa_topk_select")
+    return int(size.value)
+
+
+def mla_dsa_topk_select(scores: torch.Tensor, row_len, top_k: int, sel_idx: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None, two_stage: bool = True):
     """DSA top-k positions of each row of fp32 scores [B, W] (row b: scores[b, :row_len[b]]).
 
     Returns (sel_idx int32 device tensor, sel_count host list): the form
-    mla_decode_latent_attn takes (rows with row_len <= top_k stay dense, -1)."""
+    mla_decode_latent_attn takes (rows with row_len <= top_k stay dense, -1).
+    two_stage: long rows run on several workgroups with a workspace (allocated
+    here unless given); False keeps every row on one workgroup."""
     if scores.dtype != torch.float32:
         raise TypeError("scores must be float32")
     if scores.dim() == 1:
@@ -321,8 +336,19 @@ def mla_dsa_topk_select(scores: torch.Tensor, row_len, top_k: int, sel_idx: torc
     elif sel_idx.dtype != torch.int32 or sel_idx.numel() < total:
         raise ValueError("sel_idx must be int32 with room for every selected index")
     counts = i32_array([0] * b)
+    size = None
+    if two_stage:
+        size = ctypes.c_size_t(0)
+        check(lib.mla_dsa_topk_select(_ptr(scores), scores.stride(0), b, i32_array(lens), int(top_k), None, counts,
+                                      None, ctypes.byref(size), _stream(scores)), "mla_dsa_topk_select")
+        if workspace is None:
+            workspace = torch.empty(max(size.value, 1), dtype=torch.uint8, device=scores.device)
+        elif workspace.numel() * workspace.element_size() < size.value:
+            raise ValueError("workspace too small")
+        size = ctypes.c_size_t(workspace.numel() * workspace.element_size())
     check(lib.mla_dsa_topk_select(_ptr(scores), scores.stride(0), b, i32_array(lens), int(top_k), _ptr(sel_idx),
-                                  counts, _stream(scores)), "mla_dsa_topk_select")
+                                  counts, _ptr(workspace) if two_stage else None,
+                                  ctypes.byref(size) if two_stage else None, _stream(scores)), "mla_dsa_topk_select")
     return sel_idx[:total], [int(c) for c in counts]
 
 

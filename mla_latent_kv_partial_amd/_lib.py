@@ -50,7 +50,7 @@ _SIGNATURES = {
     "mla_absorb_v": (ctypes.c_int, [_i32, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _p]),
     "mla_decode_combine_v": (ctypes.c_int, [
         _i32, _p, _p, _i32, _i32, _i32, _i32, _pi32, _p, _i32, _i32, _p, _p, _p, _p]),
-    "mla_dsa_topk_select": (ctypes.c_int, [_p, _i64, _i32, _pi32, _i32, _p, _pi32, _p]),
+    "mla_dsa_topk_select": (ctypes.c_int, [_p, _i64, _i32, _pi32, _i32, _p, _pi32, _p, _psz, _p]),
     "mla_o_proj_workspace_bytes": (ctypes.c_int, [_i32, _i64, _i32, _i32, _psz]),
     "mla_o_proj": (ctypes.c_int, [_i32, _p, _i64, _i32, _p, _i32, _p, _p, ctypes.c_size_t, _p]),
     "mla_append_compressed": (ctypes.c_int, [

@@ -125,8 +125,20 @@ struct TopkParams {
   int32_t row[kTopkRowsPerLaunch];
   int32_t len[kTopkRowsPerLaunch];
   int32_t out_off[kTopkRowsPerLaunch];
+  // two-stage rows: candidate area of launch row i at ws + i * kTopkRowWsBytes
+  char* ws;
 };
+// Rows of at most kTopkSeg scores, or longer than kTopkSeg * kTopkMaxSegs, or
+// whose segments' candidates exceed kTopkMaxCand, run on one workgroup
+// (launch_dsa_topk); the others on kTopkMaxSegs workgroups per row, then one
+// (launch_dsa_topk_two_stage), with kTopkRowWsBytes of workspace each.
+constexpr int kTopkSeg = 16384;
+constexpr int kTopkMaxSegs = 8;
+constexpr int kTopkMaxCand = 16384;
+constexpr size_t kTopkRowWsBytes = static_cast<size_t>(kTopkMaxCand) * 8 + 256;
+bool dsa_topk_two_stage(int64_t n, int32_t top_k);
 hipError_t launch_dsa_topk(const TopkParams& p, hipStream_t stream);
+hipError_t launch_dsa_topk_two_stage(const TopkParams& p, hipStream_t stream);
 
 // ------------------------------------------------------------------ GEMM (MFMA, bf16 operands)
 constexpr int kGemmRowsPerLaunch = 128;

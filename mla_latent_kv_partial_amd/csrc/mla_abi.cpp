@@ -403,12 +403,16 @@ int mla_append_compressed(int32_t dtype, const void* kv_a, int64_t kv_a_stride_b
 }
 
 int mla_dsa_topk_select(const float* scores, int64_t score_stride, int32_t batch, const int32_t* row_len,
-                        int32_t top_k, int32_t* sel_idx, int32_t* sel_count, hipStream_t stream) {
+                        int32_t top_k, int32_t* sel_idx, int32_t* sel_count, void* workspace,
+                        size_t* workspace_bytes, hipStream_t stream) {
   if (batch < 0) return fail(MLA_ERR_ARG, "dsa_topk: batch must be >= 0");
   if (top_k < 1) return fail(MLA_ERR_ARG, "dsa_topk: top_k must be >= 1");
-  if (batch == 0) return ok();
+  if (batch == 0) {
+    if (workspace_bytes && !workspace) *workspace_bytes = 0;
+    return ok();
+  }
   if (!scores || !row_len || !sel_count) return fail(MLA_ERR_ARG, "dsa_topk: NULL pointer");
-  int64_t total = 0;
+  int64_t total = 0, two_stage = 0;
   for (int b = 0; b < batch; ++b) {
     if (row_len[b] < 1 || row_len[b] > (1 << 30))
       return fail(MLA_ERR_SHAPE, "dsa_topk: row_len[%d] = %d outside [1, 2^30]", b, row_len[b]);
@@ -416,29 +420,47 @@ int mla_dsa_topk_select(const float* scores, int64_t score_stride, int32_t batch
       return fail(MLA_ERR_SHAPE, "dsa_topk: row_len[%d] = %d exceeds the score row stride %lld", b, row_len[b],
                   static_cast<long long>(score_stride));
     if (row_len[b] > top_k) total += top_k;
+    if (mla::dsa_topk_two_stage(row_len[b], top_k)) ++two_stage;
   }
   if (total > 0x7fffffffLL) return fail(MLA_ERR_UNSUPPORTED, "dsa_topk: more than 2^31-1 selected indices");
+  // without a workspace every row runs on one workgroup
+  const bool use_ws = workspace_bytes != nullptr;
+  const size_t need = use_ws ? static_cast<size_t>(two_stage) * mla::kTopkRowWsBytes : 0;
+  if (use_ws && !workspace) {
+    *workspace_bytes = need;
+    return ok();
+  }
+  if (use_ws && *workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "dsa_topk: workspace %zu bytes < %zu required", *workspace_bytes, need);
+  if (use_ws && reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(MLA_ERR_WORKSPACE, "dsa_topk: workspace not 256-byte aligned");
   if (total > 0 && !sel_idx) return fail(MLA_ERR_ARG, "dsa_topk: sel_idx is NULL but rows are selected");
   for (int b = 0; b < batch; ++b) sel_count[b] = row_len[b] > top_k ? top_k : -1;
-  mla::TopkParams p{};
-  p.scores = scores;
-  p.stride = score_stride;
-  p.sel_idx = sel_idx;
-  p.top_k = top_k;
+  mla::TopkParams one{}, two{};
+  one.scores = two.scores = scores;
+  one.stride = two.stride = score_stride;
+  one.sel_idx = two.sel_idx = sel_idx;
+  one.top_k = two.top_k = top_k;
+  char* ws = static_cast<char*>(workspace);
+  two.ws = ws;
   int64_t off = 0;
   for (int b = 0; b < batch; ++b) {
     if (row_len[b] <= top_k) continue;
+    mla::TopkParams& p = use_ws && mla::dsa_topk_two_stage(row_len[b], top_k) ? two : one;
     p.row[p.rows] = b;
     p.len[p.rows] = row_len[b];
     p.out_off[p.rows] = static_cast<int32_t>(off);
     off += top_k;
     if (++p.rows == mla::kTopkRowsPerLaunch) {
-      hipError_t e = mla::launch_dsa_topk(p, stream);
+      hipError_t e = &p == &two ? mla::launch_dsa_topk_two_stage(p, stream) : mla::launch_dsa_topk(p, stream);
       if (e != hipSuccess) return device(e, "dsa_topk launch");
+      if (&p == &two) two.ws += static_cast<size_t>(mla::kTopkRowsPerLaunch) * mla::kTopkRowWsBytes;
       p.rows = 0;
     }
   }
-  hipError_t e = mla::launch_dsa_topk(p, stream);
+  hipError_t e = mla::launch_dsa_topk(one, stream);
+  if (e != hipSuccess) return device(e, "dsa_topk launch");
+  e = mla::launch_dsa_topk_two_stage(two, stream);
   if (e != hipSuccess) return device(e, "dsa_topk launch");
   return ok();
 }

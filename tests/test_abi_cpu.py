@@ -155,10 +155,29 @@ def test_prefill_workspace_query_and_rejections():
     assert _prefill(ws=ctypes.c_void_p(0x10000), size=need, pad=[17])[0] == SHAPE
 
 
-def _topk(batch=2, lens=(10, 3), top_k=4, stride=16, scores=FAKE, sel=FAKE):
+def _topk(batch=2, lens=(10, 3), top_k=4, stride=16, scores=FAKE, sel=FAKE, ws=None, size=None):
     counts = i32_array([7] * max(batch, 1))
-    code = lib.mla_dsa_topk_select(scores, stride, batch, i32_array(list(lens)), top_k, sel, counts, None)
+    sz = None if size is None else ctypes.byref(size)
+    code = lib.mla_dsa_topk_select(scores, stride, batch, i32_array(list(lens)), top_k, sel, counts, ws, sz, None)
     return code, [counts[i] for i in range(max(batch, 1))]
+
+
+def test_dsa_topk_workspace_query():
+    # rows of 2..8 segments of 16384 scores whose candidates fit take the
+    # two-stage path: 131328 bytes each; the query launches nothing
+    size = ctypes.c_size_t(123)
+    assert _topk(lens=(131072, 3), top_k=2048, stride=131072, size=size)[0] == OK
+    assert size.value == 131328
+    size = ctypes.c_size_t(123)
+    assert _topk(lens=(131072, 131072), top_k=2048, stride=131072, size=size)[0] == OK
+    assert size.value == 2 * 131328
+    for lens, k in (((16384, 3), 64), ((300000, 5), 64), ((131072, 5), 4096)):   # one segment, 19, 8 x 4096
+        size = ctypes.c_size_t(123)
+        assert _topk(lens=lens, top_k=k, stride=max(lens), size=size)[0] == OK and size.value == 0
+    small = ctypes.c_size_t(131327)
+    assert _topk(lens=(131072, 3), top_k=2048, stride=131072, ws=ctypes.c_void_p(0x10000), size=small)[0] == WS
+    enough = ctypes.c_size_t(131328)
+    assert _topk(lens=(131072, 3), top_k=2048, stride=131072, ws=ctypes.c_void_p(0x10010), size=enough)[0] == WS
 
 
 @pytest.mark.parametrize("kw,code", [

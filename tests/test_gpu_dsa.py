@@ -31,15 +31,20 @@ def _scores(n, layer, kind="normal"):
     return np.ascontiguousarray(s, dtype=np.float32)
 
 
+@pytest.mark.parametrize("two_stage", [True, False], ids=["two_stage", "one_workgroup"])
 @pytest.mark.parametrize("n,k,kind", [
     (5000, 300, "normal"), (2049, 2048, "normal"), (1025, 1024, "coarse"), (10000, 1000, "coarse"),
     (3000, 64, "equal"), (4000, 700, "zeros"), (4000, 2000, "zeros"), (3333, 17, "negative"), (1, 1, "normal"),
     (131072, 2048, "normal"), (131072, 2048, "coarse"),
+    # two-stage boundaries: a 1-score last segment, three segments of 5000
+    # candidates, all ties, zeros and long tie runs across segment ends
+    (16385, 64, "normal"), (40000, 5000, "coarse"), (131072, 2048, "equal"), (131072, 2048, "zeros"),
+    (65543, 2048, "coarse"), (131072, 2048, "negative"),
 ])
-def test_topk_matches_oracle_bitwise(n, k, kind):
-    say(f"dsa topk n={n} k={k} {kind}")
+def test_topk_matches_oracle_bitwise(n, k, kind, two_stage):
+    say(f"dsa topk n={n} k={k} {kind} two_stage={two_stage}")
     s = _scores(n, layer=n % 97 + k, kind=kind)
-    got, counts = _mla().mla_dsa_topk_select(dev(s).view(1, -1), [n], k)
+    got, counts = _mla().mla_dsa_topk_select(dev(s).view(1, -1), [n], k, two_stage=two_stage)
     torch.cuda.synchronize()
     ref = oracle.dsa_select(s, k)
     if ref is None:
@@ -47,6 +52,22 @@ def test_topk_matches_oracle_bitwise(n, k, kind):
     else:
         assert counts == [k]
         assert got.cpu().numpy().tolist() == ref.tolist()
+
+
+def test_topk_rows_mix_both_forms():
+    """Rows taking the two-stage form and rows on one workgroup in one call."""
+    lens = [131072, 5000, 20000, 100, 98304]
+    k = 2048
+    w = max(lens)
+    s = np.zeros((len(lens), w), dtype=np.float32)
+    for b, n in enumerate(lens):
+        s[b, :n] = _scores(n, layer=400 + b, kind="coarse" if b % 2 else "normal")
+    assert _mla().dsa_topk_workspace_bytes(lens, k) == 3 * 131328
+    got, counts = _mla().mla_dsa_topk_select(dev(s), lens, k)
+    torch.cuda.synchronize()
+    ref_idx, ref_cnt = oracle.dsa_select_rows(s, lens, k)
+    assert counts == ref_cnt.tolist()
+    assert got.cpu().numpy().tolist() == ref_idx.tolist()
 
 
 def test_topk_rows_concatenate_with_dense_rows():
