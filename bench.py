@@ -192,16 +192,29 @@ def time_graph(torch, fn, steps, warmup):
 
 
 def kernel_sources_digest(names):
-    """sha256 over the given csrc files, to tie recorded counters to a kernel version."""
+    """sha256 over what the kernel is compiled from, to tie recorded counters to
+    a kernel version: whole csrc files, and for "file:first:last" entries the
+    lines of that file from the one starting with `first` through the one
+    starting with `last` (its parameter block inside a shared header)."""
     import hashlib
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "mla_latent_kv_partial_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        name, *rng = n.split(":")
+        with open(os.path.join(ROOT, "mla_latent_kv_partial_amd", "csrc", name), "rb") as f:
+            data = f.read()
+        if rng:
+            lines = data.decode().splitlines(keepends=True)
+            i = next(k for k, ln in enumerate(lines) if ln.startswith(rng[0]))
+            j = next(k for k, ln in enumerate(lines) if k >= i and ln.startswith(rng[1]))
+            data = "".join(lines[i:j + 1]).encode()
+        h.update(data)
     return h.hexdigest()[:16]
 
 
-ATTN_SOURCES = ("decode_mfma.hip", "cdna4.hpp", "launch.hpp", "common.hpp")
+# the attention kernel: its file, the device headers it includes and its
+# parameter block (with the row limit) in launch.hpp
+ATTN_SOURCES = ("decode_mfma.hip", "cdna4.hpp", "common.hpp", "launch.hpp:constexpr int kDecodeRowsPerLaunch:constexpr",
+                "launch.hpp:struct DecodeRows:hipError_t launch_decode(")
 ATTN_PROFILE = os.path.join(ROOT, "profiles", "decode_attn_ragged_bf16.md")
 
 
