@@ -354,6 +354,12 @@ def main():
     per_launch_bytes = cache_bytes / len(layers)
     achieved = per_launch_bytes / (ms_attn * 1e-3) / 1e9
     log(f"attention {ms_attn * 1e3:.1f} us/launch  {achieved:.0f} GB/s")
+    # the streaming probe: the same bytes, launch geometry and copy schedule,
+    # no arithmetic and no partials
+    ms_probe = time_graph(torch, lambda: [mla.mla_decode_stream_probe(ly.latent, ly.rope, ly.kv_len, ly.chunk)
+                                          for ly in layers], args.steps, args.warmup)[0] / len(layers)
+    probe_gbps = per_launch_bytes / (ms_probe * 1e-3) / 1e9
+    log(f"stream probe {ms_probe * 1e3:.1f} us/launch  {probe_gbps:.0f} GB/s")
 
     result = {
         "metric": "MLA decode rows*layers/s and achieved latent-cache HBM GB/s (% of peak)",
@@ -381,6 +387,8 @@ def main():
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(kernel_sources_digest(ATTN_SOURCES)),
             "per_launch_bytes": per_launch_bytes, "launch_us": ms_attn * 1e3,
+            "stream_probe_us": ms_probe * 1e3, "stream_probe_GBps": probe_gbps,
+            "frac_of_stream_probe": achieved / probe_gbps,
             "sources_sha256": kernel_sources_digest(ATTN_SOURCES),
         },
     }

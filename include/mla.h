@@ -194,6 +194,21 @@ int mla_decode_latent_attn(int32_t dtype, const void* q_lat,
                            int32_t* dev_err, hipStream_t stream);
 
 /*
+ * Measurement, not part of the path: for a caller who wants the copy-path
+ * floor of mla_decode_latent_attn at a given shape (roofline reporting).  It
+ * reads exactly the cache bytes the attention reads for dense rows of a packed
+ * bf16 [B, W, 576] cache (rope = latent + 512, equal strides), with the same
+ * launch geometry (one workgroup per split of chunk_len attended tokens) and
+ * the same HBM -> LDS copy schedule, and computes and writes nothing.
+ * Arguments as in mla_decode_latent_attn.  Errors: MLA_ERR_ARG, MLA_ERR_SHAPE
+ * (kv_len), MLA_ERR_UNSUPPORTED (any other layout or geometry).
+ */
+int mla_decode_stream_probe(int32_t dtype, const void* latent, int64_t latent_stride_b, int64_t latent_stride_t,
+                            const void* rope, int64_t rope_stride_b, int64_t rope_stride_t, int32_t batch,
+                            int32_t kv_lora_rank, int32_t rope_dim, int32_t width, const int32_t* kv_len,
+                            int32_t chunk_len, hipStream_t stream);
+
+/*
  * Combine split partials (flash-decoding merge).  The exact log-sum-exp
  * decomposition of the page's softmax ([P1] attendAbsorbed):
  *   LSE = ln sum_{s<n_b} exp(part_lse[b,h,s])

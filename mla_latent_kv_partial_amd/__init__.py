@@ -246,6 +246,17 @@ def mla_absorb_v(o_lat: torch.Tensor, w_kv_b: torch.Tensor, qk_nope: int, v_head
     return ctx
 
 
+def mla_decode_stream_probe(latent: torch.Tensor, rope: torch.Tensor, kv_len, chunk_len: int):
+    """Measurement: stream the cache bytes mla_decode_latent_attn reads for these
+    dense rows, with its launch geometry and copy schedule, computing nothing
+    (packed bf16 [B, W, 576] cache only)."""
+    b, w, r = latent.shape
+    check(lib.mla_decode_stream_probe(_dtype_code(latent), _ptr(latent), latent.stride(0), latent.stride(1),
+                                      _ptr(rope), rope.stride(0), rope.stride(1), b, r, rope.shape[2], w,
+                                      i32_array(_host_list(kv_len)), int(chunk_len), _stream(latent)),
+          "mla_decode_stream_probe")
+
+
 def mla_decode_combine_v(part_o: torch.Tensor, part_lse: torch.Tensor, n_splits, w_kv_b: torch.Tensor, qk_nope: int,
                          v_head: int, ctx: torch.Tensor | None = None, o_lat: torch.Tensor | None = None,
                          lse: torch.Tensor | None = None):

@@ -81,6 +81,8 @@ struct DecodeParams {
   DecodeRows tab;
 };
 hipError_t launch_decode(int32_t dtype, const DecodeParams& p, hipStream_t stream);
+// Streaming probe of the attention's copy path (packed bf16 cache, dense rows).
+hipError_t launch_stream_probe(const DecodeParams& p, hipStream_t stream);
 
 // ------------------------------------------------------------------ combine
 struct CombineParams {

@@ -289,6 +289,49 @@ int mla_decode_latent_attn(int32_t dtype, const void* q_lat, const void* q_rope,
   return ok();
 }
 
+int mla_decode_stream_probe(int32_t dtype, const void* latent, int64_t latent_stride_b, int64_t latent_stride_t,
+                            const void* rope, int64_t rope_stride_b, int64_t rope_stride_t, int32_t batch,
+                            int32_t kv_lora_rank, int32_t rope_dim, int32_t width, const int32_t* kv_len,
+                            int32_t chunk_len, hipStream_t stream) {
+  if (batch < 0 || width < 1 || chunk_len < 1) return fail(MLA_ERR_ARG, "stream_probe: bad geometry");
+  if (batch == 0) return ok();
+  if (!latent || !rope || !kv_len) return fail(MLA_ERR_ARG, "stream_probe: NULL pointer");
+  // the packed bf16 layout the attention's copy path streams
+  if (dtype != MLA_DTYPE_BF16 || kv_lora_rank != 512 || rope_dim != 64 ||
+      static_cast<const char*>(rope) != static_cast<const char*>(latent) + 2 * kv_lora_rank ||
+      rope_stride_b != latent_stride_b || rope_stride_t != latent_stride_t || latent_stride_t < 576 ||
+      latent_stride_b < 0 || (reinterpret_cast<uintptr_t>(latent) & 15) || latent_stride_b % 8 || latent_stride_t % 8)
+    return fail(MLA_ERR_UNSUPPORTED, "stream_probe: needs a packed, 16-byte aligned bf16 [B, W, 576] cache");
+  for (int b = 0; b < batch; ++b)
+    if (kv_len[b] < 1 || kv_len[b] > width)
+      return fail(MLA_ERR_SHAPE, "stream_probe: kv_len[%d] = %d outside [1, %d]", b, kv_len[b], width);
+  mla::DecodeParams p{};
+  p.lat_sb = p.rope_sb = latent_stride_b;
+  p.lat_st = p.rope_st = latent_stride_t;
+  p.r = kv_lora_rank;
+  p.dr = rope_dim;
+  p.width = width;
+  p.chunk = chunk_len;
+  for (int b0 = 0; b0 < batch; b0 += mla::kDecodeRowsPerLaunch) {
+    p.rows = std::min(batch - b0, mla::kDecodeRowsPerLaunch);
+    if ((static_cast<int64_t>(p.rows - 1) * latent_stride_b + static_cast<int64_t>(width - 1) * latent_stride_t) * 2 +
+            1152 > 0xffffffffLL)
+      return fail(MLA_ERR_UNSUPPORTED, "stream_probe: rows of a launch span more than 4 GiB");
+    p.tab.split_begin[0] = 0;
+    for (int i = 0; i < p.rows; ++i) {
+      p.tab.kv_len[i] = kv_len[b0 + i];
+      p.tab.n_att[i] = kv_len[b0 + i];
+      p.tab.sel_off[i] = -1;
+      p.tab.split_begin[i + 1] = p.tab.split_begin[i] + (kv_len[b0 + i] + chunk_len - 1) / chunk_len;
+    }
+    p.s_total = p.tab.split_begin[p.rows];
+    p.latent = p.rope = advance(latent, b0 * latent_stride_b, dtype);
+    hipError_t e = mla::launch_stream_probe(p, stream);
+    if (e != hipSuccess) return device(e, "stream_probe launch");
+  }
+  return ok();
+}
+
 namespace {
 
 // o_proj: the MFMA GEMM path (rows > 64) stages the context in bf16 in the

@@ -101,6 +101,17 @@ def test_combine_v_rejections():
     assert lib.mla_decode_combine_v(1, FAKE, FAKE, 0, 4, 8, 4, ns, FAKE, 4, 4, FAKE, None, None, None) == OK
 
 
+def test_stream_probe_rejections():
+    kv = i32_array([5, 3])
+    probe = lambda dt=1, rope=0x1400, r=512, dr=64, st=576, kvl=kv, w=8: lib.mla_decode_stream_probe(
+        dt, ctypes.c_void_p(0x1000), 8 * st, st, ctypes.c_void_p(rope), 8 * st, st, 2, r, dr, w, kvl, 32, None)
+    assert probe(dt=0) == UNSUP                        # fp32 cache
+    assert probe(rope=0x2000) == UNSUP                 # not packed: rope is not latent + 512
+    assert probe(r=256) == UNSUP
+    assert probe(kvl=i32_array([9, 3])) == SHAPE       # kv_len beyond the width
+    assert lib.mla_decode_stream_probe(1, FAKE, 0, 576, FAKE, 0, 576, 0, 512, 64, 8, kv, 32, None) == OK
+
+
 def test_absorb_rejections():
     assert lib.mla_absorb_q(5, FAKE, 1, 1, FAKE, FAKE, 1, 1, 1, 1, 1, None) == ARG
     assert lib.mla_absorb_q(0, None, 1, 1, FAKE, FAKE, 1, 1, 1, 1, 1, None) == ARG

@@ -367,3 +367,15 @@ def test_combine_v_direct_partials(wdt, heads, r, dn, dv, n_splits):
     assert np.array_equal(got[0, :dv], np.zeros(dv))   # row 0, head 0: no split, o = 0
     assert_close(host_values(o_lat), o_ref, cf.F32, "fused merge o_lat", tol=1e-5)
     assert_close(got, ctx_ref, cf.F32, "fused ctx", tol=1e-5)
+
+
+def test_stream_probe_runs_and_writes_nothing():
+    """The attention's streaming probe reads the ragged rows' cache and leaves it as it was."""
+    mla = _mla()
+    inp = cf.decode_inputs(cf.RAGGED_BF16, lengths=(700, 1, 333, 64))
+    cache = dev(np.concatenate([inp.latent, inp.rope], axis=-1))
+    before = cache.clone()
+    c = cf.RAGGED_BF16
+    mla.mla_decode_stream_probe(cache[..., :c.kv_lora_rank], cache[..., c.kv_lora_rank:], inp.kv_len, 64)
+    torch.cuda.synchronize()
+    assert torch.equal(cache.view(torch.int16), before.view(torch.int16))

@@ -15,7 +15,7 @@ from conftest import build_module
 
 B = build_module()
 
-COPY_SRC = ["decode_mfma.hip", "absorb_mfma.hip", "gemm_mfma.hip", "prefill_mfma.hip"]   # HBM -> LDS copies
+COPY_SRC = ["decode_mfma.hip", "absorb_mfma.hip", "gemm_mfma.hip", "prefill_mfma.hip", "stream_probe.hip"]   # HBM -> LDS copies
 SRC = COPY_SRC + ["combine.hip"]
 
 
@@ -46,5 +46,6 @@ def test_no_spills(name, tmp_path):
     text = _asm(name, tmp_path)
     spills = [int(v) for v in re.findall(r"\.vgpr_spill_count:\s+(\d+)", text)]
     names = re.findall(r"\.name:\s+(\S+)", text)
-    hot = [s for n, s in zip(names, spills) if any(k in n for k in ("ILi4E", "absorb", "gemm", "flash", "combine"))]
+    hot = [s for n, s in zip(names, spills)
+           if any(k in n for k in ("ILi4E", "absorb", "gemm", "flash", "combine", "stream_probe"))]
     assert hot and max(hot) == 0, list(zip(names, spills))
