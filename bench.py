@@ -20,10 +20,14 @@ launch (attended tokens x 1152 B) / its mean launch time: the attention
 launches of all layers captured alone in a HIP graph (kernels run back to
 back), HIP events around the replays.  traffic = HBM bytes per launch from the
 FETCH_SIZE / WRITE_SIZE counter runs recorded in the committed profile, only
-while the kernel sources still hash to the recorded digest.  cpu_baseline = the CPU
-oracle's reconstructed decode on a bounded sample of the same rows.  extra =
-the dense (chained and layer-stacked), DSA (chain and top-k selection) and prefill
-workloads.
+while the kernel sources still hash to the recorded digest.  stream_probe_* =
+the same bytes streamed with the attention's launch geometry and copy
+schedule and no arithmetic (the floor of that copy path at this shape);
+attn_plus_merge_* = the attention and the merge (fused with absorb_v) per
+layer.  cpu_baseline = the CPU oracle's reconstructed decode on a bounded
+sample of the same rows (and its absorbed form on the same rows).  extra = the
+dense (chained and layer-stacked), DSA (chain, layer-stacked and top-k
+selection), full-layer and prefill workloads.
 """
 
 from __future__ import annotations
@@ -254,11 +258,19 @@ def cpu_baseline(cf, oracle, layer0, budget_s=12.0):
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
+    # the absorbed form (q_lat = W_UK^T q_nope, attention over latent||rope,
+    # W_UV o_lat) on the same rows, fp64
+    ta = time.perf_counter()
+    for b in order[:rows]:
+        oracle.decode_absorbed(q_nope[b:b + 1], q_rope[b:b + 1], lat[b:b + 1], rope[b:b + 1], w,
+                               inp.kv_len[b:b + 1], None, c.softmax_scale, c.qk_nope, c.v_head)
+    dta = time.perf_counter() - ta
     threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
     return {
         "value": rows / dt, "unit": "rows*layers/s", "cores": int(threads), "kind": "oracle",
         "sample": f"reconstructed fp64 decode of {rows} row(s) of layer 0 ({tokens} cached tokens) in {dt:.1f}s",
         "cache_GBps": tokens * TOKEN_BYTES / dt / 1e9,
+        "absorbed_value": rows / dta, "absorbed_cache_GBps": tokens * TOKEN_BYTES / dta / 1e9,
         "host_cpus": len(os.sched_getaffinity(0)),
     }
 
@@ -360,6 +372,13 @@ def main():
                                           for ly in layers], args.steps, args.warmup)[0] / len(layers)
     probe_gbps = per_launch_bytes / (ms_probe * 1e-3) / 1e9
     log(f"stream probe {ms_probe * 1e3:.1f} us/launch  {probe_gbps:.0f} GB/s")
+    # attention + merge (the merge fused with absorb_v, as in the step)
+    def attn_merge():
+        for ly in layers:
+            ly.attn(mla)
+            mla.mla_decode_combine_v(ly.part_o, ly.part_lse, ly.n_splits, ly.w, ly.cfg.qk_nope, ly.cfg.v_head,
+                                     ctx=ly.ctx)
+    ms_am = time_graph(torch, attn_merge, args.steps, args.warmup)[0] / len(layers)
 
     result = {
         "metric": "MLA decode rows*layers/s and achieved latent-cache HBM GB/s (% of peak)",
@@ -389,6 +408,7 @@ def main():
             "per_launch_bytes": per_launch_bytes, "launch_us": ms_attn * 1e3,
             "stream_probe_us": ms_probe * 1e3, "stream_probe_GBps": probe_gbps,
             "frac_of_stream_probe": achieved / probe_gbps,
+            "attn_plus_merge_us": ms_am * 1e3, "attn_plus_merge_GBps": per_launch_bytes / (ms_am * 1e-3) / 1e9,
             "sources_sha256": kernel_sources_digest(ATTN_SOURCES),
         },
     }
@@ -437,7 +457,25 @@ def main():
                                 "rows_layers_per_s": len(sl) / (ms_dsa * 1e-3),
                                 "attn_launch_us": ms_dsa_attn * 1e3,
                                 "gathered_GBps": gb / (ms_dsa_attn * 1e-3) / 1e9}
-        del sl
+        # layer-stacked: the layers' selections as rows of one launch
+        st_cache = torch.cat([ly.cache for ly in sl], dim=0)
+        st_q_lat = torch.cat([ly.q_lat for ly in sl], dim=0)
+        st_q_rope = torch.cat([ly.q_rope for ly in sl], dim=0)
+        st_sel = torch.cat([ly.sel for ly in sl], dim=0)
+        st_len = [n for ly in sl for n in ly.kv_len]
+        st_cnt = [c for ly in sl for c in ly.sel_count]
+        st_chunk = mla.plan_chunk_len(st_cnt, slots)
+        st_ns = [mla.split_count(c, st_chunk) for c in st_cnt]
+        st_po = torch.empty((len(st_len), scfg.heads, max(st_ns), scfg.kv_lora_rank), dtype=torch.float32,
+                            device=dev)
+        st_pl = torch.empty((len(st_len), scfg.heads, max(st_ns)), dtype=torch.float32, device=dev)
+        ms_dst = time_graph(torch, lambda: mla.mla_decode_latent_attn(
+            st_q_lat, st_q_rope, st_cache[..., :512], st_cache[..., 512:], st_len, scfg.softmax_scale, st_chunk,
+            sel_idx=st_sel, sel_count=st_cnt, part_o=st_po, part_lse=st_pl, s_max=max(st_ns)),
+            args.steps, args.warmup)[0]
+        extra["dsa_stacked_attn"] = {"rows": len(st_len), "chunk": st_chunk, "launch_us": ms_dst * 1e3,
+                                     "gathered_GBps": len(st_len) * gb / (ms_dst * 1e-3) / 1e9}
+        del sl, st_cache, st_q_lat, st_q_rope, st_sel, st_po, st_pl
         torch.cuda.empty_cache()
         # DSA top-k selection over the 131072-token context (synthetic fp32 scores)
         import numpy as np
