@@ -82,13 +82,19 @@ def _oracle(inp, reconstructed=False):
     return out
 
 
+@pytest.mark.parametrize("plan", ["fixed", "bench"])
 @pytest.mark.parametrize("cfg", cf.DECODE_CONFIGS, ids=lambda c: c.name)
-def test_decode_chain_matches_oracle(cfg):
-    say(f"decode chain {cfg.name}: generating")
+def test_decode_chain_matches_oracle(cfg, plan):
+    """Every decode workload at full size, with a fixed chunk and with the
+    split plan bench.py times (256 concurrent workgroups)."""
+    say(f"decode chain {cfg.name} ({plan} chunk): generating")
     inp = cf.decode_inputs(cfg)
     step = Step(inp)
-    say(f"decode chain {cfg.name}: gpu")
-    got = step.run(CHUNK[cfg.name])
+    n_att = [int(c) if inp.sel_count is not None and c > 0 else int(n)
+             for n, c in zip(inp.kv_len, inp.sel_count if inp.sel_count is not None else [-1] * len(inp.kv_len))]
+    chunk = CHUNK[cfg.name] if plan == "fixed" else _mla().plan_chunk_len(n_att, 256)
+    say(f"decode chain {cfg.name}: gpu, chunk {chunk}")
+    got = step.run(chunk)
     assert int(step.err.item()) == 0
     say(f"decode chain {cfg.name}: oracle")
     ref = _oracle(inp, reconstructed=cfg.name in ("tiny_f32", "dense_bf16"))
