@@ -408,7 +408,8 @@ struct Decode {
     if (!SC) {
       // O^T leaves through LDS so that every store instruction writes two
       // whole 512-byte partial rows: the wave's region holds its dims of every
-      // head, one row per head padded to an odd number of 32-byte units.
+      // head, one row per head padded to an odd number of 32-byte units.  The
+      // stores are non-temporal.
       constexpr int kEpiDims = kR / NW;
       constexpr int kEpiRow = kEpiDims * 4 + 32;
       constexpr int kChunksPerRow = kEpiDims / 4;
@@ -427,7 +428,9 @@ struct Decode {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         const f32x4 v = *reinterpret_cast<const f32x4*>(region + row * kEpiRow + c * 16) * inv;
         const int64_t ps = (static_cast<int64_t>(b) * p.heads + head0 + row) * p.s_max + s;
-        *reinterpret_cast<float4*>(p.part_o + ps * kR + kEpiDims * hw + 4 * c) = make_float4(v[0], v[1], v[2], v[3]);
+        // non-temporal: the burst at the end of the launch does not wait on
+        // the caches (3-4 us less per 169 MB launch, measured)
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p.part_o + ps * kR + kEpiDims * hw + 4 * c));
       }
     }
   }
