@@ -56,6 +56,10 @@ constexpr int kQSteps = kR / 32 + kDR / 32;                 // 18 k-steps of the
 constexpr int kDimBlocks = kR / 16;                         // 32 output blocks of 16 dims
 constexpr float kRescaleSlack = 8.f;                        // log2 units
 constexpr int kMaxHeadGroups = 4;                           // 16-head groups per workgroup
+constexpr int kQOffset = 2 * kStageBytes;                   // queries copied to LDS: stages 2 and 3
+constexpr int kQRowBytes = kR * 2 + 32;                     // an odd number of 32-byte units per head row
+static_assert(kQOffset + 64 * kQRowBytes + 64 * kDR * 2 <= kStages * kStageBytes,
+              "the queries of a 64-head group must fit stages 2 and 3");
 static_assert(kStages * kStageBytes >= kMaxHeadGroups * (16 * kMaxHeadGroups) * (kR * 4 / kMaxHeadGroups + 32),
               "the epilogue regions of the context waves must fit in the stage ring");
 
@@ -327,7 +331,22 @@ struct Decode {
     short qrraw[kDR / 32][8];
     const bool dense_row = !(GATHER && gather_row);
     if (dense_row) issue_tile_dense(0, 0);
-    if (SC) {
+    // A launch of dense rows over 64-head groups copies the group's queries
+    // HBM -> LDS with the tile copies (coalesced 1 KB rows, counted by the
+    // same waits) into stages 2 and 3, which stay free until step 0; the
+    // score waves read their fragments there after the first barrier.
+    const bool q_copy = !GATHER && NW == 4 && p.q_copy;
+    if (q_copy) {
+      const uint32_t qdst = lds_addr(g_stage) + kQOffset;
+      const char* qsrc = static_cast<const char*>(p.q_lat) + (static_cast<int64_t>(b) * p.heads + head0) * kR * 2;
+      for (int j = wave; j < 16 * NW; j += kWaves)
+        dma16(qsrc + static_cast<int64_t>(j) * kR * 2 + lane * 16, qdst + j * kQRowBytes);
+      const int hr = 8 * wave + (lane >> 3);   // 8 heads' rope parts (128 B each) per copy
+      dma16(static_cast<const char*>(p.q_rope) +
+                (static_cast<int64_t>(b) * p.qr_sb + static_cast<int64_t>(head0 + hr) * p.qr_sh) * 2 + (lane & 7) * 16,
+            qdst + 16 * NW * kQRowBytes + wave * 1024);
+    }
+    if (SC && !q_copy) {
       const uint16_t* ql = static_cast<const uint16_t*>(p.q_lat) + (static_cast<int64_t>(b) * p.heads + head) * kR;
 #pragma unroll
       for (int ks = 0; ks < kR / 32; ++ks) qraw[ks] = *reinterpret_cast<const f32x4*>(ql + 8 * g + 32 * ks);
@@ -356,7 +375,7 @@ struct Decode {
         if (GATHER) convert_queries(qraw, qrraw);
       }
     }
-    if (SC && !GATHER) convert_queries(qraw, qrraw);
+    if (SC && !GATHER && !q_copy) convert_queries(qraw, qrraw);
     if (!SC) {
 #pragma unroll
       for (int db = 0; db < kDimBlocks; ++db) reg[db] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -374,6 +393,20 @@ struct Decode {
     for (int i = 0; i <= nt; ++i) {
       if (i < nt) wait_vm_upto<kMaxDma>(ops_after(i));
       lds_barrier();
+      if (q_copy && i == 0) {
+        // the queries landed with tile 0 (issued between tiles 0 and 1); read
+        // them before tile 2 reuses their LDS
+        if (SC) {
+          const char* qb = g_stage + kQOffset + (16 * hw + h) * kQRowBytes + 16 * g;
+#pragma unroll
+          for (int ks = 0; ks < kR / 32; ++ks) reg[ks] = *reinterpret_cast<const f32x4*>(qb + 64 * ks);
+          const char* rb = g_stage + kQOffset + 16 * NW * kQRowBytes + (16 * hw + h) * (kDR * 2) + 16 * g;
+#pragma unroll
+          for (int ks = 0; ks < kDR / 32; ++ks) reg[kR / 32 + ks] = *reinterpret_cast<const f32x4*>(rb + 64 * ks);
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
+        lds_barrier();
+      }
       if (i + 2 < nt) {
         if (GATHER && gather_row) {
           const int idx = lane < kNT ? idx_area((i + 2) % kStages)[lane] : 0;
@@ -501,8 +534,11 @@ bool decode_mfma_layout_ok(const void* q_lat, const void* latent, int64_t lat_sb
          rope_st % 8 == 0;
 }
 
-hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
-  if (p.rows == 0 || p.s_total == 0) return hipSuccess;
+hipError_t launch_decode_mfma(const DecodeParams& p0, hipStream_t stream) {
+  if (p0.rows == 0 || p0.s_total == 0) return hipSuccess;
+  DecodeParams p = p0;
+  // the query copy needs 16-byte aligned q_rope rows (q_lat rows are 1 KB)
+  p.q_copy = (reinterpret_cast<uintptr_t>(p.q_rope) & 15) == 0 && p.qr_sb % 8 == 0 && p.qr_sh % 8 == 0;
   bool gather = false;
   for (int i = 0; i < p.rows; ++i) gather |= p.tab.sel_off[i] >= 0;
   const int nw = p.heads >= 64 ? 4 : p.heads / 16;

@@ -77,6 +77,7 @@ struct DecodeParams {
   int32_t rows, heads, r, dr, width;
   int32_t chunk, s_max, s_launch;        // s_launch = max splits over the launch rows
   int32_t s_total;                       // splits of all launch rows (= split_begin[rows])
+  int32_t q_copy;                        // queries may be copied HBM -> LDS (16-byte aligned q_rope rows)
   float scale;
   DecodeRows tab;
 };
