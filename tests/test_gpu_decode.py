@@ -156,6 +156,27 @@ def test_batched_rows_equal_separate_calls_bitwise():
         assert bitwise_equal(pl_b[0, :, :ns[b]], pl[b, :, :ns[b]])
 
 
+def test_query_copy_and_register_loads_agree_bitwise():
+    """Queries with 16-byte aligned rope rows are copied to LDS with the cache
+    tiles; a rope view whose rows are not aligned takes the register loads.
+    Both read the same values: identical partials."""
+    inp = _small_ragged(lengths=(700, 5, 333), seed_layer=12)
+    step = Step(inp, packed=True)
+    mla = _mla()
+    c = inp.cfg
+    q_lat = mla.mla_absorb_q(step.q_nope, step.w, c.v_head)
+    b = step.q_rope.shape[0]
+    wide = torch.zeros((b, c.heads, c.qk_rope + 1), dtype=step.q_rope.dtype, device="cuda")
+    odd = wide[:, :, 1:]                      # rows 130 B apart, starting 2 B in: not 16-byte aligned
+    odd.copy_(step.q_rope)
+    args = (step.latent, step.rope, inp.kv_len, c.softmax_scale, 128)
+    po_a, pl_a, ns_a = mla.mla_decode_latent_attn(q_lat, step.q_rope, *args)
+    po_b, pl_b, ns_b = mla.mla_decode_latent_attn(q_lat, odd, *args)
+    torch.cuda.synchronize()
+    assert ns_a == ns_b
+    assert bitwise_equal(po_a, po_b) and bitwise_equal(pl_a, pl_b)
+
+
 def test_selection_of_all_equals_dense_bitwise():
     inp = _small_ragged(lengths=(700, 5, 333), seed_layer=9)
     step = Step(inp)
