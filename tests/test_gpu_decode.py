@@ -173,8 +173,11 @@ def test_query_copy_and_register_loads_agree_bitwise():
     po_a, pl_a, ns_a = mla.mla_decode_latent_attn(q_lat, step.q_rope, *args)
     po_b, pl_b, ns_b = mla.mla_decode_latent_attn(q_lat, odd, *args)
     torch.cuda.synchronize()
-    assert ns_a == ns_b
-    assert bitwise_equal(po_a, po_b) and bitwise_equal(pl_a, pl_b)
+    assert list(ns_a) == list(ns_b)
+    for r in range(b):                        # splits past a row's count are never written
+        n = int(ns_a[r])
+        assert bitwise_equal(po_a[r, :, :n], po_b[r, :, :n])
+        assert bitwise_equal(pl_a[r, :, :n], pl_b[r, :, :n])
 
 
 def test_selection_of_all_equals_dense_bitwise():
