@@ -52,6 +52,22 @@ __global__ __launch_bounds__(256) void absorb_q_mfma_kernel(AbsorbQParams p, Rop
     const int d = k >> 4, s = k & 15;
     dma16(w + static_cast<int64_t>(d) * p.r + 8 * (s ^ swz(d)), dst + n * 1024);
   }
+  // q rows of a 16-row batch block, lane (row m, group g): the first block is
+  // requested right behind the weight copies, so its latency overlaps theirs
+  constexpr int kMaxKs = 256 / 32;
+  const int m = lane & 15, g = lane >> 4;
+  const int nks = dn / 32;
+  const uint16_t* q = static_cast<const uint16_t*>(p.q);
+  bf16x8 qa[kMaxKs];
+  auto load_q = [&](int b0) {
+    const int b = b0 + m;
+#pragma unroll
+    for (int ks = 0; ks < kMaxKs; ++ks)
+      if (ks < nks)
+        qa[ks] = b < p.batch ? *reinterpret_cast<const bf16x8*>(q + b * p.q_sb + h * p.q_sh + 32 * ks + 8 * g)
+                             : bf16x8{};
+  };
+  load_q(0);
   if (ROPE) {
     const int64_t vecs = static_cast<int64_t>(rp.rows) * rp.tokens * rp.inner;
     const int64_t waves = static_cast<int64_t>(gridDim.x) * gridDim.y * 4;
@@ -61,17 +77,13 @@ __global__ __launch_bounds__(256) void absorb_q_mfma_kernel(AbsorbQParams p, Rop
   wait_vm<0>();
   lds_barrier();
   // ---- wave: output columns c0 + 32 wave + (0..31), two 16-column blocks
-  const int m = lane & 15, g = lane >> 4;
-  const uint16_t* q = static_cast<const uint16_t*>(p.q);
   for (int b0 = 0; b0 < p.batch; b0 += 16) {
+    if (b0 > 0) load_q(b0);
     f32x4 acc[2] = {};
-    const int b = b0 + m;
-    for (int ks = 0; ks < dn / 32; ++ks) {
-      bf16x8 a;
-      if (b < p.batch)
-        a = *reinterpret_cast<const bf16x8*>(q + b * p.q_sb + h * p.q_sh + 32 * ks + 8 * g);
-      else
-        a = bf16x8{};
+#pragma unroll
+    for (int ks = 0; ks < kMaxKs; ++ks) {
+      if (ks >= nks) break;
+      const bf16x8 a = qa[ks];
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         const int cc = (32 * wave + 16 * nb) / 8 + ((m & 3) >> 1);
