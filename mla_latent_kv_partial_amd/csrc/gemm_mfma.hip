@@ -33,35 +33,89 @@ constexpr int kGMaxDma = (kGOpDma + 3) / 4;         // copies per wave per opera
 
 __shared__ __attribute__((aligned(1024))) char g_gemm[kGStages * kGStageBytes];
 
-// Epilogue of one lane: columns n .. n+3 of row m (n a multiple of 4).  With
-// ROPE the q projection's rope columns of a head are rotated at the row's
-// position and written as split halves (pairs (v0, v1) and (v2, v3) are rope
-// pairs q0 and q0 + 1 of the head); cos and sin come from the row's table.
-template <bool ROPE, bool OUT_F32>
+// Epilogue of one lane: columns n .. n+3 of row m (n a multiple of 4), bf16
+// (round to nearest even) or fp32.
+template <bool OUT_F32>
 __device__ __forceinline__ void store_cols4(const GemmNT& p, int m, int n, const f32x4& v) {
-  uint16_t* crow = static_cast<uint16_t*>(p.c) + static_cast<int64_t>(m) * p.ldc;
-  float* frow = static_cast<float*>(p.c) + static_cast<int64_t>(m) * p.ldc;
-  const int d = ROPE ? n % kQk : 0;
-  if (ROPE && d >= kDn) {
-    const int q0 = (d - kDn) >> 1;
-    uint16_t* head = crow + (n - d) + kDn;
-    uint16_t re[2], im[2];
-    const double2* cs = p.cs + static_cast<int64_t>(m) * 32 + q0;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const double2 t = cs[e];
-      const double a = v[2 * e], b = v[2 * e + 1];
-      re[e] = f64_to_bf16(a * t.x - b * t.y);
-      im[e] = f64_to_bf16(b * t.x + a * t.y);
-    }
-    *reinterpret_cast<uint32_t*>(head + q0) = re[0] | (static_cast<uint32_t>(re[1]) << 16);
-    *reinterpret_cast<uint32_t*>(head + kDr / 2 + q0) = im[0] | (static_cast<uint32_t>(im[1]) << 16);
-  } else if (OUT_F32) {
+  if (OUT_F32) {
+    float* frow = static_cast<float*>(p.c) + static_cast<int64_t>(m) * p.ldc;
     *reinterpret_cast<float4*>(frow + n) = make_float4(v[0], v[1], v[2], v[3]);
   } else {
+    uint16_t* crow = static_cast<uint16_t*>(p.c) + static_cast<int64_t>(m) * p.ldc;
     const uint32_t lo = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
     const uint32_t hi = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
     *reinterpret_cast<uint2*>(crow + n) = make_uint2(lo, hi);
+  }
+}
+
+// A wave's output blocks: block (bm, bn) lane (i16, g) holds row
+// m_base + 16 bm + i16, columns n_base + 16 bn + 4 g .. +3.  n_base is a
+// multiple of 64 and the wave spans at most 64 columns, so with ROPE (the q
+// projection, 192 columns per head: 128 no-PE, then 64 rope) its columns are
+// either all no-PE or all the rope part of one head.  Rope columns are
+// rotated at the row's position and written as split halves: columns
+// (v0, v1) and (v2, v3) are rope pairs q0 and q0 + 1 of the head, cos and sin
+// come from the row's table in double.  The table entries of row block bm + 1
+// are requested before block bm is rotated, so their latency overlaps.
+template <bool ROPE, bool OUT_F32, int BM, int BN>
+__device__ __forceinline__ void store_tile(const GemmNT& p, const f32x4 (&acc)[BM][BN], int m_base, int n_base,
+                                           int i16, int g) {
+  static_assert(16 * BN <= 64, "a wave spans at most 64 columns");
+  if (ROPE && n_base % kQk >= kDn) {
+    const int head_col = n_base - n_base % kQk;           // first column of the head
+    const int q_lane = (n_base % kQk - kDn) / 2 + 2 * g;  // pair of column n_base + 4 g
+    double2 cur[BN][2], nxt[BN][2];
+    auto load = [&](double2 (&t)[BN][2], int bm) {
+      const int m = min(m_base + 16 * bm + i16, p.m - 1);
+      const double2* cs = p.cs + static_cast<int64_t>(m) * 32 + q_lane;
+#pragma unroll
+      for (int bn = 0; bn < BN; ++bn) {
+        t[bn][0] = cs[8 * bn];
+        t[bn][1] = cs[8 * bn + 1];
+      }
+    };
+    load(cur, 0);
+#pragma unroll
+    for (int bm = 0; bm < BM; ++bm) {
+      if (bm + 1 < BM) load(nxt, bm + 1);
+      const int m = m_base + 16 * bm + i16;
+      if (m < p.m) {
+        uint16_t* head = static_cast<uint16_t*>(p.c) + static_cast<int64_t>(m) * p.ldc + head_col + kDn;
+#pragma unroll
+        for (int bn = 0; bn < BN; ++bn) {
+          if (n_base + 16 * bn + 4 * g >= p.n) continue;
+          const int q0 = q_lane + 8 * bn;
+          uint16_t re[2], im[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const double2 t = cur[bn][e];
+            const double a = acc[bm][bn][2 * e], b = acc[bm][bn][2 * e + 1];
+            re[e] = f64_to_bf16(a * t.x - b * t.y);
+            im[e] = f64_to_bf16(b * t.x + a * t.y);
+          }
+          *reinterpret_cast<uint32_t*>(head + q0) = re[0] | (static_cast<uint32_t>(re[1]) << 16);
+          *reinterpret_cast<uint32_t*>(head + kDr / 2 + q0) = im[0] | (static_cast<uint32_t>(im[1]) << 16);
+        }
+      }
+      if (bm + 1 < BM) {
+#pragma unroll
+        for (int bn = 0; bn < BN; ++bn) {
+          cur[bn][0] = nxt[bn][0];
+          cur[bn][1] = nxt[bn][1];
+        }
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int bm = 0; bm < BM; ++bm) {
+    const int m = m_base + 16 * bm + i16;
+    if (m >= p.m) continue;
+#pragma unroll
+    for (int bn = 0; bn < BN; ++bn) {
+      const int n = n_base + 16 * bn + 4 * g;
+      if (n < p.n) store_cols4<OUT_F32>(p, m, n, acc[bm][bn]);
+    }
   }
 }
 
@@ -148,16 +202,7 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(GemmNT p) {
   }
 
   // ---- epilogue: 4 consecutive columns per lane and block
-#pragma unroll
-  for (int bm = 0; bm < 4; ++bm) {
-    const int m = m0 + 64 * wm + 16 * bm + i16;
-    if (m >= p.m) continue;
-#pragma unroll
-    for (int bn = 0; bn < 4; ++bn) {
-      const int n = n0 + 64 * wn + 16 * bn + 4 * g;
-      if (n < p.n) store_cols4<ROPE, OUT_F32>(p, m, n, acc[bm][bn]);
-    }
-  }
+  store_tile<ROPE, OUT_F32>(p, acc, m0 + 64 * wm, n0 + 64 * wn, i16, g);
 }
 
 // ------------------------------------------------------------------ 256 x 256 NT GEMM
@@ -246,16 +291,7 @@ __global__ __launch_bounds__(512) void gemm256_nt_kernel(GemmNT p) {
       for (int bn = 0; bn < 4; ++bn) acc[bm][bn] = mfma16x16x32(bfr[bn], af[bm], acc[bm][bn]);
   }
 
-#pragma unroll
-  for (int bm = 0; bm < 8; ++bm) {
-    const int m = m0 + 128 * wm + 16 * bm + i16;
-    if (m >= p.m) continue;
-#pragma unroll
-    for (int bn = 0; bn < 4; ++bn) {
-      const int n = n0 + 64 * wn + 16 * bn + 4 * g;
-      if (n < p.n) store_cols4<ROPE, OUT_F32>(p, m, n, acc[bm][bn]);
-    }
-  }
+  store_tile<ROPE, OUT_F32>(p, acc, m0 + 128 * wm, n0 + 64 * wn, i16, g);
 }
 
 // cos / sin of the q RoPE angles, one thread per (row, pair): the angle is
