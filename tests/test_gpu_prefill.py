@@ -19,7 +19,7 @@ def _mla():
     return mla
 
 
-def _gpu(inp: cf.PrefillInputs, left_pad=None):
+def _gpu(inp: cf.PrefillInputs, left_pad=None, scale=None):
     """Rotate the raw rope keys at positions 0..K-1 on the GPU, then prefill."""
     c = inp.cfg
     mla = _mla()
@@ -27,17 +27,18 @@ def _gpu(inp: cf.PrefillInputs, left_pad=None):
     mla.mla_rope_partial_interleaved(rope, 0, c.qk_rope, c.theta, out=rope)
     ctx = mla.mla_prefill_reconstructed(dev(inp.c_q), dev(inp.w_qb), dev(inp.latent), rope, dev(inp.w_kvb), c.heads,
                                         c.qk_nope, c.qk_rope, c.v_head, [int(o) for o in inp.q_offsets], c.theta,
-                                        c.softmax_scale, left_pad=left_pad)
+                                        c.softmax_scale if scale is None else scale, left_pad=left_pad)
     torch.cuda.synchronize()
     return ctx
 
 
-def _oracle(inp: cf.PrefillInputs, rows=None, left_pad=None):
+def _oracle(inp: cf.PrefillInputs, rows=None, left_pad=None, scale=None):
     c = inp.cfg
     rope = oracle.rope_partial_interleaved(cf.values(inp.k_rope_raw), 0, c.qk_rope, c.theta)
     return oracle.prefill_reconstructed(cf.values(inp.c_q), cf.values(inp.w_qb), cf.values(inp.latent), rope,
-                                        cf.values(inp.w_kvb), inp.q_offsets, c.theta, left_pad, c.softmax_scale,
-                                        c.heads, c.qk_nope, c.qk_rope, c.v_head, query_rows=rows)
+                                        cf.values(inp.w_kvb), inp.q_offsets, c.theta, left_pad,
+                                        c.softmax_scale if scale is None else scale, c.heads, c.qk_nope, c.qk_rope,
+                                        c.v_head, query_rows=rows)
 
 
 @pytest.mark.parametrize("cfg,tokens,keys", [(SMALL_F32, 96, 120), (SMALL_F32, 1, 7), (SMALL_BF16, 200, 200),
@@ -47,6 +48,19 @@ def test_prefill_small_matches_oracle(cfg, tokens, keys):
     inp = cf.prefill_inputs(cfg, tokens=tokens, keys=keys)
     got = _gpu(inp)
     assert_close(host_values(got), _oracle(inp), cfg.dtype, "ctx")
+
+
+@pytest.mark.parametrize("scale", [-0.0721, 0.0])
+def test_prefill_nonpositive_scale_matches_oracle(scale):
+    """The kernel takes the softmax max from the raw scores (their min for a
+    negative scale); a negative or zero scale is still a valid softmax."""
+    say(f"prefill scale {scale}")
+    inp = cf.prefill_inputs(SMALL_BF16, tokens=130, keys=300)
+    pads = [0, 45]
+    got = host_values(_gpu(inp, left_pad=pads, scale=scale))
+    ref = _oracle(inp, left_pad=np.array(pads), scale=scale)
+    assert_close(got[0], ref[0], cf.BF16, "row 0")
+    assert_close(got[1, 45:], ref[1, 45:], cf.BF16, "row 1 past its pad")
 
 
 def test_prefill_left_pad_matches_oracle():
