@@ -27,6 +27,7 @@ namespace {
 
 constexpr int kQCols = 128;     // absorb_q output columns per workgroup
 constexpr int kVCols = 32;      // absorb_v output columns per workgroup
+constexpr int kAvBatch = 8;     // absorb_v K steps whose loads are issued together
 
 __device__ __forceinline__ int swz(int d) { return ((d & 3) << 1) ^ (((d >> 3) & 1) << 3); }
 
@@ -125,25 +126,44 @@ __global__ __launch_bounds__(NWV * 64) void absorb_v_mfma_kernel(AbsorbVParams p
     const int b = b0 + m;
     const float* o = p.o_lat + (static_cast<int64_t>(b) * p.heads + h) * p.r + wave * kq;
     f32x4 acc[NB] = {};
-#pragma unroll 4
-    for (int ks = 0; ks < kq / 32; ++ks) {
-      bf16x8 hi = bf16x8{}, lo = bf16x8{};
-      if (b < p.batch) {
-        const float4 u = *reinterpret_cast<const float4*>(o + 32 * ks + 8 * g);
-        const float4 v = *reinterpret_cast<const float4*>(o + 32 * ks + 8 * g + 4);
-        hi = to_bf16x8(u, v);
-        const float4 ru = make_float4(u.x - static_cast<float>(hi[0]), u.y - static_cast<float>(hi[1]),
-                                      u.z - static_cast<float>(hi[2]), u.w - static_cast<float>(hi[3]));
-        const float4 rv = make_float4(v.x - static_cast<float>(hi[4]), v.y - static_cast<float>(hi[5]),
-                                      v.z - static_cast<float>(hi[6]), v.w - static_cast<float>(hi[7]));
-        lo = to_bf16x8(ru, rv);
+    // kAvBatch K steps per batch: their weight and o_lat loads are all issued
+    // before the first MFMA, so each wave keeps up to kAvBatch NB KB of
+    // weights in flight
+    const int nks = kq / 32;
+    for (int ks0 = 0; ks0 < nks; ks0 += kAvBatch) {
+      bf16x8 bw[kAvBatch][NB];
+      float4 ou[kAvBatch], ov[kAvBatch];
+#pragma unroll
+      for (int u = 0; u < kAvBatch; ++u) {
+        const int ks = ks0 + u;
+        if (ks >= nks) break;
+        if (b < p.batch) {
+          ou[u] = *reinterpret_cast<const float4*>(o + 32 * ks + 8 * g);
+          ov[u] = *reinterpret_cast<const float4*>(o + 32 * ks + 8 * g + 4);
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          // B[k = latent 32ks + 8g .. +8][n = value column 16nb + m]
+          bw[u][nb] = *reinterpret_cast<const bf16x8*>(w + static_cast<int64_t>(16 * nb + m) * p.r + 32 * ks + 8 * g);
       }
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        // B[k = latent 32ks + 8g .. +8][n = value column 16nb + m]
-        const bf16x8 bw = *reinterpret_cast<const bf16x8*>(w + static_cast<int64_t>(16 * nb + m) * p.r + 32 * ks + 8 * g);
-        acc[nb] = mfma16x16x32(hi, bw, acc[nb]);
-        acc[nb] = mfma16x16x32(lo, bw, acc[nb]);
+      for (int u = 0; u < kAvBatch; ++u) {
+        if (ks0 + u >= nks) break;
+        bf16x8 hi = bf16x8{}, lo = bf16x8{};
+        if (b < p.batch) {
+          const float4 uu = ou[u], vv = ov[u];
+          hi = to_bf16x8(uu, vv);
+          const float4 ru = make_float4(uu.x - static_cast<float>(hi[0]), uu.y - static_cast<float>(hi[1]),
+                                        uu.z - static_cast<float>(hi[2]), uu.w - static_cast<float>(hi[3]));
+          const float4 rv = make_float4(vv.x - static_cast<float>(hi[4]), vv.y - static_cast<float>(hi[5]),
+                                        vv.z - static_cast<float>(hi[6]), vv.w - static_cast<float>(hi[7]));
+          lo = to_bf16x8(ru, rv);
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          acc[nb] = mfma16x16x32(hi, bw[u][nb], acc[nb]);
+          acc[nb] = mfma16x16x32(lo, bw[u][nb], acc[nb]);
+        }
       }
     }
     // partial sums of this wave: lane (column m, group g) holds rows 4g + i
