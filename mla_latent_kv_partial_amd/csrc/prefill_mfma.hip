@@ -46,16 +46,26 @@ constexpr int kBatchPerLaunch = kGemmRowsPerLaunch;   // per-row tables travel i
 // softmax in exp2 with a lazily moved reference max, and O^T[dim, query] +=
 // V^T . P^T (V^T fragments by ds_read_b64_tr_b16, each shared by the two
 // query blocks).  The layout tricks are those of the latent decode kernel: key
-// row m of a 16-key block holds key sigma(m), and a key row is 42 chunks
-// (k_nope 16, v 16, rope 8, pad 2), an odd number of 32-byte units.
+// row m of a 16-key block holds key sigma(m), and rows are odd numbers of
+// 32-byte units.  A stage holds the tile's KV rows (k_nope 16 chunks, v 16,
+// pad 2: 544 B) and then its rope rows (8 chunks, pad 2: 160 B).  Each 1 KB
+// copy then reads either KV rows or rope rows only, from a wave-uniform base
+// (SGPRs) that moves by 32 keys per tile plus a per-lane offset that stays
+// fixed, so a tile's copies cost no vector arithmetic.
 constexpr int kAWaves = 4;                                   // waves per workgroup, 32 queries each
 constexpr int kAQ = 32 * kAWaves;
 constexpr int kAK = 32;
-constexpr int kARowChunks = 42;
-constexpr int kARowBytes = kARowChunks * 16;                 // 672
-constexpr int kATileDma = (kAK * kARowChunks + 63) / 64;      // 21
+constexpr int kAKvChunks = 34;
+constexpr int kAKvRowBytes = kAKvChunks * 16;                // 544
+constexpr int kARopeChunks = 10;
+constexpr int kARopeRowBytes = kARopeChunks * 16;            // 160
+constexpr int kAKvDma = kAK * kAKvChunks / 64;               // 17 copies of 1 KB
+constexpr int kARopeDma = kAK * kARopeChunks / 64;           // 5
+constexpr int kARopeOffset = kAKvDma * 1024;                 // rope rows after the KV rows
+constexpr int kATileDma = kAKvDma + kARopeDma;               // 22
 constexpr int kAStageBytes = kATileDma * 1024;
-// Two ring stages (43 KB of LDS) and at most 168 VGPRs let three workgroups
+static_assert(kAK * kAKvChunks % 64 == 0 && kAK * kARopeChunks % 64 == 0, "whole copies per region");
+// Two ring stages (44 KB of LDS) and at most 168 VGPRs let three workgroups
 // share a CU; at 4096 tokens that ran faster than a third stage at two
 // workgroups per CU (483 against 582 us).  With two stages each tile's copies
 // are waited for in full before the next tile is issued.
@@ -97,35 +107,52 @@ __global__ __launch_bounds__(64 * kAWaves, kAWavesPerEu) void flash_attn_kernel(
   const int k_last = min(p.keys - 1, P + min(t0 + kAQ, p.tokens) - 1);
   const int nt = k_last >= k_first ? (k_last - k_first) / kAK + 1 : 0;
 
-  // ---- copy plan (same for every tile): chunk q = 64 (wave + kAWaves j) + lane is
-  // chunk c of key row q / 42; c < 32 from the KV workspace row of head h,
-  // c < 40 from the rope row, c = 40, 41 padding (re-read chunk 0)
+  // ---- copy plan (same for every tile): copy x = wave + kAWaves j of a stage
+  // fills LDS bytes [1024 x, +1024).  x < 17: KV slot q = 64 x + lane is chunk
+  // q % 34 of KV row q / 34 (chunks 32, 33 pad: re-read chunk 0); otherwise
+  // rope slot q = 64 (x - 17) + lane is chunk q % 10 of rope row q / 10
+  // (chunks 8, 9 pad).  voff[j] = the lane's byte offset from the tile's
+  // first KV (rope) row.
   const int n_dma = (kATileDma - wave + kAWaves - 1) / kAWaves;
-  int c_row[kAMaxDma];
-  int c_off[kAMaxDma];   // byte offset in the KV head slice, or rope row (sign bit set)
-#pragma unroll
-  for (int j = 0; j < kAMaxDma; ++j) {
-    const int q = 64 * (wave + kAWaves * j) + lane;
-    const int row = q / kARowChunks;
-    const int c = q - row * kARowChunks;
-    c_row[j] = min(row, kAK - 1);
-    c_off[j] = c < 32 ? c * 16 : (c < 40 ? static_cast<int>(0x80000000u | static_cast<uint32_t>((c - 32) * 16)) : 0);
-  }
   const char* kv_base = reinterpret_cast<const char*>(p.kv + (static_cast<int64_t>(b) * p.keys * p.heads + h) * kKvw);
   const char* rope_base = reinterpret_cast<const char*>(p.rope + static_cast<int64_t>(b) * p.keys * kDr);
-  const int64_t kv_stride = static_cast<int64_t>(p.heads) * kKvw * 2;
-  auto copy = [&](int j, int k0, uint32_t dst) {
-    const int key = min(k0 + c_row[j], p.keys - 1);
-    const int off = c_off[j];
-    const char* src = off >= 0 ? kv_base + key * kv_stride + off : rope_base + key * (kDr * 2) + (off & 0x7fff);
-    dma16(src, dst + (wave + kAWaves * j) * 1024);
-  };
+  const int64_t kv_stride = static_cast<int64_t>(p.heads) * kKvw * 2;   // a multiple of 512
+  uint32_t voff[kAMaxDma];
+#pragma unroll
+  for (int j = 0; j < kAMaxDma; ++j) {
+    const int x = wave + kAWaves * j;
+    if (x < kAKvDma) {
+      const int q = 64 * x + lane;
+      const int row = q / kAKvChunks, c = q - row * kAKvChunks;
+      voff[j] = static_cast<uint32_t>(row * kv_stride + (c < 32 ? c * 16 : 0));
+    } else {
+      const int q = 64 * (x - kAKvDma) + lane;
+      const int row = q / kARopeChunks, c = q - row * kARopeChunks;
+      voff[j] = static_cast<uint32_t>(row * (kDr * 2) + (c < 8 ? c * 16 : 0));
+    }
+  }
+  // A tile past the last key: its missing rows re-read the tile's first row
+  // (same chunk; rows are whole multiples of the 512-byte / 128-byte masks),
+  // whose scores are masked and whose probabilities are exactly zero.
   auto issue = [&](int s, int tile) {
     const uint32_t dst = lds_addr(g_attn + s * kAStageBytes);
     const int k0 = k_first + tile * kAK;
+    const char* kv_t = kv_base + static_cast<int64_t>(k0) * kv_stride;
+    const char* rope_t = rope_base + static_cast<int64_t>(k0) * (kDr * 2);
+    const bool part = k0 + kAK > p.keys;
+    const int rows = p.keys - k0;
 #pragma unroll
-    for (int j = 0; j < kAMaxDma - 1; ++j) copy(j, k0, dst);
-    if (n_dma == kAMaxDma) copy(kAMaxDma - 1, k0, dst);
+    for (int j = 0; j < kAMaxDma; ++j) {
+      const int x = wave + kAWaves * j;
+      if (j == kAMaxDma - 1 && n_dma < kAMaxDma) break;
+      const bool kv = x < kAKvDma;
+      uint32_t off = voff[j];
+      if (part) {
+        const uint32_t lim = static_cast<uint32_t>(rows * (kv ? kv_stride : kDr * 2));
+        off = off < lim ? off : off & (kv ? 511u : 127u);
+      }
+      dma16_off(kv ? kv_t : rope_t, off, dst + x * 1024);
+    }
   };
 
   // ---- queries of this wave: two blocks of 16, B operands of the scores
@@ -139,8 +166,9 @@ __global__ __launch_bounds__(64 * kAWaves, kAWavesPerEu) void flash_attn_kernel(
   }
   for (int t = 0; t < kAStages - 1 && t < nt; ++t) issue(t, t);
 
-  const uint32_t k_frag = sigma(m) * kARowBytes + g * 16;
-  const uint32_t v_frag = sigma(4 * g + (m >> 2)) * kARowBytes + kDn * 2 + ((m & 3) >> 1) * 16 + (m & 1) * 8;
+  const uint32_t k_frag = sigma(m) * kAKvRowBytes + g * 16;
+  const uint32_t r_frag = kARopeOffset + sigma(m) * kARopeRowBytes + g * 16;
+  const uint32_t v_frag = sigma(4 * g + (m >> 2)) * kAKvRowBytes + kDn * 2 + ((m & 3) >> 1) * 16 + (m & 1) * 8;
   f32x4 o[2][kDv / 16];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
@@ -166,10 +194,12 @@ __global__ __launch_bounds__(64 * kAWaves, kAWavesPerEu) void flash_attn_kernel(
       for (int tb = 0; tb < 2; ++tb) s[qb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < kQk / 32; ++ks) {
-      const int off = ks < kDn / 32 ? ks * 64 : 2 * kKvw + (ks - kDn / 32) * 64;   // k_nope, then rope
+      // k_nope from the KV rows, then rope from the rope rows
+      const uint32_t addr = ks < kDn / 32 ? k_frag + ks * 64 : r_frag + (ks - kDn / 32) * 64;
+      const uint32_t row16 = ks < kDn / 32 ? 16 * kAKvRowBytes : 16 * kARopeRowBytes;
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(st + k_frag + tb * 16 * kARowBytes + off);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(st + addr + tb * row16);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
           s[qb][tb] = mfma16x16x32(kf, __builtin_bit_cast(bf16x8, qreg[qb][ks]), s[qb][tb]);
@@ -210,7 +240,7 @@ __global__ __launch_bounds__(64 * kAWaves, kAWavesPerEu) void flash_attn_kernel(
 #pragma unroll
     for (int db = 0; db < kDv / 16; ++db) {
       const s16x4 v1 = lds_read_tr16(st + v_frag + db * 32);
-      const s16x4 v2 = lds_read_tr16(st + v_frag + 16 * kARowBytes + db * 32);
+      const s16x4 v2 = lds_read_tr16(st + v_frag + 16 * kAKvRowBytes + db * 32);
       const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) o[qb][db] = mfma16x16x32(vf, pb[qb], o[qb][db]);
