@@ -209,14 +209,23 @@ __global__ __launch_bounds__(64 * kAWaves, kAWavesPerEu) void flash_attn_kernel(
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       float x[8];
+      if (k0 + kAK - 1 <= P + t_lo && k0 >= pad) {
+        // every key of the tile is visible to every query of the wave (a
+        // wave-uniform branch): no mask
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
+        for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = k0 + 16 * tb + sigma(4 * g + e);
-          const bool vis = key >= pad && key <= P + t_q[qb];
-          x[4 * tb + e] = vis ? s[qb][tb][e] * p.scale_log2 : -INFINITY;
-        }
+          for (int e = 0; e < 4; ++e) x[4 * tb + e] = s[qb][tb][e] * p.scale_log2;
+      } else {
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = k0 + 16 * tb + sigma(4 * g + e);
+            const bool vis = key >= pad && key <= P + t_q[qb];
+            x[4 * tb + e] = vis ? s[qb][tb][e] * p.scale_log2 : -INFINITY;
+          }
+      }
       float mt = x[0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) mt = fmaxf(mt, x[e]);
@@ -230,9 +239,11 @@ __global__ __launch_bounds__(64 * kAWaves, kAWavesPerEu) void flash_attn_kernel(
 #pragma unroll
         for (int db = 0; db < kDv / 16; ++db) o[qb][db] *= alpha;
       }
+      // m_run still -inf: every x of the query is -inf, and exp2(-inf - 0) = 0
+      const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float pr = m_run[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[e] - m_run[qb]);
+        const float pr = __builtin_amdgcn_exp2f(x[e] - m_use);
         l_run[qb] += pr;
         pb[qb][e] = static_cast<__bf16>(pr);
       }
