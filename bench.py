@@ -172,8 +172,10 @@ def share_partials(layers, torch, dev):
         ly.part_o, ly.part_lse, ly.s_max = po, pl, s_max
 
 
-def time_graph(torch, fn, steps, warmup):
-    """Capture fn() in a HIP graph; mean ms per replay over `steps` replays."""
+def time_graph(torch, fn, steps, warmup, blocks=1):
+    """Capture fn() in a HIP graph; mean ms per replay over `steps` replays
+    (with blocks > 1: the median over `blocks` consecutive timed blocks of
+    `steps` replays each)."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -186,13 +188,16 @@ def time_graph(torch, fn, steps, warmup):
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps, g
+    times = []
+    for _ in range(blocks):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / steps)
+    return sorted(times)[len(times) // 2], g
 
 
 def kernel_sources_digest(names):
@@ -362,14 +367,15 @@ def main():
 
     # dominant kernel: latent attention alone, one launch per layer captured in
     # a graph (back-to-back kernels, no host gaps), events around the replays
-    ms_attn = time_graph(torch, lambda: [ly.attn(mla) for ly in layers], args.steps, args.warmup)[0] / len(layers)
+    ms_attn = time_graph(torch, lambda: [ly.attn(mla) for ly in layers], args.steps, args.warmup,
+                         blocks=3)[0] / len(layers)
     per_launch_bytes = cache_bytes / len(layers)
     achieved = per_launch_bytes / (ms_attn * 1e-3) / 1e9
     log(f"attention {ms_attn * 1e3:.1f} us/launch  {achieved:.0f} GB/s")
     # the streaming probe: the same bytes, launch geometry and copy schedule,
     # no arithmetic and no partials
     ms_probe = time_graph(torch, lambda: [mla.mla_decode_stream_probe(ly.latent, ly.rope, ly.kv_len, ly.chunk)
-                                          for ly in layers], args.steps, args.warmup)[0] / len(layers)
+                                          for ly in layers], args.steps, args.warmup, blocks=3)[0] / len(layers)
     probe_gbps = per_launch_bytes / (ms_probe * 1e-3) / 1e9
     log(f"stream probe {ms_probe * 1e3:.1f} us/launch  {probe_gbps:.0f} GB/s")
     # attention + merge (the merge fused with absorb_v, as in the step)
