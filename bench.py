@@ -333,8 +333,9 @@ def o_proj_prefill_leg(torch, mla, cf, dev, rows=4096, hidden=6144):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
-              "(the multi-GPU design is described in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the decode and prefill "
+              "paths here run on a single GPU (rows or sequence slices would shard across GPUs with one "
+              "exchange of split partials per row)", file=sys.stderr)
         sys.exit(2)
     import torch
     import mla_latent_kv_partial_amd as mla
