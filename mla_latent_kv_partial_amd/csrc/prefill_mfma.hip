@@ -86,6 +86,17 @@ struct AttnMfma {
   int32_t pad[kBatchPerLaunch];
 };
 
+// Max over lanes i, i ^ 16, i ^ 32 and i ^ 48 by v_permlane16_swap and
+// v_permlane32_swap (VALU; a lane shuffle through ds_bpermute waits on LDS).
+// With both operands x, the 16-lane-row swap returns rows (0, 0, 2, 2) and
+// (1, 1, 3, 3) of x, the 32-lane swap the halves (lo, lo) and (hi, hi).
+__device__ __forceinline__ float max_lanes_xor16_32(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 __device__ __forceinline__ int sigma(int m) {
   return 2 * (m & 3) + ((m >> 2) & 1) + 8 * ((m >> 3) & 1);
 }
@@ -229,8 +240,7 @@ __global__ __launch_bounds__(64 * kAWaves, kAWavesPerEu) void flash_attn_kernel(
       float mt = x[0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) mt = fmaxf(mt, x[e]);
-      mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+      mt = max_lanes_xor16_32(mt);
       const bool move = mt > m_run[qb] + kSlack;
       if (__any(move)) {
         const float alpha = move ? __builtin_amdgcn_exp2f(m_run[qb] - mt) : 1.f;
