@@ -423,6 +423,33 @@ def main():
     # ------------------------------------------------------------- extras
     if not args.no_extra:
         extra = {}
+        # the ragged workload's 8 layer instances as the 64 rows of one launch:
+        # the same kernel with its per-launch costs (dispatch, first tiles,
+        # partial burst, kernel boundary) spread over 1351 MB; a model's
+        # layers run one after the other, so this is not the step's figure
+        wmax = max(ly.cache.shape[1] for ly in layers)
+        rows_all = sum(ly.cache.shape[0] for ly in layers)
+        rs = torch.empty((rows_all, wmax, cfg.kv_lora_rank + cfg.qk_rope), dtype=torch.bfloat16, device=dev)
+        r0 = 0
+        for ly in layers:   # rows stay right-aligned: valid tokens at [wmax - len, wmax)
+            rs[r0:r0 + ly.cache.shape[0], wmax - ly.cache.shape[1]:].copy_(ly.cache)
+            r0 += ly.cache.shape[0]
+        r_lens = [n for ly in layers for n in ly.kv_len]
+        r_q_lat = torch.cat([ly.q_lat for ly in layers], dim=0)
+        r_q_rope = torch.cat([ly.q_rope for ly in layers], dim=0)
+        r_chunk = mla.plan_chunk_len(r_lens, slots)
+        r_ns = [mla.split_count(n, r_chunk) for n in r_lens]
+        r_po = torch.empty((rows_all, cfg.heads, max(r_ns), cfg.kv_lora_rank), dtype=torch.float32, device=dev)
+        r_pl = torch.empty((rows_all, cfg.heads, max(r_ns)), dtype=torch.float32, device=dev)
+        ms_r = time_graph(torch, lambda: mla.mla_decode_latent_attn(
+            r_q_lat, r_q_rope, rs[..., :cfg.kv_lora_rank], rs[..., cfg.kv_lora_rank:], r_lens, cfg.softmax_scale,
+            r_chunk, part_o=r_po, part_lse=r_pl, s_max=max(r_ns)), args.steps, args.warmup, blocks=3)[0]
+        extra["ragged_stacked_attn"] = {"rows": rows_all, "chunk": r_chunk, "splits": sum(r_ns),
+                                        "launch_us": ms_r * 1e3, "cache_MB": cache_bytes / 1e6,
+                                        "cache_GBps": cache_bytes / (ms_r * 1e-3) / 1e9,
+                                        "frac_hbm": cache_bytes / (ms_r * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del rs, r_q_lat, r_q_rope, r_po, r_pl
+        torch.cuda.empty_cache()
         # dense workload, 64 layer instances: chained (one graph) and stacked (one launch, 64 rows)
         dcfg = cf.DENSE_BF16
         n_dense = 64

@@ -69,6 +69,17 @@ __shared__ float g_alpha[2][kMaxHeadGroups][16];                                
 __shared__ int g_moved[2][kMaxHeadGroups];                                           // any rescale in the wave
 __shared__ float g_l[kMaxHeadGroups][16];                                            // softmax denominators
 
+// Max over lanes i, i ^ 16, i ^ 32 and i ^ 48 by v_permlane16_swap and
+// v_permlane32_swap (VALU; a lane shuffle through ds_bpermute waits on LDS).
+// With both operands x, the 16-lane-row swap returns rows (0, 0, 2, 2) and
+// (1, 1, 3, 3) of x, the 32-lane swap the halves (lo, lo) and (hi, hi).
+__device__ __forceinline__ float max_lanes_xor16_32(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Token held by score row m of a 16-token block.
 __device__ __forceinline__ int sigma(int m) {
   return 2 * (m & 3) + ((m >> 2) & 1) + 8 * ((m >> 3) & 1);
@@ -213,19 +224,26 @@ struct Decode {
     }
     // lane owns head h and score rows 4g+i of both blocks: tokens 16tb + sigma(4g+i)
     float x[8];
+    if (__builtin_amdgcn_readfirstlane(valid) == 0xffffffffu) {
+      // a whole tile (wave-uniform branch): no mask
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
+      for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * tb + sigma(4 * g + i);
-        const float sc = acc[2 * tb][i] + acc[2 * tb + 1][i];
-        x[4 * tb + i] = ((valid >> t) & 1u) ? sc * scale_log2 : -INFINITY;
-      }
+        for (int i = 0; i < 4; ++i) x[4 * tb + i] = (acc[2 * tb][i] + acc[2 * tb + 1][i]) * scale_log2;
+    } else {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * tb + sigma(4 * g + i);
+          const float sc = acc[2 * tb][i] + acc[2 * tb + 1][i];
+          x[4 * tb + i] = ((valid >> t) & 1u) ? sc * scale_log2 : -INFINITY;
+        }
+    }
     float mt = x[0];
 #pragma unroll
     for (int k = 1; k < 8; ++k) mt = fmaxf(mt, x[k]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+    mt = max_lanes_xor16_32(mt);
     // Move the reference max only when this tile exceeds it by the slack (the
     // first valid tile always moves it from -inf).
     const bool move = mt > m_run + kRescaleSlack;
@@ -236,10 +254,12 @@ struct Decode {
       m_run = mt;
     }
     l_run *= alpha;
+    // m_run still -inf: every x of the head is -inf, and exp2(-inf - 0) = 0
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
     bf16x8 pb;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const float pr = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[k] - m_run);
+      const float pr = __builtin_amdgcn_exp2f(x[k] - m_use);
       l_run += pr;
       pb[k] = static_cast<__bf16>(pr);
     }
