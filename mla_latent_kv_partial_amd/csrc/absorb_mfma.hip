@@ -123,48 +123,53 @@ __global__ __launch_bounds__(NWV * 64) void absorb_v_mfma_kernel(AbsorbVParams p
   const uint16_t* w = static_cast<const uint16_t*>(p.w) +
                       (static_cast<int64_t>(h) * (p.dn + p.dv) + p.dn + v0) * p.r + wave * kq;
   for (int b0 = 0; b0 < p.batch; b0 += 16) {
-    const int b = b0 + m;
-    const float* o = p.o_lat + (static_cast<int64_t>(b) * p.heads + h) * p.r + wave * kq;
+    // rows past the batch re-read its last row: their sums are never stored,
+    // and the loads need no branch (the compiler then waits for each step's
+    // own loads rather than for the whole batch)
+    const int bl = min(b0 + m, p.batch - 1);
+    const float* o = p.o_lat + (static_cast<int64_t>(bl) * p.heads + h) * p.r + wave * kq;
     f32x4 acc[NB] = {};
+    auto step = [&](const float4& uu, const float4& vv, const bf16x8 (&bwu)[NB]) {
+      const bf16x8 hi = to_bf16x8(uu, vv);
+      const float4 ru = make_float4(uu.x - static_cast<float>(hi[0]), uu.y - static_cast<float>(hi[1]),
+                                    uu.z - static_cast<float>(hi[2]), uu.w - static_cast<float>(hi[3]));
+      const float4 rv = make_float4(vv.x - static_cast<float>(hi[4]), vv.y - static_cast<float>(hi[5]),
+                                    vv.z - static_cast<float>(hi[6]), vv.w - static_cast<float>(hi[7]));
+      const bf16x8 lo = to_bf16x8(ru, rv);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        acc[nb] = mfma16x16x32(hi, bwu[nb], acc[nb]);
+        acc[nb] = mfma16x16x32(lo, bwu[nb], acc[nb]);
+      }
+    };
+    // B[k = latent 32ks + 8g .. +8][n = value column 16nb + m]
+    auto wload = [&](int ks, int nb) {
+      return *reinterpret_cast<const bf16x8*>(w + static_cast<int64_t>(16 * nb + m) * p.r + 32 * ks + 8 * g);
+    };
     // kAvBatch K steps per batch: their weight and o_lat loads are all issued
     // before the first MFMA, so each wave keeps up to kAvBatch NB KB of
     // weights in flight
     const int nks = kq / 32;
-    for (int ks0 = 0; ks0 < nks; ks0 += kAvBatch) {
+    const int nfull = nks / kAvBatch * kAvBatch;
+    for (int ks0 = 0; ks0 < nfull; ks0 += kAvBatch) {
       bf16x8 bw[kAvBatch][NB];
       float4 ou[kAvBatch], ov[kAvBatch];
 #pragma unroll
       for (int u = 0; u < kAvBatch; ++u) {
-        const int ks = ks0 + u;
-        if (ks >= nks) break;
-        if (b < p.batch) {
-          ou[u] = *reinterpret_cast<const float4*>(o + 32 * ks + 8 * g);
-          ov[u] = *reinterpret_cast<const float4*>(o + 32 * ks + 8 * g + 4);
-        }
+        ou[u] = *reinterpret_cast<const float4*>(o + 32 * (ks0 + u) + 8 * g);
+        ov[u] = *reinterpret_cast<const float4*>(o + 32 * (ks0 + u) + 8 * g + 4);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          // B[k = latent 32ks + 8g .. +8][n = value column 16nb + m]
-          bw[u][nb] = *reinterpret_cast<const bf16x8*>(w + static_cast<int64_t>(16 * nb + m) * p.r + 32 * ks + 8 * g);
+        for (int nb = 0; nb < NB; ++nb) bw[u][nb] = wload(ks0 + u, nb);
       }
 #pragma unroll
-      for (int u = 0; u < kAvBatch; ++u) {
-        if (ks0 + u >= nks) break;
-        bf16x8 hi = bf16x8{}, lo = bf16x8{};
-        if (b < p.batch) {
-          const float4 uu = ou[u], vv = ov[u];
-          hi = to_bf16x8(uu, vv);
-          const float4 ru = make_float4(uu.x - static_cast<float>(hi[0]), uu.y - static_cast<float>(hi[1]),
-                                        uu.z - static_cast<float>(hi[2]), uu.w - static_cast<float>(hi[3]));
-          const float4 rv = make_float4(vv.x - static_cast<float>(hi[4]), vv.y - static_cast<float>(hi[5]),
-                                        vv.z - static_cast<float>(hi[6]), vv.w - static_cast<float>(hi[7]));
-          lo = to_bf16x8(ru, rv);
-        }
+      for (int u = 0; u < kAvBatch; ++u) step(ou[u], ov[u], bw[u]);
+    }
+    for (int ks = nfull; ks < nks; ++ks) {
+      bf16x8 bw[NB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          acc[nb] = mfma16x16x32(hi, bw[u][nb], acc[nb]);
-          acc[nb] = mfma16x16x32(lo, bw[u][nb], acc[nb]);
-        }
-      }
+      for (int nb = 0; nb < NB; ++nb) bw[nb] = wload(ks, nb);
+      step(*reinterpret_cast<const float4*>(o + 32 * ks + 8 * g), *reinterpret_cast<const float4*>(o + 32 * ks + 8 * g + 4),
+           bw);
     }
     // partial sums of this wave: lane (column m, group g) holds rows 4g + i
 #pragma unroll
