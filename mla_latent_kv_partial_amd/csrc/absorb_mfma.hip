@@ -17,6 +17,8 @@
 //   load directly; the latent axis is split over the 4 waves and the partial
 //   sums are added in LDS.  o_lat (fp32) enters as a bf16 high part plus a
 //   bf16 residual (two MFMAs), which keeps about 16 bits of its mantissa.
+#include <algorithm>
+
 #include "cdna4.hpp"
 #include "common.hpp"
 #include "launch.hpp"
@@ -110,13 +112,15 @@ __global__ __launch_bounds__(256) void absorb_q_mfma_kernel(AbsorbQParams p, Rop
   }
 }
 
-// NB 16-column blocks per workgroup, NWV waves splitting the latent axis.
+// NB 16-column blocks per workgroup, of which the first `cols` columns are
+// the workgroup's (cols <= 16 NB); NWV waves splitting the latent axis.
 template <int NB, int NWV>
-__global__ __launch_bounds__(NWV * 64) void absorb_v_mfma_kernel(AbsorbVParams p) {
+__global__ __launch_bounds__(NWV * 64) void absorb_v_mfma_kernel(AbsorbVParams p, int cols) {
   constexpr int kCols = 16 * NB;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int v0 = blockIdx.x * kCols;
+  const int v0 = blockIdx.x * cols;
+  const int ncol = min(cols, p.dv - v0);   // columns of this workgroup that exist
   const int h = blockIdx.y;
   const int m = lane & 15, g = lane >> 4;
   const int kq = p.r / NWV;                 // latent range of this wave (a multiple of 32)
@@ -144,7 +148,9 @@ __global__ __launch_bounds__(NWV * 64) void absorb_v_mfma_kernel(AbsorbVParams p
     };
     // B[k = latent 32ks + 8g .. +8][n = value column 16nb + m]
     auto wload = [&](int ks, int nb) {
-      return *reinterpret_cast<const bf16x8*>(w + static_cast<int64_t>(16 * nb + m) * p.r + 32 * ks + 8 * g);
+      // columns past the workgroup's re-read its last one (never stored)
+      const int col = min(16 * nb + m, ncol - 1);
+      return *reinterpret_cast<const bf16x8*>(w + static_cast<int64_t>(col) * p.r + 32 * ks + 8 * g);
     };
     // kAvBatch K steps per batch: their weight and o_lat loads are all issued
     // before the first MFMA, so each wave keeps up to kAvBatch NB KB of
@@ -180,7 +186,7 @@ __global__ __launch_bounds__(NWV * 64) void absorb_v_mfma_kernel(AbsorbVParams p
     for (int e = threadIdx.x; e < 16 * kCols; e += NWV * 64) {
       const int row = e / kCols, col = e % kCols;
       const int bb = b0 + row;
-      if (bb < p.batch) {
+      if (bb < p.batch && col < ncol) {
         float sum = 0.f;
 #pragma unroll
         for (int wv = 0; wv < NWV; ++wv) sum += g_vsum[wv][row][col];
@@ -217,11 +223,21 @@ hipError_t launch_absorb_q_rope_mfma(const AbsorbQParams& p, const RopeParams& r
 
 hipError_t launch_absorb_v_mfma(const AbsorbVParams& p, hipStream_t stream) {
   // 32 columns and 4 waves per workgroup while that fills the CUs; otherwise
-  // 16 columns and 8 waves (a long latent axis over few heads, as in o_proj).
-  if (static_cast<int64_t>(p.dv / kVCols) * p.heads >= 256 || p.r % (8 * 32) != 0)
-    hipLaunchKernelGGL((absorb_v_mfma_kernel<2, 4>), dim3(p.dv / kVCols, p.heads), dim3(256), 0, stream, p);
+  // 8 waves (a long latent axis over few heads, as in o_proj) and 16 to 32
+  // columns per workgroup, as many as make the workgroups about one per CU
+  // (o_proj to 6144 columns: 384 blocks of 16 left half the CUs with two,
+  // 256 blocks of 24 give every CU the same bytes).
+  if (static_cast<int64_t>(p.dv / kVCols) * p.heads >= 256 || p.r % (8 * 32) != 0) {
+    hipLaunchKernelGGL((absorb_v_mfma_kernel<2, 4>), dim3(p.dv / kVCols, p.heads), dim3(256), 0, stream, p, kVCols);
+    return hipGetLastError();
+  }
+  const int64_t per_cu = (static_cast<int64_t>(p.dv) * p.heads + 255) / 256;
+  const int cols = static_cast<int>(std::min<int64_t>(32, std::max<int64_t>(16, (per_cu + 7) / 8 * 8)));
+  const dim3 grid(static_cast<uint32_t>((p.dv + cols - 1) / cols), p.heads);
+  if (cols <= 16)
+    hipLaunchKernelGGL((absorb_v_mfma_kernel<1, 8>), grid, dim3(512), 0, stream, p, cols);
   else
-    hipLaunchKernelGGL((absorb_v_mfma_kernel<1, 8>), dim3(p.dv / 16, p.heads), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((absorb_v_mfma_kernel<2, 8>), grid, dim3(512), 0, stream, p, cols);
   return hipGetLastError();
 }
 

@@ -19,7 +19,8 @@ def _mla():
 
 
 @pytest.mark.parametrize("dtype,rows,width,hidden", [
-    (cf.BF16, 8, 8192, 6144),      # decode rows: weight streaming on MFMA
+    (cf.BF16, 8, 8192, 6144),      # decode rows: weight streaming on MFMA (256 blocks of 24 columns)
+    (cf.BF16, 8, 1024, 4160),      # 24-column blocks, the last one partial (8 columns)
     (cf.BF16, 64, 1024, 512),
     (cf.BF16, 200, 8192, 6144),    # GEMM path, partial M tile
     (cf.BF16, 130, 512, 300),      # GEMM path, partial N tile
