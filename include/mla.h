@@ -6,7 +6,8 @@
  *   [P1] "mlx-bun 0.0.11 -> 0.0.13", package/src/model/glm52-mla.ts
  *   [P2] "mlx-bun 0.2.0 -> 0.4.0", glm52-mla.ts (left-padding mask) and
  *        glm52-cache.ts (right-aligned rows, per-row lengths, left pad)
- *   [P3] "mlx-bun 0.4.0 -> 1.0.0", glm52-dsa.ts (DSA top-k selection)
+ *   [P2] also glm52-dsa.ts (selectGlm52DsaDevice, the DSA top-k selection)
+ *   [P3] "mlx-bun 0.4.0 -> 1.0.0", glm52.ts (the DSA indexer's dense fallback)
  *
  * A decode step is the chain
  *   mla_rope_partial_interleaved (q rope part)  ->  mla_absorb_q  ->
@@ -304,8 +305,8 @@ int mla_o_proj(int32_t dtype, const float* ctx, int64_t rows, int32_t in_feature
                float* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * DSA top-k position selection.  [P3] selectGlm52DsaDevice, with the dense
- * fallback of the page's indexer (a context not longer than top_k is
+ * DSA top-k position selection.  [P2] glm52-dsa.ts, selectGlm52DsaDevice,
+ * with the dense fallback of the [P3] indexer (a context not longer than top_k is
  * attended densely).  For row b with n = row_len[b] > top_k, over the fp32
  * scores s[0..n) at scores + b * score_stride:
  *   rank key  = bitwise NOT of the order-preserving uint32 image of s[i]

@@ -1,4 +1,4 @@
-// DSA top-k position selection (page "mlx-bun 0.4.0 -> 1.0.0", glm52-dsa.ts,
+// DSA top-k position selection (page "mlx-bun 0.2.0 -> 0.4.0", glm52-dsa.ts,
 // selectGlm52DsaDevice).  Per row of float32 scores s[0..n), n > top_k:
 //   rank key  = ~(order-preserving uint32 of the float bits), so ascending
 //               keys are descending scores and equal keys mean equal bits;

@@ -2,10 +2,11 @@
 
 TEST INFRASTRUCTURE ONLY (see oracle/__init__.py).
 
-Follows page "mlx-bun 0.4.0 -> 1.0.0", file glm52-dsa.ts,
+Follows page "mlx-bun 0.2.0 -> 0.4.0", file glm52-dsa.ts,
 selectGlm52DsaDevice (the deterministic device form of the threshold-ties
-selection), with the dense fallback of the same page's indexer: a row whose
-context is not longer than top_k attends densely (no selection).
+selection), with the dense fallback of the indexer on page
+"mlx-bun 0.4.0 -> 1.0.0", file glm52.ts: a row whose context is not longer
+than top_k attends densely (no selection).
 
 Selection of one row of float32 scores s[0..n):
   1. rank key: the order-preserving map of the float bits to uint32 (negative

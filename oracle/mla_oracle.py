@@ -365,6 +365,35 @@ def combine_partials(part_o, part_lse, n_splits):
 # before the row's left pad are masked as well.
 # ---------------------------------------------------------------------------
 
+def prefill_queries(c_q, w_qb, q_offsets, theta, heads: int, qk_nope: int, qk_rope: int,
+                    query_rows: Sequence[int] | None = None):
+    """The prefill queries of page "mlx-bun 0.0.11 -> 0.0.13", glm52-mla.ts,
+    Glm52Mla.project, from the normalised q-LoRA state on.
+
+    q = c_q . w_qb^T ([B, T', H*(dn+dr)]), viewed as [B, T', H, dn+dr]: head h
+    owns features [h(dn+dr), (h+1)(dn+dr)) of the projection.  Within a head the
+    first dn features are q_nope and the last dr the rope part, which is rotated
+    by partial interleaved RoPE at position q_offsets[b] + t.
+    Returns (q_nope [B, T', H, dn], q_rope [B, T', H, dr]).
+    """
+    c_q = np.asarray(c_q, dtype=np.float64)
+    w_qb = np.asarray(w_qb, dtype=np.float64)
+    batch, tokens, _ = c_q.shape
+    qk = qk_nope + qk_rope
+    if w_qb.shape[0] != heads * qk:
+        raise OracleError("q_b_proj rows != heads * (qk_nope + qk_rope)")
+    rows = np.arange(tokens) if query_rows is None else np.asarray(query_rows, dtype=np.int64)
+    inv = rope_inverse_frequencies(qk_rope, theta)
+    q_nope = np.zeros((batch, len(rows), heads, qk_nope))
+    q_rope = np.zeros((batch, len(rows), heads, qk_rope))
+    for b in range(batch):
+        q = (c_q[b, rows] @ w_qb.T).reshape(len(rows), heads, qk)
+        q_nope[b] = q[..., :qk_nope]
+        ang = rope_angles(int(q_offsets[b]) + rows, inv)[:, None, :]   # [T', 1, dr/2]
+        q_rope[b] = rope_rotate(q[..., qk_nope:], ang, qk_rope)
+    return q_nope, q_rope
+
+
 def prefill_reconstructed(c_q, w_qb, latent, rope, w_kvb, q_offsets, theta, left_pad, scale,
                           heads: int, qk_nope: int, qk_rope: int, v_head: int,
                           query_rows: Sequence[int] | None = None) -> np.ndarray:
@@ -389,13 +418,10 @@ def prefill_reconstructed(c_q, w_qb, latent, rope, w_kvb, q_offsets, theta, left
     prefix = keys - tokens
     pads = np.zeros(batch, dtype=np.int64) if left_pad is None else np.asarray(left_pad, dtype=np.int64)
     w_uk, w_uv = split_kv_b(w_kvb, heads, qk_nope, v_head)
-    inv = rope_inverse_frequencies(qk_rope, theta)
+    q_nope_all, q_rope_all = prefill_queries(c_q, w_qb, q_offsets, theta, heads, qk_nope, qk_rope, rows)
     out = np.zeros((batch, len(rows), heads * v_head))
     for b in range(batch):
-        q = (c_q[b, rows] @ w_qb.T).reshape(len(rows), heads, qk)
-        q_nope = q[..., :qk_nope]
-        ang = rope_angles(int(q_offsets[b]) + rows, inv)[:, None, :]   # [T', 1, dr/2]
-        q_rope = rope_rotate(q[..., qk_nope:], ang, qk_rope)
+        q_nope, q_rope = q_nope_all[b], q_rope_all[b]
         k_nope = np.einsum("kr,hdr->hkd", latent[b], w_uk)              # [H, K, dn]
         v = np.einsum("kr,hvr->hkv", latent[b], w_uv)                   # [H, K, dv]
         kidx = np.arange(keys)

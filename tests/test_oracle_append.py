@@ -2,6 +2,7 @@
 glm52-mla.ts: rmsNormF32Mlx and the kv_a split of Glm52Mla.project)."""
 
 import json
+import math
 import os
 
 import numpy as np
@@ -10,6 +11,32 @@ import pytest
 import oracle
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "rms_norm_hand_example.json")
+SPLIT = os.path.join(os.path.dirname(__file__), "golden", "append_split_hand_example.json")
+
+# closed forms of the append golden file
+_FORMS = {
+    "6/sqrt12.5": 6 / math.sqrt(12.5),
+    "2/sqrt12.5": 2 / math.sqrt(12.5),
+    "cos(1)": math.cos(1.0),
+    "sin(1)": math.sin(1.0),
+    "cos(f32(0.01))": math.cos(float(np.float32(0.01))),
+    "-sin(f32(0.01))": -math.sin(float(np.float32(0.01))),
+}
+
+
+def _vals(x):
+    if isinstance(x, list):
+        return np.array([_vals(v) for v in x])
+    return _FORMS[x] if isinstance(x, str) else float(x)
+
+
+def test_append_split_hand_example():
+    """kv_a = [latent (first r) | rope key (last dr)]: RMSNorm on the first, RoPE on the second."""
+    g = json.load(open(SPLIT))
+    lat, rope = oracle.append_compressed(_vals(g["kv_a"]), _vals(g["weight"]), g["eps"], g["positions"], g["theta"],
+                                         g["kv_lora_rank"], g["rope_dim"])
+    np.testing.assert_allclose(lat, _vals(g["expected_latent"]), rtol=1e-15, atol=0)
+    np.testing.assert_allclose(rope, _vals(g["expected_rope"]), rtol=1e-15, atol=1e-16)
 
 
 def test_rms_norm_hand_example():

@@ -1,6 +1,7 @@
-"""Pins of the DSA top-k selector oracle (page "mlx-bun 0.4.0 -> 1.0.0",
-glm52-dsa.ts, selectGlm52DsaDevice) against the page's hand example, brute
-force on tiny inputs, and closed forms."""
+"""Pins of the DSA top-k selector oracle (page "mlx-bun 0.2.0 -> 0.4.0",
+glm52-dsa.ts, selectGlm52DsaDevice) against a hand-worked example of the
+page's rule (the page prints no values), brute force on tiny inputs, and
+closed forms."""
 
 import json
 import os

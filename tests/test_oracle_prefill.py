@@ -5,12 +5,45 @@ and attendReconstructed (kv_b_proj expansion, causal mask with last visible key
 prefix + t); page "mlx-bun 0.2.0 -> 0.4.0", glm52-mla.ts: left-padding mask.
 """
 
+import json
 import math
+import os
 
 import numpy as np
 import torch
 
 import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "prefill_q_split_hand_example.json")
+
+
+def _val(v):
+    """A number of the golden file: a float, or "lnX" for the natural log of X."""
+    if isinstance(v, str):
+        assert v.startswith("ln"), v
+        return math.log(float(v[2:]))
+    return float(v)
+
+
+def _vals(x):
+    return np.array([_vals(v) for v in x]) if isinstance(x, list) else _val(x)
+
+
+def test_query_split_hand_example():
+    """Head-major view of the q_b projection, no-PE part first, rope part last,
+    RoPE at position 0 = the de-interleave; then the causal softmax over two keys."""
+    g = json.load(open(GOLDEN))
+    h, dn, dr, dv = g["heads"], g["qk_nope"], g["qk_rope"], g["v_head"]
+    c_q = _vals(g["c_q"])[None, None]                    # [1, 1, ql]
+    w_qb = _vals(g["w_qb"])                              # [H (dn+dr), ql]
+    q_nope, q_rope = oracle.prefill_queries(c_q, w_qb, [g["q_offset"]], g["theta"], h, dn, dr)
+    assert np.array_equal(q_nope[0, 0], _vals(g["expected_q_nope"]))
+    assert np.array_equal(q_rope[0, 0], _vals(g["expected_q_rope"]))
+    latent = _vals(g["latent"])[None]                    # [1, K=2, r]
+    rope = _vals(g["rope"])[None]                        # [1, 2, dr]
+    ctx = oracle.prefill_reconstructed(c_q, w_qb, latent, rope, _vals(g["kv_b"]), [g["q_offset"]], g["theta"], None,
+                                       g["scale"], h, dn, dr, dv)
+    np.testing.assert_allclose(ctx[0, 0], _vals(g["expected_ctx"]), rtol=1e-14, atol=1e-15)
 
 
 def _problem(seed, batch=1, tokens=6, keys=6, heads=3, ql=7, dn=4, dr=4, dv=5, r=6, theta=10000.0):
@@ -33,11 +66,18 @@ def _prefill(p, query_rows=None):
 
 
 def _queries(p):
-    """q_nope, rotated q_rope [B,T,H,*] through the oracle's own RoPE entry."""
+    """q_nope, rotated q_rope [B,T,H,*]: the query step the hand example pins."""
+    return oracle.prefill_queries(p["c_q"], p["w_qb"], p["q_offsets"], p["theta"], p["heads"], p["dn"], p["dr"])
+
+
+def test_query_step_rope_matches_rope_entry():
+    """The queries' rope part equals the RoPE entry applied to the projected rope features."""
+    p = _problem(6, batch=2, tokens=3, keys=5)
+    _, q_rope = _queries(p)
     b, t, _ = p["c_q"].shape
-    q = (p["c_q"] @ p["w_qb"].T).reshape(b, t, p["heads"], p["dn"] + p["dr"])
-    q_rope = oracle.rope_partial_interleaved(q[..., p["dn"]:], [int(o) for o in p["q_offsets"]], p["dr"], p["theta"])
-    return q[..., :p["dn"]], q_rope
+    raw = (p["c_q"] @ p["w_qb"].T).reshape(b, t, p["heads"], p["dn"] + p["dr"])[..., p["dn"]:]
+    ref = oracle.rope_partial_interleaved(raw, [int(o) for o in p["q_offsets"]], p["dr"], p["theta"])
+    assert np.array_equal(q_rope, ref)
 
 
 def test_matches_torch_sdpa_causal_with_prefix():
