@@ -362,10 +362,12 @@ int mla_dsa_topk_select(const float* scores, int64_t score_stride, int32_t batch
  * that sees no key (inside the pad) gets ctx = 0.  ctx fp32 [batch, tokens,
  * heads*v_head].
  *
- * Workspace: with workspace == NULL the call stores the bytes it needs in
- * *workspace_bytes and returns MLA_OK without enqueuing anything.  Otherwise
- * *workspace_bytes must be at least that size (MLA_ERR_WORKSPACE) and the
- * device buffer must be 256-byte aligned; its contents are scratch.
+ * Workspace: with workspace == NULL the call stores in *workspace_bytes a
+ * size that suffices for these shapes whatever the data pointers (the other
+ * pointers may be NULL then) and returns MLA_OK without enqueuing anything.
+ * Otherwise *workspace_bytes must be at least the size the call's path needs
+ * (never more than the queried size; MLA_ERR_WORKSPACE) and the device
+ * buffer must be 256-byte aligned; its contents are scratch.
  * Limits (MLA_ERR_UNSUPPORTED): qk_nope + qk_rope <= 256, v_head <= 256,
  * qk_rope <= 512.
  */

@@ -95,7 +95,7 @@ def mla_rope_partial_interleaved(x: torch.Tensor, position_offset, rotary_dims: 
                                  token_axis: int = 1, out: torch.Tensor | None = None) -> torch.Tensor:
     """Partial interleaved RoPE of `x` (rank >= 2, feature axis last); `out=x` rotates in place."""
     if x.dim() < 2:
-        raise ValueError("partial interleaved RoPE requires rank >= 2")
+        raise ValueError(f"x has ndim {x.dim()}: a token axis and a feature axis are needed")
     rank = x.dim()
     axis = token_axis + rank if token_axis < 0 else token_axis
     if not 0 <= axis < rank - 1:
@@ -116,9 +116,9 @@ def mla_rope_partial_interleaved(x: torch.Tensor, position_offset, rotary_dims: 
     batch, sb = lead
     if per_row:
         if axis == 0:
-            raise ValueError("per-row RoPE offsets require a separate token axis")
+            raise ValueError("per-row offsets index axis 0: put the tokens on another axis")
         if len(offsets) != shape[0]:
-            raise ValueError(f"RoPE row offsets {len(offsets)} != batch {shape[0]}")
+            raise ValueError(f"{len(offsets)} offsets for {shape[0]} rows")
         rep = batch // shape[0] if shape[0] else 1
         offsets = [o for o in offsets for _ in range(rep)]
     tokens, st = shape[axis], strides[axis]

@@ -457,7 +457,12 @@ struct Decode {
         p.part_lse[ps] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
       }
     }
-    lds_barrier();   // every wave is past the loop and its copies: the stages are free
+    // A split of one tile still copied tile 1 (the fixed wait counts above),
+    // and gathered rows copy index tiles that no count covers: wait for all of
+    // this wave's copies before the barrier, so that no copy can land in the
+    // stages while the context waves stage O^T there.
+    wait_vm<0>();
+    lds_barrier();   // every wave's copies have landed: the stages are free
     if (!SC) {
       // O^T leaves through LDS so that every store instruction writes two
       // whole 512-byte partial rows: the wave's region holds its dims of every
@@ -542,8 +547,11 @@ hipError_t launch_nw(const DecodeParams& p, bool packed, int groups, hipStream_t
 
 }  // namespace
 
+// Head counts of the instantiated groupings: one workgroup of 16 or 32 heads,
+// or groups of 64 heads.  Other multiples of 16 (48, 80, ...) would need a
+// grouping the kernel does not have; they take the generic kernel.
 bool decode_mfma_supported(int32_t dtype, int32_t heads, int32_t r, int32_t dr) {
-  return dtype == kBF16 && r == kR && dr == kDR && heads % 16 == 0 && (heads <= 64 || heads % 64 == 0);
+  return dtype == kBF16 && r == kR && dr == kDR && heads > 0 && (heads == 16 || heads == 32 || heads % 64 == 0);
 }
 
 // Layout requirements of the copy path: 16-byte aligned rows.
@@ -561,7 +569,7 @@ hipError_t launch_decode_mfma(const DecodeParams& p0, hipStream_t stream) {
   p.q_copy = (reinterpret_cast<uintptr_t>(p.q_rope) & 15) == 0 && p.qr_sb % 8 == 0 && p.qr_sh % 8 == 0;
   bool gather = false;
   for (int i = 0; i < p.rows; ++i) gather |= p.tab.sel_off[i] >= 0;
-  const int nw = p.heads >= 64 ? 4 : p.heads / 16;
+  const int nw = p.heads % 64 == 0 ? 4 : p.heads / 16;   // 1, 2 or 4 (decode_mfma_supported)
   const int groups = p.heads / (16 * nw);
   // Packed cache: rope right after the latent, same strides, and every byte
   // offset of a row start (plus its 1152 bytes) below 2^32.
@@ -572,7 +580,8 @@ hipError_t launch_decode_mfma(const DecodeParams& p0, hipStream_t stream) {
   switch (nw) {
     case 1: return gather ? launch_nw<1, true>(p, packed, groups, stream) : launch_nw<1, false>(p, packed, groups, stream);
     case 2: return gather ? launch_nw<2, true>(p, packed, groups, stream) : launch_nw<2, false>(p, packed, groups, stream);
-    default: return gather ? launch_nw<4, true>(p, packed, groups, stream) : launch_nw<4, false>(p, packed, groups, stream);
+    case 4: return gather ? launch_nw<4, true>(p, packed, groups, stream) : launch_nw<4, false>(p, packed, groups, stream);
+    default: return hipErrorInvalidValue;   // unreachable behind decode_mfma_supported
   }
 }
 

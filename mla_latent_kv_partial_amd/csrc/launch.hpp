@@ -190,7 +190,8 @@ struct PrefillParams {
   void* workspace;
   float* ctx;
 };
-size_t prefill_workspace_bytes(const PrefillParams& p);
+size_t prefill_workspace_bytes(const PrefillParams& p);            // of the path these buffers take
+size_t prefill_workspace_bytes_any_path(const PrefillParams& p);   // enough for either path
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 
 // Inverse-frequency table of partial interleaved RoPE, built on the host in

@@ -84,15 +84,15 @@ int mla_rope_partial_interleaved(int32_t dtype, const void* x, void* y, int32_t 
     return fail(MLA_ERR_ARG, "rope: batch, tokens, inner must be >= 0 and feat >= 1");
   if (!offsets) return fail(MLA_ERR_ARG, "rope: offsets is NULL");
   if (n_offsets != 1 && n_offsets != batch)
-    return fail(MLA_ERR_ROPE, "RoPE row offsets %d != batch %d", n_offsets, batch);
+    return fail(MLA_ERR_ROPE, "rope: n_offsets=%d, need 1 or batch=%d", n_offsets, batch);
   for (int i = 0; i < n_offsets; ++i) {
-    if (offsets[i] < 0) return fail(MLA_ERR_ROPE, "RoPE position offset must be a non-negative integer");
+    if (offsets[i] < 0) return fail(MLA_ERR_ROPE, "rope: offsets[%d] = %lld < 0", i, static_cast<long long>(offsets[i]));
     if (static_cast<double>(offsets[i]) + tokens > kMaxPosition)
       return fail(MLA_ERR_UNSUPPORTED, "rope: offset + tokens exceeds 2^53");
   }
   if (rotary_dims <= 0 || (rotary_dims & 1) || rotary_dims > feat)
-    return fail(MLA_ERR_ROPE, "RoPE dimensions must be positive, even, and fit the feature axis");
-  if (!(theta > 0.0) || !isfinite(theta)) return fail(MLA_ERR_ROPE, "RoPE theta must be positive");
+    return fail(MLA_ERR_ROPE, "rope: rotary_dims=%d, need an even count in [2, feat=%d]", rotary_dims, feat);
+  if (!(theta > 0.0) || !isfinite(theta)) return fail(MLA_ERR_ROPE, "rope: theta=%g, need finite > 0", theta);
   if (rotary_dims > 2 * mla::kRopeMaxPairs)
     return fail(MLA_ERR_UNSUPPORTED, "rope: rotary_dims %d > %d", rotary_dims, 2 * mla::kRopeMaxPairs);
   if (static_cast<int64_t>(batch) * tokens * inner == 0) return ok();
@@ -145,10 +145,10 @@ int mla_decode_query(int32_t dtype, const void* q_nope, int64_t qn_stride_b, int
   if (!valid_dtype(dtype)) return fail(MLA_ERR_ARG, "decode_query: unknown dtype %d", dtype);
   if (batch < 0 || heads < 1 || qk_nope < 1 || v_head < 1 || kv_lora_rank < 1)
     return fail(MLA_ERR_ARG, "decode_query: batch >= 0 and positive heads, qk_nope, v_head, kv_lora_rank required");
-  if (qk_rope <= 0 || (qk_rope & 1)) return fail(MLA_ERR_ROPE, "RoPE dimensions must be positive and even");
+  if (qk_rope <= 0 || (qk_rope & 1)) return fail(MLA_ERR_ROPE, "decode_query: qk_rope=%d, need an even count >= 2", qk_rope);
   if (qk_rope > 2 * mla::kRopeMaxPairs)
     return fail(MLA_ERR_UNSUPPORTED, "decode_query: qk_rope %d > %d", qk_rope, 2 * mla::kRopeMaxPairs);
-  if (!(theta > 0.0) || !isfinite(theta)) return fail(MLA_ERR_ROPE, "RoPE theta must be positive");
+  if (!(theta > 0.0) || !isfinite(theta)) return fail(MLA_ERR_ROPE, "decode_query: theta=%g, need finite > 0", theta);
   if (batch == 0) return ok();
   if (!q_nope || !q_rope_in || !q_rope_out || !w_kv_b || !q_lat || !positions)
     return fail(MLA_ERR_ARG, "decode_query: NULL pointer");
@@ -156,7 +156,7 @@ int mla_decode_query(int32_t dtype, const void* q_nope, int64_t qn_stride_b, int
     return fail(MLA_ERR_ARG, "decode_query: negative stride");
   if (batch > 65535 * 8) return fail(MLA_ERR_UNSUPPORTED, "decode_query: batch too large");
   for (int b = 0; b < batch; ++b) {
-    if (positions[b] < 0) return fail(MLA_ERR_ROPE, "RoPE position offset must be a non-negative integer");
+    if (positions[b] < 0) return fail(MLA_ERR_ROPE, "decode_query: positions[%d] < 0", b);
     if (positions[b] >= (int64_t{1} << 53)) return fail(MLA_ERR_UNSUPPORTED, "decode_query: position >= 2^53");
   }
   mla::RopeParams rp{};
@@ -226,7 +226,7 @@ int mla_decode_latent_attn(int32_t dtype, const void* q_lat, const void* q_rope,
       return fail(MLA_ERR_SHAPE, "decode: kv_len[%d] = %d outside [1, %d]", b, kv_len[b], width);
     int n = kv_len[b];
     if (sel_count) {
-      if (sel_count[b] == 0) return fail(MLA_ERR_SELECTION, "DSA selection cannot be empty (row %d)", b);
+      if (sel_count[b] == 0) return fail(MLA_ERR_SELECTION, "decode: sel_count[%d] = 0 (a selected row attends >= 1 index)", b);
       if (sel_count[b] < -1) return fail(MLA_ERR_SELECTION, "decode: sel_count[%d] = %d", b, sel_count[b]);
       if (sel_count[b] > 0) {
         n = sel_count[b];
@@ -404,9 +404,9 @@ int mla_append_compressed(int32_t dtype, const void* kv_a, int64_t kv_a_stride_b
   if (!valid_dtype(dtype)) return fail(MLA_ERR_ARG, "append: unknown dtype %d", dtype);
   if (batch < 0 || tokens < 0 || kv_lora_rank < 1 || rope_dim < 1 || slot < 0)
     return fail(MLA_ERR_ARG, "append: batch, tokens, slot >= 0 and positive kv_lora_rank, rope_dim required");
-  if (!isfinite(eps) || eps < 0.f) return fail(MLA_ERR_ARG, "RMSNorm epsilon must be non-negative");
-  if (rope_dim & 1) return fail(MLA_ERR_ROPE, "RoPE dimensions must be positive, even, and fit the feature axis");
-  if (!(theta > 0.0) || !isfinite(theta)) return fail(MLA_ERR_ROPE, "RoPE theta must be positive");
+  if (!isfinite(eps) || eps < 0.f) return fail(MLA_ERR_ARG, "append: eps=%g, need finite >= 0", static_cast<double>(eps));
+  if (rope_dim & 1) return fail(MLA_ERR_ROPE, "append: rope_dim=%d, need an even count", rope_dim);
+  if (!(theta > 0.0) || !isfinite(theta)) return fail(MLA_ERR_ROPE, "append: theta=%g, need finite > 0", theta);
   if (rope_dim > 2 * mla::kRopeMaxPairs || kv_lora_rank > 65536)
     return fail(MLA_ERR_UNSUPPORTED, "append: rope_dim <= %d and kv_lora_rank <= 65536 supported", 2 * mla::kRopeMaxPairs);
   if (batch == 0 || tokens == 0) return ok();
@@ -415,7 +415,7 @@ int mla_append_compressed(int32_t dtype, const void* kv_a, int64_t kv_a_stride_b
       rope_stride_t < 1)
     return fail(MLA_ERR_ARG, "append: bad stride");
   for (int b = 0; b < batch; ++b) {
-    if (positions[b] < 0) return fail(MLA_ERR_ROPE, "RoPE position offset must be a non-negative integer");
+    if (positions[b] < 0) return fail(MLA_ERR_ROPE, "append: positions[%d] < 0", b);
     if (static_cast<double>(positions[b]) + tokens > kMaxPosition)
       return fail(MLA_ERR_UNSUPPORTED, "append: position + tokens exceeds 2^53");
   }
@@ -583,9 +583,9 @@ int mla_prefill_reconstructed(int32_t dtype, int32_t batch, int32_t tokens, int3
   if (batch < 0 || tokens < 1 || keys < 1 || heads < 1 || q_lora_rank < 1 || kv_lora_rank < 1 || qk_nope < 1 ||
       qk_rope < 1 || v_head < 1)
     return fail(MLA_ERR_ARG, "prefill: batch >= 0 and positive geometry required");
-  if (keys < tokens) return fail(MLA_ERR_SHAPE, "MLA state cannot be shorter than the query block");
-  if (qk_rope & 1) return fail(MLA_ERR_ROPE, "RoPE dimensions must be positive, even, and fit the feature axis");
-  if (!(theta > 0.0) || !isfinite(theta)) return fail(MLA_ERR_ROPE, "RoPE theta must be positive");
+  if (keys < tokens) return fail(MLA_ERR_SHAPE, "prefill: keys=%d < tokens=%d (the keys include the query block)", keys, tokens);
+  if (qk_rope & 1) return fail(MLA_ERR_ROPE, "prefill: qk_rope=%d, need an even count", qk_rope);
+  if (!(theta > 0.0) || !isfinite(theta)) return fail(MLA_ERR_ROPE, "prefill: theta=%g, need finite > 0", theta);
   if (!isfinite(softmax_scale)) return fail(MLA_ERR_ARG, "prefill: softmax_scale must be finite");
   if (qk_nope + qk_rope > 256 || v_head > 256 || qk_rope > 2 * mla::kRopeMaxPairs)
     return fail(MLA_ERR_UNSUPPORTED, "prefill: qk_nope + qk_rope <= 256 and v_head <= 256 supported");
@@ -612,11 +612,11 @@ int mla_prefill_reconstructed(int32_t dtype, int32_t batch, int32_t tokens, int3
   p.theta = theta;
   p.scale = softmax_scale;
   p.ctx = ctx;
-  const size_t need = mla::prefill_workspace_bytes(p);
   if (!workspace) {
-    *workspace_bytes = need;
+    *workspace_bytes = mla::prefill_workspace_bytes_any_path(p);
     return ok();
   }
+  const size_t need = mla::prefill_workspace_bytes(p);
   if (*workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE, "prefill: workspace %zu bytes < %zu required", *workspace_bytes, need);
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(MLA_ERR_WORKSPACE, "prefill: workspace not 256-byte aligned");
@@ -624,7 +624,7 @@ int mla_prefill_reconstructed(int32_t dtype, int32_t batch, int32_t tokens, int3
   if (!q_c || !w_q_b || !latent || !rope || !w_kv_b || !q_offsets || !ctx)
     return fail(MLA_ERR_ARG, "prefill: NULL pointer");
   for (int b = 0; b < batch; ++b) {
-    if (q_offsets[b] < 0) return fail(MLA_ERR_ROPE, "RoPE position offset must be a non-negative integer");
+    if (q_offsets[b] < 0) return fail(MLA_ERR_ROPE, "prefill: q_offsets[%d] < 0", b);
     if (static_cast<double>(q_offsets[b]) + tokens > kMaxPosition)
       return fail(MLA_ERR_UNSUPPORTED, "prefill: offset + tokens exceeds 2^53");
     if (left_pad && (left_pad[b] < 0 || left_pad[b] > keys))

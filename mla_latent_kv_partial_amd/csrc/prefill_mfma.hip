@@ -28,6 +28,7 @@
 
 namespace mla {
 
+bool prefill_mfma_shape_ok(const PrefillParams& p);
 bool prefill_mfma_supported(const PrefillParams& p);
 size_t prefill_mfma_workspace_bytes(const PrefillParams& p);
 hipError_t launch_prefill_mfma(const PrefillParams& p, hipStream_t stream);
@@ -291,11 +292,17 @@ size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace
 
+// The shapes of the MFMA path (64: the K step of the GEMMs) ...
+bool prefill_mfma_shape_ok(const PrefillParams& p) {
+  return p.dtype == kBF16 && p.dn == kDn && p.dr == kDr && p.dv == kDv && p.ql % 64 == 0 && p.r % 64 == 0 &&
+         p.heads <= 65535;
+}
+
+// ... and 16-byte aligned buffers.
 bool prefill_mfma_supported(const PrefillParams& p) {
   auto al = [](const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15) == 0; };
-  // 64: the K step of the GEMMs
-  return p.dtype == kBF16 && p.dn == kDn && p.dr == kDr && p.dv == kDv && p.ql % 64 == 0 && p.r % 64 == 0 &&
-         al(p.q_c) && al(p.w_qb) && al(p.latent) && al(p.rope) && al(p.w_kvb) && al(p.ctx) && p.heads <= 65535;
+  return prefill_mfma_shape_ok(p) && al(p.q_c) && al(p.w_qb) && al(p.latent) && al(p.rope) && al(p.w_kvb) &&
+         al(p.ctx);
 }
 
 // q RoPE table of one launch: {cos, sin} (double) per query row and pair

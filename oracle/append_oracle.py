@@ -21,7 +21,7 @@ from .mla_oracle import OracleError, rope_partial_interleaved
 def rms_norm(x: np.ndarray, weight: np.ndarray, eps: float) -> np.ndarray:
     """RMSNorm over the last axis in float64."""
     if not np.isfinite(eps) or eps < 0:
-        raise OracleError("RMSNorm epsilon must be non-negative")
+        raise OracleError(f"eps={eps}: need a finite value >= 0")
     x = np.asarray(x, dtype=np.float64)
     w = np.asarray(weight, dtype=np.float64)
     if w.shape != (x.shape[-1],):

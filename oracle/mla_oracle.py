@@ -92,31 +92,26 @@ def rope_partial_interleaved(x: np.ndarray, position_offset, rotary_dims: int, t
     """
     x = np.asarray(x, dtype=np.float64)
     rank = x.ndim
+    # The page rejects these inputs before rotating (partialInterleavedRopeMlx);
+    # the conditions are restated here, the messages are this oracle's own.
+    width = x.shape[-1] if rank else 0
+    if (not isinstance(rotary_dims, (int, np.integer)) or isinstance(rotary_dims, bool)
+            or not 0 < rotary_dims <= width or rotary_dims % 2):
+        raise OracleError(f"rotary_dims={rotary_dims}: need an even count in (0, {width}]")
+    if not (math.isfinite(theta) and theta > 0):
+        raise OracleError(f"theta={theta}: need a finite value > 0")
     if rank < 2:
-        raise OracleError("partial interleaved RoPE requires rank >= 2")
+        raise OracleError(f"input of ndim {rank}: need a token axis and a feature axis")
     axis = token_axis + rank if token_axis < 0 else token_axis
-    if axis < 0 or axis >= rank:
-        raise OracleError(f"axis {token_axis} is invalid for rank {rank}")
-    if axis == rank - 1:
-        raise OracleError("RoPE token axis cannot be the feature axis")
+    if not 0 <= axis < rank - 1:
+        raise OracleError(f"token_axis={token_axis}: need an axis before the last (feature) axis of a {rank}-d input")
     per_row = not np.isscalar(position_offset) and not isinstance(position_offset, (int, np.integer))
-    if per_row:
-        offsets = list(position_offset)
-        if axis == 0:
-            raise OracleError("per-row RoPE offsets require a separate token axis")
-        if len(offsets) != x.shape[0]:
-            raise OracleError(f"RoPE row offsets {len(offsets)} != batch {x.shape[0]}")
-    else:
-        offsets = [position_offset]
-    for off in offsets:
-        if isinstance(off, bool) or not isinstance(off, (int, np.integer)) or int(off) < 0:
-            raise OracleError("RoPE position offset must be a non-negative integer")
-    d = x.shape[-1]
-    if (not isinstance(rotary_dims, (int, np.integer)) or rotary_dims <= 0 or rotary_dims % 2
-            or rotary_dims > d):
-        raise OracleError("RoPE dimensions must be positive, even, and fit the feature axis")
-    if not math.isfinite(theta) or theta <= 0:
-        raise OracleError("RoPE theta must be positive")
+    offsets = list(position_offset) if per_row else [position_offset]
+    if per_row and (axis == 0 or len(offsets) != x.shape[0]):
+        raise OracleError(f"{len(offsets)} per-row offsets with tokens on axis {axis}: need one offset for each "
+                          f"of the {x.shape[0]} entries of axis 0, and the tokens on another axis")
+    if any(isinstance(o, bool) or not isinstance(o, (int, np.integer)) or int(o) < 0 for o in offsets):
+        raise OracleError("position offsets: need integers >= 0")
 
     tokens = x.shape[axis]
     half = rotary_dims // 2
@@ -181,16 +176,16 @@ def attended_positions(kv_len: int, selection) -> np.ndarray:
     Duplicates are attended once per occurrence (a gather keeps them).
     """
     if kv_len < 1:
-        raise OracleError("a decode row must hold at least one cached token")
+        raise OracleError(f"kv_len={kv_len}: a decode row holds at least one token")
     if selection is None:
         return np.arange(kv_len, dtype=np.int64)
     sel = np.asarray(selection)
     if sel.ndim != 1 or sel.size == 0:
-        raise OracleError("DSA selection cannot be empty")
+        raise OracleError("selection list: need a 1-d list with at least one entry")
     if not np.issubdtype(sel.dtype, np.integer):
-        raise OracleError("DSA selection must hold integers")
+        raise OracleError("selection list: need integer entries")
     if sel.min() < 0 or sel.max() >= kv_len:
-        raise OracleError(f"DSA position outside cached prefix {kv_len}")
+        raise OracleError(f"selection list: entries must lie in [0, {kv_len})")
     return sel.astype(np.int64)
 
 
@@ -214,7 +209,7 @@ def _selections(batch: int, selections):
     if selections is None:
         return [None] * batch
     if len(selections) != batch:
-        raise OracleError(f"batched MLA selections {len(selections)} != batch {batch}")
+        raise OracleError(f"{len(selections)} selection entries for {batch} rows")
     return list(selections)
 
 
@@ -410,7 +405,7 @@ def prefill_reconstructed(c_q, w_qb, latent, rope, w_kvb, q_offsets, theta, left
     batch, tokens, _ = c_q.shape
     keys = latent.shape[1]
     if keys < tokens:
-        raise OracleError("MLA state cannot be shorter than the query block")
+        raise OracleError(f"keys={keys} < tokens={tokens}: the key block includes the query block")
     qk = qk_nope + qk_rope
     if w_qb.shape[0] != heads * qk:
         raise OracleError("q_b_proj rows != heads * (qk_nope + qk_rope)")

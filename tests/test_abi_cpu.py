@@ -142,15 +142,30 @@ def test_decode_query_empty_batch_is_ok():
     assert _query(b=0, pos=[0]) == OK
 
 
-def _prefill(ws=None, size=0, **kw):
+def _prefill(ws=None, size=0, ptr=FAKE, **kw):
     a = dict(dtype=1, b=1, t=16, k=16, h=4, ql=32, r=32, dn=16, dr=8, dv=16, offs=[0], theta=1e4, pad=None)
     a.update(kw)
     sz = ctypes.c_size_t(size)
     code = lib.mla_prefill_reconstructed(
-        a["dtype"], a["b"], a["t"], a["k"], a["h"], a["ql"], a["r"], a["dn"], a["dr"], a["dv"], FAKE, FAKE, FAKE,
-        FAKE, FAKE, i64_array(a["offs"]), a["theta"], None if a["pad"] is None else i32_array(a["pad"]), 0.1,
-        ws, ctypes.byref(sz), FAKE, None)
+        a["dtype"], a["b"], a["t"], a["k"], a["h"], a["ql"], a["r"], a["dn"], a["dr"], a["dv"], ptr, ptr, ptr,
+        ptr, ptr, i64_array(a["offs"]), a["theta"], None if a["pad"] is None else i32_array(a["pad"]), 0.1,
+        ws, ctypes.byref(sz), ptr, None)
     return code, sz.value
+
+
+def test_prefill_workspace_query_fits_either_path():
+    """The size query with NULL data pointers suffices whichever path the real
+    pointers select: 16-byte aligned bf16 buffers of the GLM head geometry take
+    the MFMA path, misaligned ones the generic path (fp32 intermediates).  The
+    calls stop at the negative offset, after the workspace check."""
+    glm = dict(t=64, k=64, h=2, ql=64, r=64, dn=128, dr=64, dv=128)
+    code, need = _prefill(ptr=None, **glm)
+    assert code == OK and need > 0
+    ws = ctypes.c_void_p(0x100000)
+    for ptr in (ctypes.c_void_p(0x2000), ctypes.c_void_p(0x2008)):     # aligned, then misaligned
+        assert _prefill(ws=ws, size=need, ptr=ptr, offs=[-1], **glm)[0] == ROPE
+    # the generic path alone needs more than the MFMA path for these shapes
+    assert _prefill(ws=ws, size=need // 2, ptr=ctypes.c_void_p(0x2008), offs=[-1], **glm)[0] == WS
 
 
 def test_prefill_workspace_query_and_rejections():

@@ -300,11 +300,12 @@ def test_absorb_unit_query_selects_weight_row_exactly():
     assert torch.equal(q_lat[0], wt[:, 5]) and torch.equal(q_lat[1], wt[:, 127])
 
 
-@pytest.mark.parametrize("heads", [16, 32, 128])
+@pytest.mark.parametrize("heads", [16, 32, 48, 128])
 @pytest.mark.parametrize("packed", [True, False])
 def test_head_counts_match_oracle(heads, packed):
     """The MFMA kernel's head-group variants (16, 32, 64 x 2 heads per launch)
-    on ragged rows, packed and separate latent / rope caches."""
+    and a head count it has no grouping for (48: the generic kernel) on ragged
+    rows, packed and separate latent / rope caches."""
     cfg = cf.with_shape(cf.RAGGED_BF16, heads=heads)
     inp = cf.decode_inputs(cfg, layer=heads, lengths=(300, 1, 77))
     say(f"heads={heads} packed={packed}")
@@ -314,7 +315,7 @@ def test_head_counts_match_oracle(heads, packed):
     assert_close(host_values(got["lse"]), ref["lse"], cfg.dtype, "lse")
 
 
-@pytest.mark.parametrize("heads", [16, 32, 128])
+@pytest.mark.parametrize("heads", [16, 32, 48, 128])
 def test_head_counts_gathered_match_oracle(heads):
     cfg = cf.with_shape(cf.DSA_BF16, heads=heads, tokens=4096, selected=300)
     inp = cf.decode_inputs(cfg, layer=heads)

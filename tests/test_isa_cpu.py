@@ -41,11 +41,39 @@ def test_m0_only_set_by_the_copy_sequences(name, tmp_path):
             assert body[i + 1].startswith("global_load_lds_dword"), body[i + 1]
 
 
+def _spills(text):
+    names = re.findall(r"\.name:\s+(\S+)", text)
+    spills = [int(v) for v in re.findall(r"\.vgpr_spill_count:\s+(\d+)", text)]
+    kernels = [n for n in names if "kernel" in n]
+    assert len(kernels) == len(spills), (kernels, spills)
+    return dict(zip(kernels, spills))
+
+
 @pytest.mark.parametrize("name", SRC)
 def test_no_spills(name, tmp_path):
-    text = _asm(name, tmp_path)
-    spills = [int(v) for v in re.findall(r"\.vgpr_spill_count:\s+(\d+)", text)]
-    names = re.findall(r"\.name:\s+(\S+)", text)
-    hot = [s for n, s in zip(names, spills)
-           if any(k in n for k in ("ILi4E", "absorb", "gemm", "flash", "combine", "stream_probe"))]
-    assert hot and max(hot) == 0, list(zip(names, spills))
+    """Every hot kernel fits its register budget: the 64-head attention
+    variants (NW = 4), the absorb, GEMM, flash-attention, merge and probe kernels."""
+    sp = _spills(_asm(name, tmp_path))
+    hot = {n: s for n, s in sp.items()
+           if any(k in n for k in ("ILi4E", "absorb", "gemm", "flash", "combine", "stream_probe"))}
+    assert hot and max(hot.values()) == 0, hot
+
+
+# VGPR spills of the attention variants for launches of 16 and 32 heads
+# (NW = 1, 2: a context wave owns 512 or 256 latent dims); template arguments
+# <NW, GATHER, PACKED>.  Correct but slower; a change may lower these counts,
+# never raise them.
+SMALL_HEAD_SPILLS = {(1, 1, 1): 52, (1, 1, 0): 104, (1, 0, 1): 0, (1, 0, 0): 92,
+                     (2, 1, 1): 0, (2, 1, 0): 24, (2, 0, 1): 0, (2, 0, 0): 0}
+
+
+def test_small_head_attention_spills_do_not_grow(tmp_path):
+    sp = _spills(_asm("decode_mfma.hip", tmp_path))
+    seen = {}
+    for n, s in sp.items():
+        m = re.search(r"decode_mfma_kernelILi(\d)ELb(\d)ELb(\d)E", n)
+        if m and m.group(1) in ("1", "2"):
+            seen[tuple(int(v) for v in m.groups())] = s
+    assert set(seen) == set(SMALL_HEAD_SPILLS), seen
+    grown = {k: (v, SMALL_HEAD_SPILLS[k]) for k, v in seen.items() if v > SMALL_HEAD_SPILLS[k]}
+    assert not grown, grown
