@@ -344,6 +344,24 @@ int mla_dsa_topk_select(const float* scores, int64_t score_stride, int32_t batch
                         size_t* workspace_bytes, hipStream_t stream);
 
 /*
+ * mla_dsa_topk_select without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The positions and sel_count are those of
+ * mla_dsa_topk_select with a workspace (bit-identical).  The two-stage rows
+ * (see workspace above) use a fixed scratch array in the library's device
+ * memory instead: 32 such rows at most (4 MiB; each device holds its own copy
+ * until the process ends), and every other row runs on one workgroup.  The
+ * call allocates and frees nothing.  All calls on one device share the
+ * scratch: calls that overlap on one device (several streams or threads)
+ * race and must be serialised by the caller.
+ * Errors: as mla_dsa_topk_select, and MLA_ERR_WORKSPACE when more than 32
+ * rows take the two-stage form (split the batch); MLA_ERR_DEVICE if the
+ * scratch address cannot be obtained on the current device.
+ */
+int mla_dsa_topk_select_noalloc(const float* scores, int64_t score_stride, int32_t batch, const int32_t* row_len,
+                                int32_t top_k, int32_t* sel_idx, int32_t* sel_count, hipStream_t stream);
+
+/*
  * Reconstructed causal prefill.  [P1] Glm52Mla.project (q_b_proj of the
  * normalised q-LoRA state, reshape [B,T,H,dn+dr], split no-PE / rope, RoPE of
  * the rope part at q_offsets[b] + t) and Glm52Mla.attendReconstructed

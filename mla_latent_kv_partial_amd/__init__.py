@@ -21,7 +21,7 @@ __all__ = [
     "MlaError", "LIB_PATH", "EXPORTS", "mla_rope_partial_interleaved", "mla_absorb_q", "mla_decode_latent_attn",
     "mla_decode_combine", "mla_absorb_v", "mla_prefill_reconstructed", "mla_version", "split_count",
     "plan_chunk_len", "prefill_workspace_bytes", "mla_dsa_topk_select", "mla_append_compressed",
-    "mla_o_proj", "mla_decode_query",
+    "mla_o_proj", "mla_decode_query", "mla_dsa_topk_select_noalloc",
 ]
 
 
@@ -360,6 +360,30 @@ def mla_dsa_topk_select(scores: torch.Tensor, row_len, top_k: int, sel_idx: torc
     check(lib.mla_dsa_topk_select(_ptr(scores), scores.stride(0), b, i32_array(lens), int(top_k), _ptr(sel_idx),
                                   counts, _ptr(workspace) if two_stage else None,
                                   ctypes.byref(size) if two_stage else None, _stream(scores)), "mla_dsa_topk_select")
+    return sel_idx[:total], [int(c) for c in counts]
+
+
+def mla_dsa_topk_select_noalloc(scores: torch.Tensor, row_len, top_k: int, sel_idx: torch.Tensor):
+    """mla_dsa_topk_select without a workspace: the library's fixed device
+    scratch serves the long rows (at most 32 of them per call).  sel_idx (int32,
+    room for top_k per selected row) is the caller's; nothing is allocated.
+    Returns (sel_idx[:selected], sel_count host list)."""
+    if scores.dtype != torch.float32:
+        raise TypeError("scores must be float32")
+    if scores.dim() == 1:
+        scores = scores.view(1, -1)
+    if scores.dim() != 2 or scores.stride(1) != 1:
+        raise ValueError("scores must be [B, W] with a unit feature stride")
+    lens = _host_list(row_len)
+    b = scores.shape[0]
+    if len(lens) != b:
+        raise ValueError("row_len needs one entry per score row")
+    total = sum(int(top_k) for n in lens if n > top_k)
+    if sel_idx.dtype != torch.int32 or sel_idx.numel() < total:
+        raise ValueError("sel_idx must be int32 with room for every selected index")
+    counts = i32_array([0] * b)
+    check(lib.mla_dsa_topk_select_noalloc(_ptr(scores), scores.stride(0), b, i32_array(lens), int(top_k),
+                                          _ptr(sel_idx), counts, _stream(scores)), "mla_dsa_topk_select_noalloc")
     return sel_idx[:total], [int(c) for c in counts]
 
 

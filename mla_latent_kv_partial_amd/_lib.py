@@ -23,7 +23,7 @@ EXPORTS = (
     "mla_last_error", "mla_version", "mla_rope_partial_interleaved", "mla_absorb_q", "mla_decode_latent_attn",
     "mla_decode_combine", "mla_absorb_v", "mla_prefill_reconstructed", "mla_dsa_topk_select",
     "mla_append_compressed", "mla_o_proj_workspace_bytes", "mla_o_proj", "mla_decode_query",
-    "mla_decode_combine_v", "mla_decode_stream_probe",
+    "mla_decode_combine_v", "mla_decode_stream_probe", "mla_dsa_topk_select_noalloc",
 )
 
 _p = ctypes.c_void_p
@@ -53,6 +53,7 @@ _SIGNATURES = {
     "mla_decode_combine_v": (ctypes.c_int, [
         _i32, _p, _p, _i32, _i32, _i32, _i32, _pi32, _p, _i32, _i32, _p, _p, _p, _p]),
     "mla_dsa_topk_select": (ctypes.c_int, [_p, _i64, _i32, _pi32, _i32, _p, _pi32, _p, _psz, _p]),
+    "mla_dsa_topk_select_noalloc": (ctypes.c_int, [_p, _i64, _i32, _pi32, _i32, _p, _pi32, _p]),
     "mla_o_proj_workspace_bytes": (ctypes.c_int, [_i32, _i64, _i32, _i32, _psz]),
     "mla_o_proj": (ctypes.c_int, [_i32, _p, _i64, _i32, _p, _i32, _p, _p, ctypes.c_size_t, _p]),
     "mla_append_compressed": (ctypes.c_int, [

@@ -38,6 +38,8 @@
 //      the one-workgroup form run over them (the score of a candidate is its
 //      key mapped back, bit for bit).
 // Both forms give the same integers.
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -488,6 +490,33 @@ hipError_t launch_dsa_topk(const TopkParams& p, hipStream_t stream) {
   if (p.rows == 0) return hipSuccess;
   hipLaunchKernelGGL(dsa_topk_kernel, dim3(p.rows), dim3(kTT), 0, stream, p);
   return hipGetLastError();
+}
+
+// The candidate areas of mla_dsa_topk_select_noalloc: a fixed array in device
+// memory (each device holds its own copy for the life of the process), so that
+// entry allocates nothing.  Every call on a device shares it: calls that
+// overlap on one device race.  Host code never passes the array's name to a
+// kernel (in host code it is a host-side stand-in): the address on the current
+// device comes from hipGetSymbolAddress, looked up once per device.
+static __device__ __align__(256) char scratch[static_cast<size_t>(kTopkNoAllocRows) * kTopkRowWsBytes];
+
+hipError_t dsa_topk_scratch(char** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static char* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<char*>(p);
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace mla

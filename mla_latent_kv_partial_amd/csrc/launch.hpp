@@ -142,6 +142,11 @@ constexpr size_t kTopkRowWsBytes = static_cast<size_t>(kTopkMaxCand) * 8 + 256;
 bool dsa_topk_two_stage(int64_t n, int32_t top_k);
 hipError_t launch_dsa_topk(const TopkParams& p, hipStream_t stream);
 hipError_t launch_dsa_topk_two_stage(const TopkParams& p, hipStream_t stream);
+// Fixed device scratch of mla_dsa_topk_select_noalloc: kTopkNoAllocRows
+// two-stage rows.  *ptr = its address on the current device (looked up once
+// per device).
+constexpr int kTopkNoAllocRows = 32;
+hipError_t dsa_topk_scratch(char** ptr);
 
 // ------------------------------------------------------------------ GEMM (MFMA, bf16 operands)
 constexpr int kGemmRowsPerLaunch = 128;

@@ -445,51 +445,47 @@ int mla_append_compressed(int32_t dtype, const void* kv_a, int64_t kv_a_stride_b
   return ok();
 }
 
-int mla_dsa_topk_select(const float* scores, int64_t score_stride, int32_t batch, const int32_t* row_len,
-                        int32_t top_k, int32_t* sel_idx, int32_t* sel_count, void* workspace,
-                        size_t* workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Host checks of a top-k call; counts the selected indices and the rows that
+// take the two-stage form.
+int topk_check(const float* scores, int64_t score_stride, int32_t batch, const int32_t* row_len, int32_t top_k,
+               const int32_t* sel_count, int64_t* total, int64_t* two_stage) {
   if (batch < 0) return fail(MLA_ERR_ARG, "dsa_topk: batch must be >= 0");
   if (top_k < 1) return fail(MLA_ERR_ARG, "dsa_topk: top_k must be >= 1");
-  if (batch == 0) {
-    if (workspace_bytes && !workspace) *workspace_bytes = 0;
-    return ok();
-  }
+  *total = *two_stage = 0;
+  if (batch == 0) return ok();
   if (!scores || !row_len || !sel_count) return fail(MLA_ERR_ARG, "dsa_topk: NULL pointer");
-  int64_t total = 0, two_stage = 0;
   for (int b = 0; b < batch; ++b) {
     if (row_len[b] < 1 || row_len[b] > (1 << 30))
       return fail(MLA_ERR_SHAPE, "dsa_topk: row_len[%d] = %d outside [1, 2^30]", b, row_len[b]);
     if (batch > 1 && row_len[b] > score_stride)
       return fail(MLA_ERR_SHAPE, "dsa_topk: row_len[%d] = %d exceeds the score row stride %lld", b, row_len[b],
                   static_cast<long long>(score_stride));
-    if (row_len[b] > top_k) total += top_k;
-    if (mla::dsa_topk_two_stage(row_len[b], top_k)) ++two_stage;
+    if (row_len[b] > top_k) *total += top_k;
+    if (mla::dsa_topk_two_stage(row_len[b], top_k)) ++*two_stage;
   }
-  if (total > 0x7fffffffLL) return fail(MLA_ERR_UNSUPPORTED, "dsa_topk: more than 2^31-1 selected indices");
-  // without a workspace every row runs on one workgroup
-  const bool use_ws = workspace_bytes != nullptr;
-  const size_t need = use_ws ? static_cast<size_t>(two_stage) * mla::kTopkRowWsBytes : 0;
-  if (use_ws && !workspace) {
-    *workspace_bytes = need;
-    return ok();
-  }
-  if (use_ws && *workspace_bytes < need)
-    return fail(MLA_ERR_WORKSPACE, "dsa_topk: workspace %zu bytes < %zu required", *workspace_bytes, need);
-  if (use_ws && reinterpret_cast<uintptr_t>(workspace) % 256)
-    return fail(MLA_ERR_WORKSPACE, "dsa_topk: workspace not 256-byte aligned");
-  if (total > 0 && !sel_idx) return fail(MLA_ERR_ARG, "dsa_topk: sel_idx is NULL but rows are selected");
+  if (*total > 0x7fffffffLL) return fail(MLA_ERR_UNSUPPORTED, "dsa_topk: more than 2^31-1 selected indices");
+  return ok();
+}
+
+// Writes sel_count and launches the selection; ws == NULL runs every row on
+// one workgroup, otherwise the two-stage rows use ws (kTopkRowWsBytes each).
+int topk_launch(const float* scores, int64_t score_stride, int32_t batch, const int32_t* row_len, int32_t top_k,
+                int32_t* sel_idx, int32_t* sel_count, char* ws, hipStream_t stream) {
   for (int b = 0; b < batch; ++b) sel_count[b] = row_len[b] > top_k ? top_k : -1;
   mla::TopkParams one{}, two{};
   one.scores = two.scores = scores;
   one.stride = two.stride = score_stride;
   one.sel_idx = two.sel_idx = sel_idx;
   one.top_k = two.top_k = top_k;
-  char* ws = static_cast<char*>(workspace);
   two.ws = ws;
   int64_t off = 0;
   for (int b = 0; b < batch; ++b) {
     if (row_len[b] <= top_k) continue;
-    mla::TopkParams& p = use_ws && mla::dsa_topk_two_stage(row_len[b], top_k) ? two : one;
+    mla::TopkParams& p = ws && mla::dsa_topk_two_stage(row_len[b], top_k) ? two : one;
     p.row[p.rows] = b;
     p.len[p.rows] = row_len[b];
     p.out_off[p.rows] = static_cast<int32_t>(off);
@@ -506,6 +502,57 @@ int mla_dsa_topk_select(const float* scores, int64_t score_stride, int32_t batch
   e = mla::launch_dsa_topk_two_stage(two, stream);
   if (e != hipSuccess) return device(e, "dsa_topk launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_dsa_topk_select(const float* scores, int64_t score_stride, int32_t batch, const int32_t* row_len,
+                        int32_t top_k, int32_t* sel_idx, int32_t* sel_count, void* workspace,
+                        size_t* workspace_bytes, hipStream_t stream) {
+  int64_t total = 0, two_stage = 0;
+  int rc = topk_check(scores, score_stride, batch, row_len, top_k, sel_count, &total, &two_stage);
+  if (rc != MLA_OK) return rc;
+  if (batch == 0) {
+    if (workspace_bytes && !workspace) *workspace_bytes = 0;
+    return ok();
+  }
+  // without a workspace every row runs on one workgroup
+  const bool use_ws = workspace_bytes != nullptr;
+  const size_t need = use_ws ? static_cast<size_t>(two_stage) * mla::kTopkRowWsBytes : 0;
+  if (use_ws && !workspace) {
+    *workspace_bytes = need;
+    return ok();
+  }
+  if (use_ws && *workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "dsa_topk: workspace %zu bytes < %zu required", *workspace_bytes, need);
+  if (use_ws && reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(MLA_ERR_WORKSPACE, "dsa_topk: workspace not 256-byte aligned");
+  if (total > 0 && !sel_idx) return fail(MLA_ERR_ARG, "dsa_topk: sel_idx is NULL but rows are selected");
+  return topk_launch(scores, score_stride, batch, row_len, top_k, sel_idx, sel_count,
+                     use_ws ? static_cast<char*>(workspace) : nullptr, stream);
+}
+
+int mla_dsa_topk_select_noalloc(const float* scores, int64_t score_stride, int32_t batch, const int32_t* row_len,
+                                int32_t top_k, int32_t* sel_idx, int32_t* sel_count, hipStream_t stream) {
+  int64_t total = 0, two_stage = 0;
+  int rc = topk_check(scores, score_stride, batch, row_len, top_k, sel_count, &total, &two_stage);
+  if (rc != MLA_OK) return rc;
+  if (two_stage > mla::kTopkNoAllocRows)
+    return fail(MLA_ERR_WORKSPACE,
+                "dsa_topk_noalloc: %lld rows take the two-stage form; the fixed scratch holds %d (split the batch)",
+                static_cast<long long>(two_stage), mla::kTopkNoAllocRows);
+  if (batch == 0) return ok();
+  if (total > 0 && !sel_idx) return fail(MLA_ERR_ARG, "dsa_topk: sel_idx is NULL but rows are selected");
+  char* ws = nullptr;
+  if (two_stage > 0) {
+    hipError_t e = mla::dsa_topk_scratch(&ws);
+    if (e != hipSuccess) return device(e, "dsa_topk_noalloc scratch");
+  }
+  // rows that need no scratch run on one workgroup as in mla_dsa_topk_select;
+  // with ws == NULL (no two-stage row) that is every row
+  return topk_launch(scores, score_stride, batch, row_len, top_k, sel_idx, sel_count, ws, stream);
 }
 
 int mla_decode_combine(const float* part_o, const float* part_lse, int32_t batch, int32_t heads, int32_t kv_lora_rank,
