@@ -106,7 +106,9 @@ class DecodeLayer:
         self.n_splits = [mla.split_count(n, self.chunk) for n in self.n_att]
         self.s_max = max(self.n_splits)
         b = len(self.kv_len)
-        self.part_o = torch.empty((b, self.cfg.heads, self.s_max, self.cfg.kv_lora_rank), dtype=torch.float32,
+        # bf16 split partials for the bf16 cache (one rounding of each
+        # normalised split context; half the partial bytes of fp32)
+        self.part_o = torch.empty((b, self.cfg.heads, self.s_max, self.cfg.kv_lora_rank), dtype=self.cache.dtype,
                                   device=dev)
         self.part_lse = torch.empty((b, self.cfg.heads, self.s_max), dtype=torch.float32, device=dev)
 
@@ -166,7 +168,7 @@ def share_partials(layers, torch, dev):
     s_max = max(ly.s_max for ly in layers)
     b = max(len(ly.kv_len) for ly in layers)
     c = layers[0].cfg
-    po = torch.empty((b, c.heads, s_max, c.kv_lora_rank), dtype=torch.float32, device=dev)
+    po = torch.empty((b, c.heads, s_max, c.kv_lora_rank), dtype=layers[0].part_o.dtype, device=dev)
     pl = torch.empty((b, c.heads, s_max), dtype=torch.float32, device=dev)
     for ly in layers:
         ly.part_o, ly.part_lse, ly.s_max = po, pl, s_max
@@ -439,7 +441,7 @@ def main():
         r_q_rope = torch.cat([ly.q_rope for ly in layers], dim=0)
         r_chunk = mla.plan_chunk_len(r_lens, slots)
         r_ns = [mla.split_count(n, r_chunk) for n in r_lens]
-        r_po = torch.empty((rows_all, cfg.heads, max(r_ns), cfg.kv_lora_rank), dtype=torch.float32, device=dev)
+        r_po = torch.empty((rows_all, cfg.heads, max(r_ns), cfg.kv_lora_rank), dtype=torch.bfloat16, device=dev)
         r_pl = torch.empty((rows_all, cfg.heads, max(r_ns)), dtype=torch.float32, device=dev)
         ms_r = time_graph(torch, lambda: mla.mla_decode_latent_attn(
             r_q_lat, r_q_rope, rs[..., :cfg.kv_lora_rank], rs[..., cfg.kv_lora_rank:], r_lens, cfg.softmax_scale,
@@ -467,7 +469,7 @@ def main():
         lens = [dcfg.tokens] * n_dense
         chunk = mla.plan_chunk_len(lens, slots)
         ns = [mla.split_count(n, chunk) for n in lens]
-        po = torch.empty((n_dense, dcfg.heads, max(ns), dcfg.kv_lora_rank), dtype=torch.float32, device=dev)
+        po = torch.empty((n_dense, dcfg.heads, max(ns), dcfg.kv_lora_rank), dtype=torch.bfloat16, device=dev)
         pl = torch.empty((n_dense, dcfg.heads, max(ns)), dtype=torch.float32, device=dev)
         ms_s = time_graph(torch, lambda: mla.mla_decode_latent_attn(
             q_lat, q_rope, stacked[..., :512], stacked[..., 512:], lens, dcfg.softmax_scale, chunk, part_o=po,
@@ -500,7 +502,7 @@ def main():
         st_cnt = [c for ly in sl for c in ly.sel_count]
         st_chunk = mla.plan_chunk_len(st_cnt, slots)
         st_ns = [mla.split_count(c, st_chunk) for c in st_cnt]
-        st_po = torch.empty((len(st_len), scfg.heads, max(st_ns), scfg.kv_lora_rank), dtype=torch.float32,
+        st_po = torch.empty((len(st_len), scfg.heads, max(st_ns), scfg.kv_lora_rank), dtype=torch.bfloat16,
                             device=dev)
         st_pl = torch.empty((len(st_len), scfg.heads, max(st_ns)), dtype=torch.float32, device=dev)
         ms_dst = time_graph(torch, lambda: mla.mla_decode_latent_attn(

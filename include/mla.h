@@ -179,8 +179,11 @@ int mla_decode_query(int32_t dtype, const void* q_nope, int64_t qn_stride_b, int
  * rope_dim] of `dtype`, strides (qr_stride_b, qr_stride_h, 1), already rotated.
  * kv_len [host] int32[batch], each in [1, width] (MLA_ERR_SHAPE otherwise).
  * sel_count [host] int32[batch] or NULL.  sel_idx device int32 (may be NULL
- * only if no row is selected).  part_o [batch, heads, s_max, r] and
- * part_lse [batch, heads, s_max] fp32; s_max >= max_b n_b (MLA_ERR_SHAPE).
+ * only if no row is selected).  part_o [batch, heads, s_max, r] of
+ * part_dtype (MLA_DTYPE_F32, or MLA_DTYPE_BF16: each normalised split context
+ * rounded once to bf16, round to nearest even; half the bytes that the
+ * attention writes and the merge reads back) and part_lse [batch, heads,
+ * s_max] fp32; s_max >= max_b n_b (MLA_ERR_SHAPE).
  * Limits (MLA_ERR_UNSUPPORTED): kv_lora_rank <= 1024, rope_dim <= 256.
  */
 int mla_decode_latent_attn(int32_t dtype, const void* q_lat,
@@ -191,7 +194,7 @@ int mla_decode_latent_attn(int32_t dtype, const void* q_lat,
                            int32_t width, const int32_t* kv_len,
                            const int32_t* sel_idx, const int32_t* sel_count,
                            float softmax_scale, int32_t chunk_len,
-                           float* part_o, float* part_lse, int32_t s_max,
+                           int32_t part_dtype, void* part_o, float* part_lse, int32_t s_max,
                            int32_t* dev_err, hipStream_t stream);
 
 /*
@@ -217,9 +220,10 @@ int mla_decode_stream_probe(int32_t dtype, const void* latent, int64_t latent_st
  * Splits with lse = -inf contribute nothing; if every split of (b,h) is
  * empty, o_lat = 0 and lse = -inf.
  * n_splits [host] int32[batch], each in [1, s_max].  lse may be NULL.
- * Layouts as in mla_decode_latent_attn; o_lat [batch, heads, r], lse [batch, heads].
+ * part_o of part_dtype (fp32 or bf16) and the other layouts as in
+ * mla_decode_latent_attn; o_lat fp32 [batch, heads, r], lse [batch, heads].
  */
-int mla_decode_combine(const float* part_o, const float* part_lse,
+int mla_decode_combine(int32_t part_dtype, const void* part_o, const float* part_lse,
                        int32_t batch, int32_t heads, int32_t kv_lora_rank, int32_t s_max,
                        const int32_t* n_splits, float* o_lat, float* lse, hipStream_t stream);
 
@@ -231,12 +235,12 @@ int mla_decode_combine(const float* part_o, const float* part_lse,
  *   ctx[b, h*dv + v] = sum_c o_lat[b,h,c] * w_kv_b[h*(dn+dv) + dn + v, c]
  * with o_lat as defined for mla_decode_combine.  `dtype` is the dtype of
  * w_kv_b (layout as in mla_absorb_q); the projection accumulates in fp32 over
- * the fp32 o_lat.  part_o, part_lse, n_splits as in mla_decode_combine;
+ * the fp32 o_lat.  part_dtype, part_o, part_lse, n_splits as in mla_decode_combine;
  * ctx fp32 [batch, heads*v_head] contiguous.  o_lat [batch, heads, r] and
  * lse [batch, heads] may be NULL; when given they receive the merge.
  * Limits (MLA_ERR_UNSUPPORTED): kv_lora_rank <= 1024.
  */
-int mla_decode_combine_v(int32_t dtype, const float* part_o, const float* part_lse,
+int mla_decode_combine_v(int32_t dtype, int32_t part_dtype, const void* part_o, const float* part_lse,
                          int32_t batch, int32_t heads, int32_t kv_lora_rank, int32_t s_max,
                          const int32_t* n_splits, const void* w_kv_b, int32_t qk_nope, int32_t v_head,
                          float* ctx, float* o_lat, float* lse, hipStream_t stream);

@@ -185,11 +185,12 @@ def mla_decode_latent_attn(q_lat: torch.Tensor, q_rope: torch.Tensor, latent: to
                            kv_len, softmax_scale: float, chunk_len: int, sel_idx: torch.Tensor | None = None,
                            sel_count=None, part_o: torch.Tensor | None = None,
                            part_lse: torch.Tensor | None = None, s_max: int | None = None,
-                           dev_err: torch.Tensor | None = None):
+                           dev_err: torch.Tensor | None = None, part_dtype: torch.dtype = torch.float32):
     """Split-T latent attention partials.  Returns (part_o, part_lse, n_splits list).
 
     latent [B,W,r] and rope [B,W,dr] (strided views of a cache; feature stride 1);
     kv_len and sel_count are host sequences; sel_idx an int32 device tensor.
+    part_o is float32 or bfloat16 (its dtype when given, else part_dtype).
     """
     b, h, r = q_lat.shape
     w = latent.shape[1]
@@ -202,7 +203,7 @@ def mla_decode_latent_attn(q_lat: torch.Tensor, q_rope: torch.Tensor, latent: to
         s_max = max(n_splits) if n_splits else 1
     dev = q_lat.device
     if part_o is None:
-        part_o = torch.empty((b, h, s_max, r), dtype=torch.float32, device=dev)
+        part_o = torch.empty((b, h, s_max, r), dtype=part_dtype, device=dev)
     if part_lse is None:
         part_lse = torch.empty((b, h, s_max), dtype=torch.float32, device=dev)
     if sel_idx is not None and sel_idx.dtype != torch.int32:
@@ -215,21 +216,22 @@ def mla_decode_latent_attn(q_lat: torch.Tensor, q_rope: torch.Tensor, latent: to
         _dtype_code(latent), _ptr(q_lat), _ptr(q_rope), q_rope.stride(0), q_rope.stride(1),
         _ptr(latent), latent.stride(0), latent.stride(1), _ptr(rope), rope.stride(0), rope.stride(1),
         b, h, r, dr, w, i32_array(lens), _ptr(sel_idx), None if counts is None else i32_array(counts),
-        float(softmax_scale), int(chunk_len), _ptr(part_o), _ptr(part_lse), int(s_max), _ptr(dev_err),
-        _stream(q_lat)), "mla_decode_latent_attn")
+        float(softmax_scale), int(chunk_len), _dtype_code(part_o), _ptr(part_o), _ptr(part_lse), int(s_max),
+        _ptr(dev_err), _stream(q_lat)), "mla_decode_latent_attn")
     return part_o, part_lse, n_splits
 
 
 def mla_decode_combine(part_o: torch.Tensor, part_lse: torch.Tensor, n_splits, o_lat: torch.Tensor | None = None,
                        lse: torch.Tensor | None = None, want_lse: bool = True):
-    """Merge partials into o_lat [B,H,r] (and lse [B,H])."""
+    """Merge partials (float32 or bfloat16) into o_lat [B,H,r] (and lse [B,H])."""
     b, h, s_max, r = part_o.shape
     if o_lat is None:
         o_lat = torch.empty((b, h, r), dtype=torch.float32, device=part_o.device)
     if lse is None and want_lse:
         lse = torch.empty((b, h), dtype=torch.float32, device=part_o.device)
-    check(lib.mla_decode_combine(_ptr(part_o), _ptr(part_lse), b, h, r, s_max, i32_array(_host_list(n_splits)),
-                                 _ptr(o_lat), _ptr(lse), _stream(part_o)), "mla_decode_combine")
+    check(lib.mla_decode_combine(_dtype_code(part_o), _ptr(part_o), _ptr(part_lse), b, h, r, s_max,
+                                 i32_array(_host_list(n_splits)), _ptr(o_lat), _ptr(lse), _stream(part_o)),
+          "mla_decode_combine")
     return o_lat, lse
 
 
@@ -267,7 +269,8 @@ def mla_decode_combine_v(part_o: torch.Tensor, part_lse: torch.Tensor, n_splits,
         ctx = torch.empty((b, h * v_head), dtype=torch.float32, device=part_o.device)
     if not w_kv_b.is_contiguous():
         raise ValueError("w_kv_b must be contiguous")
-    check(lib.mla_decode_combine_v(_dtype_code(w_kv_b), _ptr(part_o), _ptr(part_lse), b, h, r, s_max,
+    check(lib.mla_decode_combine_v(_dtype_code(w_kv_b), _dtype_code(part_o), _ptr(part_o), _ptr(part_lse), b, h, r,
+                                   s_max,
                                    i32_array(_host_list(n_splits)), _ptr(w_kv_b), int(qk_nope), int(v_head), _ptr(ctx),
                                    _ptr(o_lat), _ptr(lse), _stream(part_o)), "mla_decode_combine_v")
     return ctx

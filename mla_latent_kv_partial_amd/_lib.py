@@ -45,13 +45,13 @@ _SIGNATURES = {
         _i32, _p, _i64, _i64, _p, _p, _i64, _i64, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _pi64, _f64, _p]),
     "mla_decode_latent_attn": (ctypes.c_int, [
         _i32, _p, _p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
-        _pi32, _p, _pi32, _f32, _i32, _p, _p, _i32, _p, _p]),
-    "mla_decode_combine": (ctypes.c_int, [_p, _p, _i32, _i32, _i32, _i32, _pi32, _p, _p, _p]),
+        _pi32, _p, _pi32, _f32, _i32, _i32, _p, _p, _i32, _p, _p]),
+    "mla_decode_combine": (ctypes.c_int, [_i32, _p, _p, _i32, _i32, _i32, _i32, _pi32, _p, _p, _p]),
     "mla_absorb_v": (ctypes.c_int, [_i32, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _p]),
     "mla_decode_stream_probe": (ctypes.c_int, [
         _i32, _p, _i64, _i64, _p, _i64, _i64, _i32, _i32, _i32, _i32, _pi32, _i32, _p]),
     "mla_decode_combine_v": (ctypes.c_int, [
-        _i32, _p, _p, _i32, _i32, _i32, _i32, _pi32, _p, _i32, _i32, _p, _p, _p, _p]),
+        _i32, _i32, _p, _p, _i32, _i32, _i32, _i32, _pi32, _p, _i32, _i32, _p, _p, _p, _p]),
     "mla_dsa_topk_select": (ctypes.c_int, [_p, _i64, _i32, _pi32, _i32, _p, _pi32, _p, _psz, _p]),
     "mla_dsa_topk_select_noalloc": (ctypes.c_int, [_p, _i64, _i32, _pi32, _i32, _p, _pi32, _p]),
     "mla_o_proj_workspace_bytes": (ctypes.c_int, [_i32, _i64, _i32, _i32, _psz]),

@@ -50,20 +50,25 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
 }
 
+// The LDS destination must sit in an SGPR for m0.  The compiler may keep a
+// wave-uniform value in a VGPR (it then prints a VGPR for an "s" operand, which
+// does not assemble); readfirstlane moves it to an SGPR (no-op when it is one).
+__device__ __forceinline__ uint32_t sgpr(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+
 // Each lane copies 16 bytes from `src` to lds + 16 * lane (lds is wave-uniform).
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(sgpr(lds)) : "memory", "m0");
 }
 
 // Same, from the wave-uniform base `sbase` plus a per-lane 32-bit byte offset.
 __device__ __forceinline__ void dma16_off(const void* sbase, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(sbase), "s"(lds)
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(sbase), "s"(sgpr(lds))
                : "memory", "m0");
 }
 
 // Each active lane copies 4 bytes from `src` to lds + 4 * lane.
 __device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(sgpr(lds)) : "memory", "m0");
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding.

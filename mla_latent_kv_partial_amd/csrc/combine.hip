@@ -57,6 +57,15 @@ __device__ __forceinline__ float split_weight(float v, float m) {
   return (m == -INFINITY || v == -INFINITY) ? 0.f : expf(v - m);
 }
 
+// Four consecutive partial features as fp32: one 16-byte load of fp32
+// partials, or one 8-byte load of bf16 partials (widened exactly).
+__device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 load4(const uint16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xffff0000u));
+}
+
 // a split with no valid token (weight 0) adds nothing, whatever its partial holds
 __device__ __forceinline__ void fma4(float4& acc, float w, const float4& v) {
   if (w == 0.f) return;
@@ -68,7 +77,8 @@ __device__ __forceinline__ void fma4(float4& acc, float w, const float4& v) {
 
 // Two workgroups per CU (at most 128 VGPRs): the (head, row) grid of a decode
 // step then runs in one round.
-template <bool VEC, int VM>
+// PT: the partials' storage type (float, or uint16_t for bf16 bits).
+template <typename PT, bool VEC, int VM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void combine_kernel(CombineParams p) {
   constexpr int kU = kUnroll;   // batch of partial loads per thread
   const int h = blockIdx.x, b = blockIdx.y;
@@ -78,7 +88,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const int n = p.n_splits[b];
   const int64_t bh = static_cast<int64_t>(b) * p.heads + h;
   const float* lse_in = p.part_lse + bh * p.s_max;
-  const float* po = p.part_o + bh * p.s_max * p.r;
+  const PT* po = static_cast<const PT*>(p.part_o) + bh * p.s_max * p.r;
   __shared__ float red_m[kWaves], red_l[kWaves];
   __shared__ float ws[kMaxSplitsLds];   // split lse, then split weights
   __shared__ float4 grp_s[kGroups - 1][kGroupThreads];
@@ -121,7 +131,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int s = min(grp + kGroups * u, n - 1);
-      v0[u] = *reinterpret_cast<const float4*>(po + static_cast<int64_t>(s) * p.r + c);
+      v0[u] = load4(po + static_cast<int64_t>(s) * p.r + c);
     }
   }
 
@@ -168,7 +178,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         if (c0 > 0 || s > grp) {
 #pragma unroll
           for (int u = 0; u < kU; ++u)
-            v0[u] = *reinterpret_cast<const float4*>(po + static_cast<int64_t>(min(s + kGroups * u, n - 1)) * p.r + c);
+            v0[u] = load4(po + static_cast<int64_t>(min(s + kGroups * u, n - 1)) * p.r + c);
         }
 #pragma unroll
         for (int u = 0; u < kU; ++u)
@@ -193,7 +203,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       float acc = 0.f;
       for (int s = 0; s < n; ++s) {
         const float w = weight(s);
-        if (w != 0.f) acc = fmaf(w, po[static_cast<int64_t>(s) * p.r + c], acc);
+        if (w != 0.f) acc = fmaf(w, ld(po + static_cast<int64_t>(s) * p.r + c), acc);
       }
       if (p.o_lat) p.o_lat[bh * p.r + c] = acc * inv;
       if constexpr (VM != kVNone) o_sh[c] = acc * inv;
@@ -251,30 +261,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   }
 }
 
-}  // namespace
-
-hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
-  if (p.rows == 0) return hipSuccess;
-  // 16-byte partial rows: r a multiple of 4 from 16-byte aligned bases
-  const bool vec = p.r >= 4 && (p.r & 3) == 0 && (reinterpret_cast<uintptr_t>(p.part_o) & 15) == 0 &&
-                   (reinterpret_cast<uintptr_t>(p.o_lat) & 15) == 0;
+template <typename PT>
+hipError_t launch_combine_t(const CombineParams& p, hipStream_t stream) {
+  // whole 4-feature partial groups from aligned bases (16 bytes fp32, 8 bf16)
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(p.part_o) & (4 * sizeof(PT) - 1);
+  const bool vec = p.r >= 4 && (p.r & 3) == 0 && pa == 0 && (reinterpret_cast<uintptr_t>(p.o_lat) & 15) == 0;
   const dim3 grid(p.heads, p.rows), block(kThreads);
   if (!p.ctx) {
     if (vec)
-      hipLaunchKernelGGL((combine_kernel<true, kVNone>), grid, block, 0, stream, p);
+      hipLaunchKernelGGL((combine_kernel<PT, true, kVNone>), grid, block, 0, stream, p);
     else
-      hipLaunchKernelGGL((combine_kernel<false, kVNone>), grid, block, 0, stream, p);
+      hipLaunchKernelGGL((combine_kernel<PT, false, kVNone>), grid, block, 0, stream, p);
     return hipGetLastError();
   }
   const bool fast = vec && p.w_dtype == kBF16 && p.r % 64 == 0 && p.r / 64 <= kFastLoads &&
                     p.dv <= kFastCols * kFastPasses && (reinterpret_cast<uintptr_t>(p.w) & 15) == 0;
   if (fast)
-    hipLaunchKernelGGL((combine_kernel<true, kVFastBf16>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((combine_kernel<PT, true, kVFastBf16>), grid, block, 0, stream, p);
   else if (vec)
-    hipLaunchKernelGGL((combine_kernel<true, kVGeneric>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((combine_kernel<PT, true, kVGeneric>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((combine_kernel<false, kVGeneric>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((combine_kernel<PT, false, kVGeneric>), grid, block, 0, stream, p);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
+  if (p.rows == 0) return hipSuccess;
+  return p.part_bf16 ? launch_combine_t<uint16_t>(p, stream) : launch_combine_t<float>(p, stream);
 }
 
 }  // namespace mla

@@ -99,7 +99,12 @@ __global__ __launch_bounds__(kTile) void decode_generic_kernel(DecodeParams p) {
 #pragma unroll
   for (int k = 0; k < kPerThread; ++k) {
     const int c = tid + k * kTile;
-    if (c < p.r) p.part_o[ps * p.r + c] = o[k] * inv_l;
+    if (c < p.r) {
+      if (p.part_bf16)
+        static_cast<uint16_t*>(p.part_o)[ps * p.r + c] = f32_to_bf16(o[k] * inv_l);
+      else
+        static_cast<float*>(p.part_o)[ps * p.r + c] = o[k] * inv_l;
+    }
   }
   if (tid == 0) p.part_lse[ps] = l > 0.f ? m + logf(l) : -INFINITY;
 }

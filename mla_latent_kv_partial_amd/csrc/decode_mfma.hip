@@ -23,7 +23,7 @@
 //
 // HBM -> LDS: 32-token tiles stream through a 4-stage LDS ring by
 // global_load_lds_dwordx4 (each lane moves 16 bytes), two tiles ahead of the
-// score waves.  A token occupies one 1184-byte LDS row: latent (1024 B), rope
+// score waves; with 64 heads the context waves issue the copies.  A token occupies one 1184-byte LDS row: latent (1024 B), rope
 // (128 B), 32 B of padding.  A gathered row uses the same copies with
 // per-token addresses, so a gather and a dense read of the same tokens are
 // bit-identical.  The running max of a head only moves when a tile exceeds it
@@ -96,9 +96,18 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
 template <int NW, bool GATHER, bool PACKED>
 struct Decode {
   static constexpr int kWaves = 2 * NW;
-  // Wave v issues tile copies n = v, v + kWaves, ... below kDmaPerTile:
-  // kMaxDma or kMaxDma - 1 of them.
-  static constexpr int kMaxDma = (kDmaPerTile + kWaves - 1) / kWaves;
+  // Copy-issuing waves.  With 64 heads only the context waves issue the tile
+  // copies: a copy instruction holds its wave until the CU's address path
+  // takes it (about 16 cycles per 1 KB copy), so issuing a tile stalls the
+  // issuing waves for several hundred cycles, and the score waves, whose
+  // scores and softmax are the loop's critical path, start their MFMAs right
+  // after the barrier instead.  With 16 or 32 heads every wave issues (fewer
+  // waves, and a single context wave would hold all 37 copies in registers).
+  static constexpr int kIssuers = NW == 4 ? NW : kWaves;
+  static constexpr int kFirstIssuer = NW == 4 ? NW : 0;
+  // Issuing wave kFirstIssuer + v issues tile copies n = v, v + kIssuers, ...
+  // below kDmaPerTile: kMaxDma or kMaxDma - 1 of them; the others none.
+  static constexpr int kMaxDma = (kDmaPerTile + kIssuers - 1) / kIssuers;
   // Context waves: dim blocks per wave; reg[db * NW + hb] holds dims
   // 16 (c kCtxBlocks + db) + 4 g + (0..3) of head 16 hb + h.
   static constexpr int kCtxBlocks = kDimBlocks / NW;
@@ -144,13 +153,46 @@ struct Decode {
   // row_v: lane t < 32 holds token t's row, as a byte offset from lat_base
   // (PACKED) or as a row slot.
   __device__ __forceinline__ void copy(int i, int row_v, uint32_t dst) const {
-    const int v = __builtin_amdgcn_ds_bpermute(dma_src[i], row_v);
-    const int off = dma_off[i];
+    int src4, off;
+    plan(i, src4, off);
+    const int v = __builtin_amdgcn_ds_bpermute(src4, row_v);
     if (PACKED) {
-      dma16_off(lat_base, static_cast<uint32_t>(v) + static_cast<uint32_t>(off), dst + (wave + kWaves * i) * 1024);
+      dma16_off(lat_base, static_cast<uint32_t>(v) + static_cast<uint32_t>(off), dst + block(i) * 1024);
     } else {
       const char* src = off >= 0 ? lat_base + v * lat_st + off : rope_base + v * rope_st + (off & 0x7fff);
-      dma16(src, dst + (wave + kWaves * i) * 1024);
+      dma16(src, dst + block(i) * 1024);
+    }
+  }
+
+  // LDS block (1 KB) of this wave's copy i within a stage.
+  __device__ __forceinline__ int block(int i) const { return wave - kFirstIssuer + kIssuers * i; }
+
+  // Copy plan (the same for every tile): copy i of an issuing wave moves
+  // stage chunk k = 64 block(i) + lane, which is chunk c of token row k / 74
+  // (c < 64 latent, c < 72 rope, 72 and 73 padding).  src4 = 4 x the token
+  // row (a bpermute address); off = the chunk's byte offset in the packed row,
+  // or in the latent row, or in the rope row with the sign bit set.  The plan
+  // stays in registers, except in the 64-head separate-array form, whose
+  // issuing (context) waves also hold 64-bit addresses: it recomputes the plan,
+  // which keeps them unspilled.
+  __device__ __forceinline__ void plan_of(int i, int& src4, int& off) const {
+    const int k = 64 * block(i) + lane;
+    int row = k / kRowChunks;
+    const int c = k - row * kRowChunks;
+    row = min(row, kNT - 1);   // the tail of the last copy lands past the rows; it reads a valid token
+    src4 = 4 * row;
+    if (PACKED)
+      off = c < 72 ? c * 16 : 0;   // rope follows the latent in the packed row
+    else
+      off = c < 64 ? c * 16 : (c < 72 ? static_cast<int>(0x80000000u | static_cast<uint32_t>((c - 64) * 16)) : 0);
+  }
+  static constexpr bool kPlanInRegs = PACKED || NW < 4;
+  __device__ __forceinline__ void plan(int i, int& src4, int& off) const {
+    if (kPlanInRegs) {
+      src4 = dma_src[i];
+      off = dma_off[i];
+    } else {
+      plan_of(i, src4, off);
     }
   }
 
@@ -158,21 +200,23 @@ struct Decode {
   // inside the split; past its end the copy reads the valid slot width - 1
   // (those tokens are masked).  No lane exchange needed.
   __device__ __forceinline__ void issue_tile_dense(int s, int tile) const {
+    if (n_dma == 0) return;   // not an issuing wave (wave-uniform)
     const uint32_t dst = lds_addr(stage(s));
     const int first = tile * kNT;
     const int base = pad + sel_base + first;
 #pragma unroll
     for (int i = 0; i < kMaxDma; ++i) {
       if (i == kMaxDma - 1 && n_dma != kMaxDma) break;
-      const int r = dma_src[i] >> 2;
+      int src4, off;
+      plan(i, src4, off);
+      const int r = src4 >> 2;
       const int slot = first + r < n_tok ? base + r : p.width - 1;
-      const int off = dma_off[i];
       if (PACKED) {
         dma16_off(lat_base, static_cast<uint32_t>(slot) * static_cast<uint32_t>(lat_st) + static_cast<uint32_t>(off),
-                  dst + (wave + kWaves * i) * 1024);
+                  dst + block(i) * 1024);
       } else {
         const char* src = off >= 0 ? lat_base + slot * lat_st + off : rope_base + slot * rope_st + (off & 0x7fff);
-        dma16(src, dst + (wave + kWaves * i) * 1024);
+        dma16(src, dst + block(i) * 1024);
       }
     }
   }
@@ -185,17 +229,19 @@ struct Decode {
 
   // Copy one tile into stage s.  slot_v: lane t < 32 holds token t's row slot.
   __device__ __forceinline__ void issue_tile(int s, int slot_v) const {
+    if (n_dma == 0) return;   // not an issuing wave (wave-uniform)
     const uint32_t dst = lds_addr(stage(s));
     const int row_v = PACKED ? static_cast<int>(static_cast<uint32_t>(slot_v) * static_cast<uint32_t>(lat_st)) : slot_v;
 #pragma unroll
-    for (int i = 0; i < kMaxDma - 1; ++i) copy(i, row_v, dst);   // every wave has these
+    for (int i = 0; i < kMaxDma - 1; ++i) copy(i, row_v, dst);   // every issuing wave has these
     if (n_dma == kMaxDma) copy(kMaxDma - 1, row_v, dst);
   }
 
   // Gathered rows: copy the 32 selection indices of a tile (clamped inside the
-  // row's list) into the index area of stage s.  Wave 0 only.
+  // row's list) into the index area of stage s.  The first issuing wave only
+  // (its tile-copy waits cover these copies, see ops_after).
   __device__ __forceinline__ void issue_idx(int s, int tile) const {
-    if (gather_row && wave == 0 && lane < kNT) {
+    if (gather_row && wave == kFirstIssuer && lane < kNT) {
       const int j = min(tile * kNT + lane, n_tok - 1);
       dma4(p.sel + sel_base + j, lds_addr(idx_area(s)));
     }
@@ -310,21 +356,12 @@ struct Decode {
   }
 
   __device__ __forceinline__ void run(int b, int s) {
-    // ---- per-lane copy plan (the same for every tile): copy i of this wave
-    // moves stage chunk k = 64 (wave + kWaves i) + lane, which is chunk c of
-    // token row k / 74 (c < 64 latent, c < 72 rope, 72 and 73 padding).
-    n_dma = (kDmaPerTile - wave + kWaves - 1) / kWaves;
+    // ---- the copy plan (see plan_of)
+    const int v = wave - kFirstIssuer;
+    n_dma = v < 0 ? 0 : (kDmaPerTile - v + kIssuers - 1) / kIssuers;
+    if (kPlanInRegs) {
 #pragma unroll
-    for (int i = 0; i < kMaxDma; ++i) {
-      const int k = 64 * (wave + kWaves * i) + lane;
-      int row = k / kRowChunks;
-      const int c = k - row * kRowChunks;
-      row = min(row, kNT - 1);   // the tail of the last copy lands past the rows; it reads a valid token
-      dma_src[i] = 4 * row;
-      if (PACKED)
-        dma_off[i] = c < 72 ? c * 16 : 0;   // rope follows the latent in the packed row
-      else
-        dma_off[i] = c < 64 ? c * 16 : (c < 72 ? static_cast<int>(0x80000000u | static_cast<uint32_t>((c - 64) * 16)) : 0);
+      for (int i = 0; i < kMaxDma; ++i) plan_of(i, dma_src[i], dma_off[i]);
     }
     // ---- per-lane LDS fragment bases
     qk_base = sigma(h) * kRowBytes + g * 16;
@@ -488,7 +525,15 @@ struct Decode {
         const int64_t ps = (static_cast<int64_t>(b) * p.heads + head0 + row) * p.s_max + s;
         // non-temporal: the burst at the end of the launch does not wait on
         // the caches (3-4 us less per 169 MB launch, measured)
-        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p.part_o + ps * kR + kEpiDims * hw + 4 * c));
+        const int64_t e = ps * kR + kEpiDims * hw + 4 * c;
+        if (p.part_bf16) {
+          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+          const u32x2 pk = {static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16),
+                            static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16)};
+          __builtin_nontemporal_store(pk, reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.part_o) + e));
+        } else {
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(static_cast<float*>(p.part_o) + e));
+        }
       }
     }
   }

@@ -71,13 +71,14 @@ struct DecodeParams {
   const void* rope;
   int64_t rope_sb, rope_st;
   const int32_t* sel;     // selection base (may be null)
-  float* part_o;          // [rows,H,s_max,r]
+  void* part_o;           // [rows,H,s_max,r] fp32, or bf16 when part_bf16
   float* part_lse;        // [rows,H,s_max]
   int32_t* dev_err;
   int32_t rows, heads, r, dr, width;
   int32_t chunk, s_max, s_launch;        // s_launch = max splits over the launch rows
   int32_t s_total;                       // splits of all launch rows (= split_begin[rows])
   int32_t q_copy;                        // queries may be copied HBM -> LDS (16-byte aligned q_rope rows)
+  int32_t part_bf16;                     // partials stored as bf16 (round to nearest even)
   float scale;
   DecodeRows tab;
 };
@@ -87,11 +88,12 @@ hipError_t launch_stream_probe(const DecodeParams& p, hipStream_t stream);
 
 // ------------------------------------------------------------------ combine
 struct CombineParams {
-  const float* part_o;
+  const void* part_o;     // fp32, or bf16 when part_bf16
   const float* part_lse;
   float* o_lat;           // may be null when ctx is set
   float* lse;             // may be null
   int32_t rows, heads, r, s_max;
+  int32_t part_bf16;
   // value projection after the merge (ctx = o_lat . W_UV^T), when ctx is set
   const void* w;          // [H*(dn+dv), r] of w_dtype
   float* ctx;             // [rows, H*dv]

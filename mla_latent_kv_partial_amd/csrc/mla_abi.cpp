@@ -202,9 +202,10 @@ int mla_decode_latent_attn(int32_t dtype, const void* q_lat, const void* q_rope,
                            const void* rope, int64_t rope_stride_b, int64_t rope_stride_t, int32_t batch,
                            int32_t heads, int32_t kv_lora_rank, int32_t rope_dim, int32_t width,
                            const int32_t* kv_len, const int32_t* sel_idx, const int32_t* sel_count,
-                           float softmax_scale, int32_t chunk_len, float* part_o, float* part_lse, int32_t s_max,
-                           int32_t* dev_err, hipStream_t stream) {
+                           float softmax_scale, int32_t chunk_len, int32_t part_dtype, void* part_o,
+                           float* part_lse, int32_t s_max, int32_t* dev_err, hipStream_t stream) {
   if (!valid_dtype(dtype)) return fail(MLA_ERR_ARG, "decode: unknown dtype %d", dtype);
+  if (!valid_dtype(part_dtype)) return fail(MLA_ERR_ARG, "decode: unknown part_dtype %d", part_dtype);
   if (batch < 0 || heads < 1 || kv_lora_rank < 1 || rope_dim < 1 || width < 1)
     return fail(MLA_ERR_ARG, "decode: batch >= 0 and positive heads, kv_lora_rank, rope_dim, width required");
   if (chunk_len < 1) return fail(MLA_ERR_ARG, "decode: chunk_len must be >= 1");
@@ -260,6 +261,7 @@ int mla_decode_latent_attn(int32_t dtype, const void* q_lat, const void* q_rope,
   p.chunk = chunk_len;
   p.s_max = s_max;
   p.scale = softmax_scale;
+  p.part_bf16 = part_dtype == MLA_DTYPE_BF16;
   int32_t sel_off = 0;
   for (int b0 = 0; b0 < batch; b0 += mla::kDecodeRowsPerLaunch) {
     p.rows = std::min(batch - b0, mla::kDecodeRowsPerLaunch);
@@ -281,7 +283,8 @@ int mla_decode_latent_attn(int32_t dtype, const void* q_lat, const void* q_rope,
     p.q_rope = advance(q_rope, b0 * qr_stride_b, dtype);
     p.latent = advance(latent, b0 * latent_stride_b, dtype);
     p.rope = advance(rope, b0 * rope_stride_b, dtype);
-    p.part_o = part_o + static_cast<int64_t>(b0) * heads * s_max * kv_lora_rank;
+    p.part_o = static_cast<char*>(part_o) +
+               static_cast<int64_t>(b0) * heads * s_max * kv_lora_rank * static_cast<int64_t>(elem_size(part_dtype));
     p.part_lse = part_lse + static_cast<int64_t>(b0) * heads * s_max;
     hipError_t e = mfma ? mla::launch_decode_mfma(p, stream) : mla::launch_decode_generic(dtype, p, stream);
     if (e != hipSuccess) return device(e, "decode launch");
@@ -555,8 +558,10 @@ int mla_dsa_topk_select_noalloc(const float* scores, int64_t score_stride, int32
   return topk_launch(scores, score_stride, batch, row_len, top_k, sel_idx, sel_count, ws, stream);
 }
 
-int mla_decode_combine(const float* part_o, const float* part_lse, int32_t batch, int32_t heads, int32_t kv_lora_rank,
-                       int32_t s_max, const int32_t* n_splits, float* o_lat, float* lse, hipStream_t stream) {
+int mla_decode_combine(int32_t part_dtype, const void* part_o, const float* part_lse, int32_t batch, int32_t heads,
+                       int32_t kv_lora_rank, int32_t s_max, const int32_t* n_splits, float* o_lat, float* lse,
+                       hipStream_t stream) {
+  if (!valid_dtype(part_dtype)) return fail(MLA_ERR_ARG, "combine: unknown part_dtype %d", part_dtype);
   if (batch < 0 || heads < 1 || kv_lora_rank < 1 || s_max < 1)
     return fail(MLA_ERR_ARG, "combine: batch >= 0 and positive heads, kv_lora_rank, s_max required");
   if (batch == 0) return ok();
@@ -569,11 +574,12 @@ int mla_decode_combine(const float* part_o, const float* part_lse, int32_t batch
   p.heads = heads;
   p.r = kv_lora_rank;
   p.s_max = s_max;
+  p.part_bf16 = part_dtype == MLA_DTYPE_BF16;
   for (int b0 = 0; b0 < batch; b0 += mla::kCombineRowsPerLaunch) {
     p.rows = std::min(batch - b0, mla::kCombineRowsPerLaunch);
     for (int i = 0; i < p.rows; ++i) p.n_splits[i] = n_splits[b0 + i];
     const int64_t bh = static_cast<int64_t>(b0) * heads;
-    p.part_o = part_o + bh * s_max * kv_lora_rank;
+    p.part_o = advance(part_o, bh * s_max * kv_lora_rank, part_dtype);
     p.part_lse = part_lse + bh * s_max;
     p.o_lat = o_lat + bh * kv_lora_rank;
     p.lse = lse ? lse + bh : nullptr;
@@ -583,10 +589,12 @@ int mla_decode_combine(const float* part_o, const float* part_lse, int32_t batch
   return ok();
 }
 
-int mla_decode_combine_v(int32_t dtype, const float* part_o, const float* part_lse, int32_t batch, int32_t heads,
+int mla_decode_combine_v(int32_t dtype, int32_t part_dtype, const void* part_o, const float* part_lse, int32_t batch,
+                         int32_t heads,
                          int32_t kv_lora_rank, int32_t s_max, const int32_t* n_splits, const void* w_kv_b,
                          int32_t qk_nope, int32_t v_head, float* ctx, float* o_lat, float* lse, hipStream_t stream) {
   if (!valid_dtype(dtype)) return fail(MLA_ERR_ARG, "combine_v: unknown dtype %d", dtype);
+  if (!valid_dtype(part_dtype)) return fail(MLA_ERR_ARG, "combine_v: unknown part_dtype %d", part_dtype);
   if (batch < 0 || heads < 1 || kv_lora_rank < 1 || s_max < 1 || qk_nope < 1 || v_head < 1)
     return fail(MLA_ERR_ARG,
                 "combine_v: batch >= 0 and positive heads, kv_lora_rank, s_max, qk_nope, v_head required");
@@ -603,13 +611,14 @@ int mla_decode_combine_v(int32_t dtype, const float* part_o, const float* part_l
   p.s_max = s_max;
   p.w = w_kv_b;
   p.w_dtype = dtype;
+  p.part_bf16 = part_dtype == MLA_DTYPE_BF16;
   p.dn = qk_nope;
   p.dv = v_head;
   for (int b0 = 0; b0 < batch; b0 += mla::kCombineRowsPerLaunch) {
     p.rows = std::min(batch - b0, mla::kCombineRowsPerLaunch);
     for (int i = 0; i < p.rows; ++i) p.n_splits[i] = n_splits[b0 + i];
     const int64_t bh = static_cast<int64_t>(b0) * heads;
-    p.part_o = part_o + bh * s_max * kv_lora_rank;
+    p.part_o = advance(part_o, bh * s_max * kv_lora_rank, part_dtype);
     p.part_lse = part_lse + bh * s_max;
     p.o_lat = o_lat ? o_lat + bh * kv_lora_rank : nullptr;
     p.lse = lse ? lse + bh : nullptr;

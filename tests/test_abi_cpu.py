@@ -61,12 +61,12 @@ def test_rope_empty_is_a_no_op():
 
 def _decode(**kw):
     a = dict(dtype=1, b=2, h=64, r=512, dr=64, w=100, kv=[100, 50], sel=None, cnt=None, chunk=32, s_max=4,
-             scale=0.07, sel_idx=None)
+             scale=0.07, sel_idx=None, pdt=0)
     a.update(kw)
     return lib.mla_decode_latent_attn(
         a["dtype"], FAKE, FAKE, 64 * 64, 64, FAKE, 100 * 576, 576, FAKE, 100 * 576, 576, a["b"], a["h"], a["r"],
         a["dr"], a["w"], i32_array(a["kv"]), a["sel_idx"], None if a["cnt"] is None else i32_array(a["cnt"]),
-        a["scale"], a["chunk"], FAKE, FAKE, a["s_max"], None, None)
+        a["scale"], a["chunk"], a["pdt"], FAKE, FAKE, a["s_max"], None, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -75,7 +75,7 @@ def _decode(**kw):
     (dict(cnt=[0, -1], sel_idx=FAKE), SEL), (dict(cnt=[-2, -1], sel_idx=FAKE), SEL),
     (dict(cnt=[5, -1], sel_idx=None), ARG),
     (dict(chunk=0), ARG), (dict(h=0), ARG), (dict(dtype=3), ARG), (dict(scale=float("nan")), ARG),
-    (dict(r=2048), UNSUP), (dict(dr=512), UNSUP),
+    (dict(r=2048), UNSUP), (dict(dr=512), UNSUP), (dict(pdt=5), ARG),
 ])
 def test_decode_rejections(kw, code):
     assert _decode(**kw) == code
@@ -85,20 +85,21 @@ def test_decode_empty_batch_is_ok():
     assert _decode(b=0, kv=[]) == OK
 
 
-@pytest.mark.parametrize("ns,code", [([0, 1], SHAPE), ([5, 1], SHAPE)])
-def test_combine_rejections(ns, code):
-    assert lib.mla_decode_combine(FAKE, FAKE, 2, 4, 8, 4, i32_array(ns), FAKE, None, None) == code
+@pytest.mark.parametrize("pdt,ns,code", [(0, [0, 1], SHAPE), (1, [5, 1], SHAPE), (2, [1, 1], ARG)])
+def test_combine_rejections(pdt, ns, code):
+    assert lib.mla_decode_combine(pdt, FAKE, FAKE, 2, 4, 8, 4, i32_array(ns), FAKE, None, None) == code
 
 
 def test_combine_v_rejections():
     ns = i32_array([2, 1])
-    assert lib.mla_decode_combine_v(7, FAKE, FAKE, 2, 4, 8, 4, ns, FAKE, 4, 4, FAKE, None, None, None) == ARG
-    assert lib.mla_decode_combine_v(1, FAKE, FAKE, 2, 4, 8, 4, ns, FAKE, 4, 0, FAKE, None, None, None) == ARG
-    assert lib.mla_decode_combine_v(1, FAKE, FAKE, 2, 4, 8, 4, ns, FAKE, 4, 4, None, None, None, None) == ARG
-    assert lib.mla_decode_combine_v(1, FAKE, FAKE, 2, 4, 8, 4, i32_array([5, 1]), FAKE, 4, 4, FAKE, None, None,
+    assert lib.mla_decode_combine_v(7, 0, FAKE, FAKE, 2, 4, 8, 4, ns, FAKE, 4, 4, FAKE, None, None, None) == ARG
+    assert lib.mla_decode_combine_v(1, 0, FAKE, FAKE, 2, 4, 8, 4, ns, FAKE, 4, 0, FAKE, None, None, None) == ARG
+    assert lib.mla_decode_combine_v(1, 0, FAKE, FAKE, 2, 4, 8, 4, ns, FAKE, 4, 4, None, None, None, None) == ARG
+    assert lib.mla_decode_combine_v(1, 0, FAKE, FAKE, 2, 4, 8, 4, i32_array([5, 1]), FAKE, 4, 4, FAKE, None, None,
                                     None) == SHAPE
-    assert lib.mla_decode_combine_v(1, FAKE, FAKE, 2, 4, 2048, 4, ns, FAKE, 4, 4, FAKE, None, None, None) == UNSUP
-    assert lib.mla_decode_combine_v(1, FAKE, FAKE, 0, 4, 8, 4, ns, FAKE, 4, 4, FAKE, None, None, None) == OK
+    assert lib.mla_decode_combine_v(1, 0, FAKE, FAKE, 2, 4, 2048, 4, ns, FAKE, 4, 4, FAKE, None, None, None) == UNSUP
+    assert lib.mla_decode_combine_v(1, 0, FAKE, FAKE, 0, 4, 8, 4, ns, FAKE, 4, 4, FAKE, None, None, None) == OK
+    assert lib.mla_decode_combine_v(1, 3, FAKE, FAKE, 2, 4, 8, 4, ns, FAKE, 4, 4, FAKE, None, None, None) == ARG
 
 
 def test_stream_probe_rejections():

@@ -44,7 +44,7 @@ class Step:
         self.sel = dev(inp.sel_idx) if inp.sel_idx is not None else None
         self.err = torch.zeros(1, dtype=torch.int32, device="cuda")
 
-    def run(self, chunk):
+    def run(self, chunk, part_dtype=torch.float32):
         mla = _mla()
         c, inp = self.cfg, self.inp
         q_rope = self.q_rope.clone()
@@ -52,7 +52,8 @@ class Step:
         mla.mla_rope_partial_interleaved(view, [int(o) for o in inp.offsets], c.qk_rope, c.theta, out=view)
         q_lat = mla.mla_absorb_q(self.q_nope, self.w, c.v_head)
         po, pl, ns = mla.mla_decode_latent_attn(q_lat, q_rope, self.latent, self.rope, inp.kv_len, c.softmax_scale,
-                                                chunk, sel_idx=self.sel, sel_count=inp.sel_count, dev_err=self.err)
+                                                chunk, sel_idx=self.sel, sel_count=inp.sel_count, dev_err=self.err,
+                                                part_dtype=part_dtype)
         o_lat, lse = mla.mla_decode_combine(po, pl, ns)
         ctx = mla.mla_absorb_v(o_lat, self.w, c.qk_nope, c.v_head)
         # the same merge and projection in one launch
@@ -108,6 +109,34 @@ def test_decode_chain_matches_oracle(cfg, plan):
     if "ctx_rec" in ref:
         assert_close(host_values(got["ctx"]), ref["ctx_rec"], cfg.dtype, "ctx vs reconstructed oracle")
         assert_close(host_values(got["ctx_v"]), ref["ctx_rec"], cfg.dtype, "fused ctx vs reconstructed oracle")
+
+
+@pytest.mark.parametrize("cfg", [cf.DENSE_BF16, cf.RAGGED_BF16, cf.DSA_BF16], ids=lambda c: c.name)
+def test_decode_chain_bf16_partials(cfg):
+    """The bf16 workloads at full size in the split plan bench.py times, with
+    the split partials stored in bf16: the chain against the oracle at the bf16
+    bar, and the partials bit-identical to the fp32 partials of the same call
+    rounded to bf16 (one rounding of the same normalised values)."""
+    mla = _mla()
+    say(f"bf16 partials {cfg.name}: generating")
+    inp = cf.decode_inputs(cfg)
+    step = Step(inp)
+    n_att = [int(c) if inp.sel_count is not None and c > 0 else int(n)
+             for n, c in zip(inp.kv_len, inp.sel_count if inp.sel_count is not None else [-1] * len(inp.kv_len))]
+    chunk = mla.plan_chunk_len(n_att, 256)
+    got = step.run(chunk, part_dtype=torch.bfloat16)
+    ref32 = step.run(chunk)
+    assert int(step.err.item()) == 0
+    assert got["part_o"].dtype == torch.bfloat16
+    for b, n in enumerate(got["n_splits"]):
+        assert bitwise_equal(got["part_o"][b, :, :n], ref32["part_o"][b, :, :n].to(torch.bfloat16))
+        assert bitwise_equal(got["part_lse"][b, :, :n], ref32["part_lse"][b, :, :n])
+    say(f"bf16 partials {cfg.name}: oracle")
+    ref = _oracle(inp)
+    assert_close(host_values(got["o_lat"]), ref["o_lat"], cfg.dtype, "o_lat (bf16 partials)")
+    assert_close(host_values(got["lse"]), ref["lse"], cfg.dtype, "lse (bf16 partials)")
+    assert_close(host_values(got["ctx"]), ref["ctx"], cfg.dtype, "ctx (bf16 partials)")
+    assert_close(host_values(got["ctx_v"]), ref["ctx"], cfg.dtype, "fused combine_v ctx (bf16 partials)")
 
 
 def _small_ragged(lengths=(700, 1, 333), seed_layer=5):
@@ -362,6 +391,36 @@ def test_combine_direct_partials(heads, r, n_splits, s_max, misalign):
     fin = np.isfinite(lse_ref)
     assert np.array_equal(np.isfinite(lse_h), fin)
     assert np.allclose(lse_h[fin], lse_ref[fin], rtol=0, atol=1e-5)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_merge_of_bf16_partials(fused):
+    """The merge (and the fused merge + projection) reading bf16 partials, with
+    empty splits, against the oracle's merge of the same (exactly widened) values."""
+    mla = _mla()
+    n_splits = (1, 9, 31, 40)
+    b, heads, r, dn, dv = len(n_splits), 8, 512, 128, 128
+    s_max = max(n_splits)
+    po = cf.store(gen.normal_f32(98, 1, (b, heads, s_max, r)), cf.BF16)
+    pl = 3.0 * gen.normal_f32(98, 2, (b, heads, s_max))
+    empty = np.random.default_rng(12).random((b, heads, s_max)) < 0.2
+    empty[0, 0, :] = True
+    pl[empty] = -np.inf
+    w = cf.store(gen.normal_f32(98, 3, (heads * (dn + dv), r), std=r ** -0.5), cf.BF16)
+    po_ref = np.where(empty[..., None], 0.0, cf.values(po))
+    o_ref, lse_ref = oracle.combine_partials(po_ref, pl, n_splits)
+    o_lat = torch.empty((b, heads, r), dtype=torch.float32, device="cuda")
+    lse = torch.empty((b, heads), dtype=torch.float32, device="cuda")
+    if fused:
+        ctx = mla.mla_decode_combine_v(dev(po), dev(pl), list(n_splits), dev(w), dn, dv, o_lat=o_lat, lse=lse)
+    else:
+        mla.mla_decode_combine(dev(po), dev(pl), list(n_splits), o_lat=o_lat, lse=lse)
+    torch.cuda.synchronize()
+    assert_close(host_values(o_lat), o_ref, cf.F32, "merged o_lat of bf16 partials", tol=1e-5)
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(host_values(lse)), fin)
+    if fused:
+        assert_close(host_values(ctx), oracle.absorb_v(o_ref, cf.values(w), dn, dv), cf.F32, "fused ctx", tol=1e-5)
 
 
 @pytest.mark.parametrize("wdt,heads,r,dn,dv,n_splits", [

@@ -34,10 +34,13 @@ def test_m0_only_set_by_the_copy_sequences(name, tmp_path):
     assert lines, "expected the copy sequences to set m0"
     others = [ln for ln in lines if not ln.startswith("s_mov_b32 m0,")]
     assert not others, f"compiler-generated uses of m0: {others[:5]}"
-    # every m0 write is immediately followed by an LDS copy
+    # every m0 write comes from an SGPR (the text form would print a VGPR for
+    # an "s" operand the compiler kept in a VGPR, which does not assemble) and
+    # is immediately followed by an LDS copy
     body = [ln.strip() for ln in text.splitlines()]
     for i, ln in enumerate(body):
         if ln.startswith("s_mov_b32 m0,"):
+            assert re.match(r"s_mov_b32 m0, s\d+$", ln), ln
             assert body[i + 1].startswith("global_load_lds_dword"), body[i + 1]
 
 
