@@ -3,14 +3,14 @@
 // attendAbsorbed).  For row b, head h over its n_b splits:
 //   LSE = ln sum_s exp(lse_s),  o = sum_s exp(lse_s - LSE) o_s.
 // One workgroup of 512 threads per (head, row).  The partials of one
-// (row, head) are contiguous [n_b, r] fp32.  Four groups of 128 threads split
-// the splits (group j takes s = j mod 4); a thread owns four consecutive
-// latent features (one 16-byte load per split) and loads 16 splits at a
-// time.  The first 16 loads of every thread are issued before the split
-// weights are known, so their latency overlaps the log-sum-exp reduction,
-// which runs as one (max, sum) pair per thread, wave shuffles and a single
-// LDS exchange; the split weights are then formed once each, in LDS.  The
-// four group sums meet in LDS.
+// (row, head) are contiguous [n_b, r] (fp32 or bf16).  Four groups of 128
+// threads split the splits (group j takes s = j mod 4); a thread owns four
+// consecutive latent features and loads 16 splits (their lse and partials)
+// at a time, all in flight together.  Every thread of a group reads the same
+// lse values, so each keeps the group's running (max, sum of weights) itself
+// and weights its partials at once: no block-wide log-sum-exp reduction sits
+// between the loads and the accumulation.  The four groups' (max, sum,
+// partial sums) then meet in LDS once.
 //
 // With a value projection (mla_decode_combine_v) the merged latent context of
 // the (head, row) stays in LDS and the same workgroup projects it through the
@@ -75,6 +75,94 @@ __device__ __forceinline__ void fma4(float4& acc, float w, const float4& v) {
   acc.w = fmaf(w, v.w, acc.w);
 }
 
+constexpr float kLog2e = 1.4426950408889634f;
+
+// exp(x - m) for x <= m; 0 for x = -inf
+__device__ __forceinline__ float weight_of(float x, float m) {
+  return x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((x - m) * kLog2e);
+}
+
+// The splits s = grp + 4 k of one (row, head), features c .. c + 3, in
+// batches of kUnroll: Mg = their max lse, lg = sum exp(lse_s - Mg) and
+// acc = sum exp(lse_s - Mg) o_s (Mg = -inf: no split with a token).  Every
+// thread of the group reads the same lse values, so Mg and lg agree across
+// the group.  The first batch (lse in ls, partials in v) is loaded by the
+// caller; its entries past n hold lse -inf.
+template <typename PT>
+__device__ __forceinline__ void group_merge(const PT* po, const float* lse_in, int n, int r, int c, int grp,
+                                            float (&ls)[kUnroll], float4 (&v)[kUnroll], float& Mg, float& lg,
+                                            float4& acc) {
+  Mg = -INFINITY;
+  lg = 0.f;
+  acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = grp; s0 < n; s0 += kGroups * kUnroll) {
+    if (s0 > grp) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int sc = min(s0 + kGroups * u, n - 1);
+        ls[u] = s0 + kGroups * u < n ? lse_in[sc] : -INFINITY;
+        v[u] = load4(po + static_cast<int64_t>(sc) * r + c);
+      }
+    }
+    float bm = ls[0];
+#pragma unroll
+    for (int u = 1; u < kUnroll; ++u) bm = fmaxf(bm, ls[u]);
+    const float mn = fmaxf(Mg, bm);
+    if (mn == -INFINITY) continue;   // no token in these splits yet (same in the whole group)
+    const float rs = weight_of(Mg, mn);
+    acc.x *= rs; acc.y *= rs; acc.z *= rs; acc.w *= rs;
+    lg *= rs;
+    Mg = mn;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const float w = weight_of(ls[u], Mg);
+      lg += w;
+      fma4(acc, w, v[u]);
+    }
+  }
+}
+
+// The first batch of group_merge: lse and partials of splits grp + 4 u,
+// clamped to a valid split (entries past n get lse -inf; their partials are
+// loaded but never used, which keeps the loads free of branches).
+template <typename PT>
+__device__ __forceinline__ void first_batch(const PT* po, const float* lse_in, int n, int r, int c, int grp,
+                                            float (&ls)[kUnroll], float4 (&v)[kUnroll]) {
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int sc = min(grp + kGroups * u, n - 1);
+    ls[u] = lse_in[sc];
+    v[u] = load4(po + static_cast<int64_t>(sc) * r + c);
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u)
+    if (grp + kGroups * u >= n) ls[u] = -INFINITY;
+}
+
+// The four groups' merges meet: group 0 thread gt combines them (gm, gl: the
+// groups' max and sum, part: groups 1..3's partial sums) into the merged
+// features (o) and the log-sum-exp.
+__device__ __forceinline__ void meet_groups(const float* gm, const float* gl, const float4* p1, const float4* p2,
+                                            const float4* p3, float4 acc, float4& o, float& lse) {
+  float m = gm[0];
+#pragma unroll
+  for (int g = 1; g < kGroups; ++g) m = fmaxf(m, gm[g]);
+  if (m == -INFINITY) {
+    o = make_float4(0.f, 0.f, 0.f, 0.f);
+    lse = -INFINITY;
+    return;
+  }
+  const float f0 = weight_of(gm[0], m), f1 = weight_of(gm[1], m), f2 = weight_of(gm[2], m), f3 = weight_of(gm[3], m);
+  const float4 a1 = *p1, a2 = *p2, a3 = *p3;
+  const float l = f0 * gl[0] + f1 * gl[1] + f2 * gl[2] + f3 * gl[3];
+  const float inv = 1.f / l;
+  o.x = (f0 * acc.x + f1 * a1.x + f2 * a2.x + f3 * a3.x) * inv;
+  o.y = (f0 * acc.y + f1 * a1.y + f2 * a2.y + f3 * a3.y) * inv;
+  o.z = (f0 * acc.z + f1 * a1.z + f2 * a2.z + f3 * a3.z) * inv;
+  o.w = (f0 * acc.w + f1 * a1.w + f2 * a2.w + f3 * a3.w) * inv;
+  lse = m + logf(l);
+}
+
 // Two workgroups per CU (at most 128 VGPRs): the (head, row) grid of a decode
 // step then runs in one round.
 // PT: the partials' storage type (float, or uint16_t for bf16 bits).
@@ -118,87 +206,65 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
   };
 
-  // The thread's first split lse is requested first, then the first batch of
-  // partials of the first feature block: the lse reduction waits only for the
-  // former, the partial loads stay in flight through it.
-  const float lse0_raw = lse_in[min(tid, n - 1)];
-  asm volatile("" ::: "memory");
-  float4 v0[kU];
-  if (VEC) {
-    // clamped to a valid split and feature (n >= 1): a value past either end
-    // is loaded but never used, which keeps the loads free of branches
-    const int c = min(4 * gt, p.r - 4);
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int s = min(grp + kGroups * u, n - 1);
-      v0[u] = load4(po + static_cast<int64_t>(s) * p.r + c);
-    }
-  }
-
-  // ---- LSE over the splits: per-thread (max, sum) pairs, then waves, then
-  // LDS; the split lse values are kept in LDS for the weights
-  const float lse0 = tid < n ? lse0_raw : -INFINITY;
-  float m = lse0, l = lse0 == -INFINITY ? 0.f : 1.f;
-  if (tid < n && tid < kMaxSplitsLds) ws[tid] = lse0;
-  for (int s = tid + kThreads; s < n; s += kThreads) {
-    const float x = lse_in[s];
-    if (s < kMaxSplitsLds) ws[s] = x;
-    lse_merge(m, l, x, 1.f);
-  }
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    const float m2 = __shfl_xor(m, off, kWave), l2 = __shfl_xor(l, off, kWave);
-    lse_merge(m, l, m2, l2);
-  }
-  if (lane == 0) {
-    red_m[wave] = m;
-    red_l[wave] = l;
-  }
-  __syncthreads();
-  m = red_m[0];
-  l = red_l[0];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) lse_merge(m, l, red_m[w], red_l[w]);
-  // each thread turns the lse values it stored into weights; beyond the LDS
-  // copy the weights are formed where they are used
-  if (tid < n && tid < kMaxSplitsLds) ws[tid] = split_weight(lse0, m);
-  for (int s = tid + kThreads; s < min(n, kMaxSplitsLds); s += kThreads) ws[s] = split_weight(ws[s], m);
-  __syncthreads();
-  auto weight = [&](int s) { return s < kMaxSplitsLds ? ws[s] : split_weight(lse_in[s], m); };
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-
-  if (VEC) {
+  if constexpr (VEC) {
+    __shared__ float gm_s[kGroups], gl_s[kGroups];
     for (int c0 = 0; c0 < p.r; c0 += 4 * kGroupThreads) {
       const bool own = c0 + 4 * gt < p.r;
       const int c = min(c0 + 4 * gt, p.r - 4);
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-      // whole batches of kU splits per thread, loads clamped as above;
-      // the first batch of the first feature block is already in flight
-      for (int s = grp; s < n; s += kGroups * kU) {
-        if (c0 > 0 || s > grp) {
-#pragma unroll
-          for (int u = 0; u < kU; ++u)
-            v0[u] = load4(po + static_cast<int64_t>(min(s + kGroups * u, n - 1)) * p.r + c);
-        }
-#pragma unroll
-        for (int u = 0; u < kU; ++u)
-          if (s + kGroups * u < n) fma4(acc, weight(s + kGroups * u), v0[u]);
-      }
+      float ls[kU];
+      float4 v[kU];
+      first_batch(po, lse_in, n, p.r, c, grp, ls, v);
+      float mg, lg;
+      float4 acc;
+      group_merge(po, lse_in, n, p.r, c, grp, ls, v, mg, lg, acc);
       if (grp > 0) grp_s[grp - 1][gt] = acc;
+      if (gt == 0) {
+        gm_s[grp] = mg;
+        gl_s[grp] = lg;
+      }
       __syncthreads();
-      if (grp == 0 && own) {
-#pragma unroll
-        for (int j = 0; j < kGroups - 1; ++j) {
-          const float4 o = grp_s[j][gt];
-          acc.x += o.x; acc.y += o.y; acc.z += o.z; acc.w += o.w;
+      if (grp == 0) {
+        float4 o;
+        float lse;
+        meet_groups(gm_s, gl_s, &grp_s[0][gt], &grp_s[1][gt], &grp_s[2][gt], acc, o, lse);
+        if (own) {
+          if (p.o_lat) *reinterpret_cast<float4*>(p.o_lat + bh * p.r + c) = o;
+          if constexpr (VM != kVNone) *reinterpret_cast<float4*>(o_sh + c) = o;
         }
-        const float4 o = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-        if (p.o_lat) *reinterpret_cast<float4*>(p.o_lat + bh * p.r + c) = o;
-        if constexpr (VM != kVNone) *reinterpret_cast<float4*>(o_sh + c) = o;
+        if (c0 == 0 && gt == 0 && p.lse) p.lse[bh] = lse;
       }
       __syncthreads();
     }
   } else {
+    // ---- scalar path: LSE over the splits (per-thread (max, sum) pairs,
+    // waves, LDS), split weights in LDS, one thread per feature
+    const float lse0 = tid < n ? lse_in[tid] : -INFINITY;
+    float m = lse0, l = lse0 == -INFINITY ? 0.f : 1.f;
+    if (tid < n && tid < kMaxSplitsLds) ws[tid] = lse0;
+    for (int s = tid + kThreads; s < n; s += kThreads) {
+      const float x = lse_in[s];
+      if (s < kMaxSplitsLds) ws[s] = x;
+      lse_merge(m, l, x, 1.f);
+    }
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+      const float m2 = __shfl_xor(m, off, kWave), l2 = __shfl_xor(l, off, kWave);
+      lse_merge(m, l, m2, l2);
+    }
+    if (lane == 0) {
+      red_m[wave] = m;
+      red_l[wave] = l;
+    }
+    __syncthreads();
+    m = red_m[0];
+    l = red_l[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) lse_merge(m, l, red_m[w], red_l[w]);
+    if (tid < n && tid < kMaxSplitsLds) ws[tid] = split_weight(lse0, m);
+    for (int s = tid + kThreads; s < min(n, kMaxSplitsLds); s += kThreads) ws[s] = split_weight(ws[s], m);
+    __syncthreads();
+    auto weight = [&](int s) { return s < kMaxSplitsLds ? ws[s] : split_weight(lse_in[s], m); };
+    const float inv = l > 0.f ? 1.f / l : 0.f;
     for (int c = tid; c < p.r; c += kThreads) {
       float acc = 0.f;
       for (int s = 0; s < n; ++s) {
@@ -208,8 +274,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       if (p.o_lat) p.o_lat[bh * p.r + c] = acc * inv;
       if constexpr (VM != kVNone) o_sh[c] = acc * inv;
     }
+    if (p.lse && tid == 0) p.lse[bh] = l > 0.f ? m + logf(l) : -INFINITY;
   }
-  if (p.lse && tid == 0) p.lse[bh] = l > 0.f ? m + logf(l) : -INFINITY;
   if constexpr (VM == kVNone) return;
   __syncthreads();   // o_sh complete
 
@@ -261,6 +327,125 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   }
 }
 
+// ---- The fused merge + projection for bf16 weights, kv_lora_rank 512 and
+// v_head <= 128 (the decode step's combine_v): one workgroup of 1024 threads
+// per (head, pair of rows).  Each half of the workgroup merges one row as
+// combine_kernel does, while the head's value block (v_head weight rows of
+// 1 KB) streams into LDS by global_load_lds copies issued right behind the
+// merge's first loads.  The projection then reads every weight element from
+// LDS once for both rows.  Against one workgroup per (head, row) this fetches
+// each value block once per row pair rather than per row, and the weights no
+// longer wait for the merge.  Workgroup ids run head fastest: the row pairs
+// of a head share an XCD and its L2.
+constexpr int kPairThreads = 2 * kThreads;
+constexpr int kPairR = 512;
+constexpr int kWRowBytes = kPairR * 2 + 32;    // weight row in LDS: an odd number of 32-byte units
+constexpr int kPairMaxDv = 128;
+constexpr int kEighths = kPairThreads / kPairMaxDv;   // projection: the latent axis in 8 parts of 64
+static_assert(kEighths * 64 == kPairR, "the projection splits the latent axis in eighths of 64");
+
+__shared__ __attribute__((aligned(1024))) char g_w[kPairMaxDv * kWRowBytes];
+
+template <typename PT>
+__global__ __launch_bounds__(kPairThreads) void combine_v_pair_kernel(CombineParams p) {
+  constexpr int kU = kUnroll;
+  const int h = blockIdx.x;
+  const int half = __builtin_amdgcn_readfirstlane(threadIdx.x / kThreads);
+  const int tid = threadIdx.x % kThreads;   // thread of this half
+  const int lane = tid & (kWave - 1);
+  const int b_want = 2 * blockIdx.y + half;
+  const bool real = b_want < p.rows;
+  const int b = real ? b_want : p.rows - 1;   // a missing second row merges the last row again, unstored
+  const int n = p.n_splits[b];
+  const int64_t bh = static_cast<int64_t>(b) * p.heads + h;
+  const float* lse_in = p.part_lse + bh * p.s_max;
+  const PT* po = static_cast<const PT*>(p.part_o) + bh * p.s_max * kPairR;
+  __shared__ float gm_s[2][kGroups], gl_s[2][kGroups];
+  __shared__ float4 grp_all[2][kGroups - 1][kGroupThreads];   // group sums, then the projection's partial sums
+  __shared__ __attribute__((aligned(16))) float o_sh[2][kPairR];
+
+  const int grp = __builtin_amdgcn_readfirstlane(tid / kGroupThreads);
+  const int gt = tid % kGroupThreads;
+  const int c = 4 * gt;   // this thread's four latent features (kPairR = 4 x 128)
+
+  // the merge's first batch (lse and partials of 16 splits per thread), then
+  // the value block behind it: weight row j (output column j) to
+  // g_w + j * kWRowBytes, one 1 KB copy per row; wave v of the workgroup copies
+  // rows v, v + 16, ...  (the compiler's waits for the merge's loads count
+  // only its own loads, so they also wait for some of the copies issued after
+  // them: safe, and nothing the merge waits for lies behind the copies)
+  float ls[kU];
+  float4 v[kU];
+  first_batch(po, lse_in, n, kPairR, c, grp, ls, v);
+  {
+    const int wgw = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint16_t* wb = static_cast<const uint16_t*>(p.w) + (static_cast<int64_t>(h) * (p.dn + p.dv) + p.dn) * kPairR;
+    for (int j = wgw; j < p.dv; j += kPairThreads / kWave)
+      dma16(wb + static_cast<int64_t>(j) * kPairR + 8 * lane, lds_addr(g_w) + j * kWRowBytes);
+  }
+  float mg, lg;
+  float4 acc;
+  group_merge(po, lse_in, n, kPairR, c, grp, ls, v, mg, lg, acc);
+  if (grp > 0) grp_all[half][grp - 1][gt] = acc;
+  if (gt == 0) {
+    gm_s[half][grp] = mg;
+    gl_s[half][grp] = lg;
+  }
+  __syncthreads();
+  if (grp == 0) {
+    float4 o;
+    float lse;
+    meet_groups(gm_s[half], gl_s[half], &grp_all[half][0][gt], &grp_all[half][1][gt], &grp_all[half][2][gt], acc, o,
+                lse);
+    if (p.o_lat && real) *reinterpret_cast<float4*>(p.o_lat + bh * kPairR + c) = o;
+    *reinterpret_cast<float4*>(&o_sh[half][c]) = o;
+    if (p.lse && real && gt == 0) p.lse[bh] = lse;
+  }
+  wait_vm<0>();      // this wave's weight copies (and every load) have landed
+  __syncthreads();   // o_sh of both rows and the whole value block are in LDS
+
+  // ---- projection: thread (e, j) sums latent features 64 e .. 64 e + 63 of
+  // output column j for both rows; a wave covers 64 consecutive weight rows
+  // at one feature offset (conflict-free at the 1056-byte row stride)
+  const int T = threadIdx.x;
+  const int e = T / kPairMaxDv, j = T % kPairMaxDv;
+  float a0 = 0.f, a1 = 0.f;
+  if (j < p.dv) {
+    const char* wr = g_w + j * kWRowBytes + e * 128;
+    const float* o0 = &o_sh[0][64 * e];
+    const float* o1 = &o_sh[1][64 * e];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const f32x4 wb = *reinterpret_cast<const f32x4*>(wr + 16 * k);   // 8 bf16
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t wu = __float_as_uint(wb[t]);
+        const float wl = __uint_as_float(wu << 16), wh = __uint_as_float(wu & 0xffff0000u);
+        const int cc = 8 * k + 2 * t;
+        a0 = fmaf(o0[cc], wl, a0);
+        a0 = fmaf(o0[cc + 1], wh, a0);
+        a1 = fmaf(o1[cc], wl, a1);
+        a1 = fmaf(o1[cc + 1], wh, a1);
+      }
+    }
+  }
+  float* psum = reinterpret_cast<float*>(grp_all);   // [kEighths][2][kPairMaxDv] (8 KB of the 12 KB)
+  __syncthreads();   // every half is past its reads of grp_all
+  psum[(e * 2 + 0) * kPairMaxDv + j] = a0;
+  psum[(e * 2 + 1) * kPairMaxDv + j] = a1;
+  __syncthreads();
+  if (T < 2 * kPairMaxDv) {
+    const int row = T / kPairMaxDv, jj = T % kPairMaxDv;
+    const int bo = 2 * blockIdx.y + row;
+    if (jj < p.dv && bo < p.rows) {
+      float sum = 0.f;
+#pragma unroll
+      for (int q = 0; q < kEighths; ++q) sum += psum[(q * 2 + row) * kPairMaxDv + jj];
+      p.ctx[static_cast<int64_t>(bo) * p.heads * p.dv + static_cast<int64_t>(h) * p.dv + jj] = sum;
+    }
+  }
+}
+
 template <typename PT>
 hipError_t launch_combine_t(const CombineParams& p, hipStream_t stream) {
   // whole 4-feature partial groups from aligned bases (16 bytes fp32, 8 bf16)
@@ -272,6 +457,11 @@ hipError_t launch_combine_t(const CombineParams& p, hipStream_t stream) {
       hipLaunchKernelGGL((combine_kernel<PT, true, kVNone>), grid, block, 0, stream, p);
     else
       hipLaunchKernelGGL((combine_kernel<PT, false, kVNone>), grid, block, 0, stream, p);
+    return hipGetLastError();
+  }
+  // the pair kernel: bf16 weights with r = 512, dv <= 128 (16-byte aligned weight rows)
+  if (vec && p.w_dtype == kBF16 && p.r == kPairR && p.dv <= kPairMaxDv && (reinterpret_cast<uintptr_t>(p.w) & 15) == 0) {
+    hipLaunchKernelGGL((combine_v_pair_kernel<PT>), dim3(p.heads, (p.rows + 1) / 2), dim3(kPairThreads), 0, stream, p);
     return hipGetLastError();
   }
   const bool fast = vec && p.w_dtype == kBF16 && p.r % 64 == 0 && p.r / 64 <= kFastLoads &&

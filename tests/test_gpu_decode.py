@@ -424,7 +424,8 @@ def test_merge_of_bf16_partials(fused):
 
 
 @pytest.mark.parametrize("wdt,heads,r,dn,dv,n_splits", [
-    (cf.BF16, 8, 512, 128, 128, (1, 9, 31, 40)),   # bf16 fast path (eight threads per column)
+    (cf.BF16, 8, 512, 128, 128, (1, 9, 31, 40)),   # bf16, r = 512: the row-pair kernel
+    (cf.BF16, 3, 512, 64, 96, (5, 2, 7)),          # row-pair kernel with an odd row count, dv < 128
     (cf.BF16, 3, 448, 32, 64, (5, 2)),              # fast path, r / 64 = 7, one pass of columns
     (cf.BF16, 2, 1024, 16, 40, (3, 12)),            # r beyond the fast path: one thread per column
     (cf.BF16, 2, 512, 128, 192, (4, 6)),            # dv beyond the fast path
