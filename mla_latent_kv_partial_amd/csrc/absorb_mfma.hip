@@ -36,9 +36,9 @@ __device__ __forceinline__ int swz(int d) { return ((d & 3) << 1) ^ (((d >> 3) &
 __shared__ __attribute__((aligned(1024))) char g_wtile[256 * kQCols * 2];   // up to dn = 256 rows
 __shared__ float g_vsum[8][16][kVCols + 1];   // per wave, up to 8 waves
 
-// ROPE: the workgroups' waves also rotate the query's rope part (one wave per
-// (row, head) vector, rope_vector), between issuing the weight-tile copies and
-// waiting for them, so the rotation hides under the copy latency.
+// ROPE: two waves of each workgroup rotate the query's rope part while the
+// other two issue the weight-tile copies, so the rotation hides under the copy
+// latency.
 template <bool ROPE>
 __global__ __launch_bounds__(256) void absorb_q_mfma_kernel(AbsorbQParams p, RopeParams rp) {
   const int lane = threadIdx.x & 63;
@@ -47,21 +47,16 @@ __global__ __launch_bounds__(256) void absorb_q_mfma_kernel(AbsorbQParams p, Rop
   const int h = blockIdx.y;
   const int dn = p.dn;
   const uint16_t* w = static_cast<const uint16_t*>(p.w) + (static_cast<int64_t>(h) * (dn + p.dv)) * p.r + c0;
-  // ---- stage W_UK[h][0..dn)[c0 .. c0+128): position k = 16 d + s holds chunk s ^ swz(d)
-  const int copies = dn * 16 / 64;          // 1 KB each
-  const uint32_t dst = lds_addr(g_wtile);
-  for (int n = wave; n < copies; n += 4) {
-    const int k = 64 * n + lane;
-    const int d = k >> 4, s = k & 15;
-    dma16(w + static_cast<int64_t>(d) * p.r + 8 * (s ^ swz(d)), dst + n * 1024);
-  }
-  // q rows of a 16-row batch block, lane (row m, group g): the first block is
-  // requested right behind the weight copies, so its latency overlaps theirs
+  // Waves 0 and 1 issue the weight-tile copies; with ROPE, waves 2 and 3
+  // rotate the query's rope part meanwhile (one wave per (row, head) vector).
+  // The rotating waves have no copies in flight, so their wait before the
+  // rotated stores (which may alias the loads) covers only their own loads.
   constexpr int kMaxKs = 256 / 32;
   const int m = lane & 15, g = lane >> 4;
   const int nks = dn / 32;
   const uint16_t* q = static_cast<const uint16_t*>(p.q);
   bf16x8 qa[kMaxKs];
+  // q rows of a 16-row batch block, lane (row m, group g)
   auto load_q = [&](int b0) {
     const int b = b0 + m;
 #pragma unroll
@@ -70,11 +65,21 @@ __global__ __launch_bounds__(256) void absorb_q_mfma_kernel(AbsorbQParams p, Rop
         qa[ks] = b < p.batch ? *reinterpret_cast<const bf16x8*>(q + b * p.q_sb + h * p.q_sh + 32 * ks + 8 * g)
                              : bf16x8{};
   };
+  if (wave < 2) {
+    // ---- stage W_UK[h][0..dn)[c0 .. c0+128): position k = 16 d + s holds chunk s ^ swz(d)
+    const int copies = dn * 16 / 64;   // 1 KB each
+    const uint32_t dst = lds_addr(g_wtile);
+    for (int n = wave; n < copies; n += 2) {
+      const int k = 64 * n + lane;
+      const int d = k >> 4, s = k & 15;
+      dma16(w + static_cast<int64_t>(d) * p.r + 8 * (s ^ swz(d)), dst + n * 1024);
+    }
+  }
   load_q(0);
-  if (ROPE) {
+  if (ROPE && wave >= 2) {
     const int64_t vecs = static_cast<int64_t>(rp.rows) * rp.tokens * rp.inner;
-    const int64_t waves = static_cast<int64_t>(gridDim.x) * gridDim.y * 4;
-    for (int64_t v = (static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x) * 4 + wave; v < vecs; v += waves)
+    const int64_t waves = static_cast<int64_t>(gridDim.x) * gridDim.y * 2;
+    for (int64_t v = (static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x) * 2 + (wave - 2); v < vecs; v += waves)
       rope_vector<uint16_t>(rp, v, lane);
   }
   wait_vm<0>();
