@@ -14,20 +14,24 @@ cache).  Per layer the step runs the whole chain through the C ABI:
 The step is captured once in a HIP graph and replayed; W warmup replays, then
 K timed replays between synchronisations.
 
-Printed: one JSON line.  value = rows*layers/s of the step.  roofline = the
-latent attention kernel (the dominant kernel): algorithmic cache bytes per
-launch (attended tokens x 1152 B) / its mean launch time: the attention
-launches of all layers captured alone in a HIP graph (kernels run back to
-back), HIP events around the replays.  traffic = HBM bytes per launch from the
-FETCH_SIZE / WRITE_SIZE counter runs recorded in the committed profile, only
-while the kernel sources still hash to the recorded digest.  stream_probe_* =
-the same bytes streamed with the attention's launch geometry and copy
-schedule and no arithmetic (the floor of that copy path at this shape);
-attn_plus_merge_* = the attention and the merge (fused with absorb_v) per
-layer.  cpu_baseline = the CPU oracle's reconstructed decode on a bounded
-sample of the same rows (and its absorbed form on the same rows).  extra = the
-dense (chained and layer-stacked), DSA (chain, layer-stacked and top-k
-selection), full-layer and prefill workloads.
+Printed: one JSON line.  value = rows*layers/s of the step (ms_per_step_spread:
+p10/p50/p90 of the per-step event timings).  roofline = the latent attention
+kernel (the dominant kernel): algorithmic cache bytes per launch (attended
+tokens x 1152 B) / its mean launch time: the attention launches of all layers
+captured alone in a HIP graph (kernels run back to back), HIP events around
+the replays (on the stream they run on).  traffic = HBM bytes per launch from
+the FETCH_SIZE / WRITE_SIZE counter runs recorded in the committed profile,
+only while the kernel sources still hash to the recorded digest.
+stream_probe_* = the same bytes streamed with the attention's launch geometry
+and copy schedule and no arithmetic (the floor of that copy path at this
+shape).  roofline.k3_k4 = the attention and the merge (fused with absorb_v)
+over the same cache bytes: per layer, and for the ragged layers, 64 dense
+layer instances and 64 DSA selections stacked as the rows of one launch each.
+cpu_baseline = the CPU oracle (reconstructed and absorbed forms) on every
+workload, each on the sample it names (median of 3; one run for the ragged
+rows and the prefill), with the CPU model and thread count.  extra = the
+stacked legs, the dense and DSA chains, the top-k selection, the full layer
+and the prefill legs.
 """
 
 from __future__ import annotations
@@ -175,9 +179,11 @@ def share_partials(layers, torch, dev):
 
 
 def time_graph(torch, fn, steps, warmup, blocks=1):
-    """Capture fn() in a HIP graph; mean ms per replay over `steps` replays
-    (with blocks > 1: the median over `blocks` consecutive timed blocks of
-    `steps` replays each)."""
+    """Capture fn() in a HIP graph and replay it: `warmup` untimed replays, then
+    `blocks` timed blocks of `steps` replays, with a HIP event on the current
+    stream (where the replays run) before every replay and after the last.
+    Returns (ms per replay: the median over the blocks of each block's mean,
+    graph, per-replay samples in ms over all blocks)."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -190,16 +196,26 @@ def time_graph(torch, fn, steps, warmup, blocks=1):
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
-    times = []
+    means, samples = [], []
     for _ in range(blocks):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record()
+        for k in range(steps):
             g.replay()
-        e1.record()
+            ev[k + 1].record()
         torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1) / steps)
-    return sorted(times)[len(times) // 2], g
+        per = [ev[k].elapsed_time(ev[k + 1]) for k in range(steps)]
+        samples += per
+        means.append(ev[0].elapsed_time(ev[steps]) / steps)
+    return sorted(means)[len(means) // 2], g, samples
+
+
+def spread(samples, scale=1.0):
+    """p10 / p50 / p90 of per-replay samples (ms), times `scale`."""
+    import numpy as np
+    a = np.asarray(samples, dtype=np.float64) * scale
+    return {"p10": float(np.percentile(a, 10)), "p50": float(np.percentile(a, 50)),
+            "p90": float(np.percentile(a, 90))}
 
 
 def kernel_sources_digest(names):
@@ -244,41 +260,120 @@ def recorded_traffic(digest):
     return float(m.group(1))
 
 
-def cpu_baseline(cf, oracle, layer0, budget_s=12.0):
-    """The oracle's reconstructed decode (the plain definition) on rows of layer 0
-    of the timed workload, until about `budget_s` seconds of CPU work."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _median(xs):
+    xs = sorted(xs)
+    return xs[len(xs) // 2]
+
+
+def _oracle_decode_args(cf, oracle, inp, rows):
+    """The oracle's arguments for `rows` of a decode workload (exact fp64 values
+    of the stored inputs; the query's rope part rotated by the oracle)."""
+    import numpy as np
+    c = inp.cfg
+    rows = list(rows)
+    q_rope = oracle.rope_partial_interleaved(cf.values(inp.q_rope_raw[rows])[:, None],
+                                             [int(inp.offsets[b]) for b in rows], c.qk_rope, c.theta)[:, 0]
+    sel = None
+    if inp.sel_count is not None:
+        sel = [inp.attended(b) if inp.sel_count[b] > 0 else None for b in rows]
+    return (cf.values(inp.q_nope[rows]), q_rope, cf.values(inp.latent[rows]), cf.values(inp.rope[rows]),
+            cf.values(inp.w_kvb), np.asarray(inp.kv_len)[rows], sel, c.softmax_scale, c.qk_nope, c.v_head)
+
+
+def cpu_baseline(cf, oracle):
+    """The oracle (plain fp64 NumPy, BLAS threads as found) on every workload:
+    decode in rows*layers/s and effective cache GB/s, prefill in GFLOP/s, each
+    in its reconstructed (plain definition) and absorbed forms.  Median of 3
+    runs, one run for the ragged rows and the prefill, each on the sample
+    named in `sample`."""
     import numpy as np
     import threadpoolctl
-    inp = cf.decode_inputs(layer0.cfg, layer=0)
-    c = inp.cfg
-    q_rope = oracle.rope_partial_interleaved(cf.values(inp.q_rope_raw)[:, None], [int(o) for o in inp.offsets],
-                                             c.qk_rope, c.theta)[:, 0]
-    lat, rope, w = cf.values(inp.latent), cf.values(inp.rope), cf.values(inp.w_kvb)
-    q_nope = cf.values(inp.q_nope)
-    order = np.argsort(inp.kv_len)            # shortest rows first keeps the sample bounded
-    rows, tokens, t0 = 0, 0, time.perf_counter()
+    out = {}
+
+    def timed(fn, reps):
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return _median(ts), len(ts)
+
+    def decode_cfg(name, inp, rows, reps, sample):
+        toks = sum(len(inp.attended(b)) for b in rows)
+        res = {"sample": sample, "rows": len(rows), "attended_tokens": toks, "runs": reps}
+        args = _oracle_decode_args(cf, oracle, inp, rows)
+        for form in ("reconstructed", "absorbed"):
+            fn = oracle.decode_reconstructed if form == "reconstructed" else oracle.decode_absorbed
+            dt, n = timed(lambda: fn(*args), reps)
+            res[form] = {"s": dt, "rows_layers_per_s": len(rows) / dt, "cache_GBps": toks * TOKEN_BYTES / dt / 1e9}
+        out[name] = res
+        log(f"cpu baseline {name}: {res['reconstructed']['s']:.2f} s reconstructed, {res['absorbed']['s']:.2f} s absorbed")
+
+    inp = cf.decode_inputs(cf.TINY_F32)
+    decode_cfg("tiny_f32", inp, [0], 3, "the whole workload (1 row, 128 tokens)")
+    inp = cf.decode_inputs(cf.DENSE_BF16)
+    decode_cfg("dense_bf16", inp, [0], 3, "the whole workload (1 row, 4096 tokens)")
+    inp = cf.decode_inputs(cf.DSA_BF16)
+    decode_cfg("dsa_bf16", inp, [0], 3, "the whole workload (1 row, 2048 selected of 131072)")
+    inp.latent = inp.rope = None
+    # ragged rows: rows of layer 0 in a seeded random order, each taken while
+    # the sample stays within 10000 cached tokens (about 15 s of the plain
+    # definition on 16 cores); the rate is also scaled to the whole layer by
+    # its cached tokens (the oracle's cost is linear in the tokens of a row)
+    inp = cf.decode_inputs(cf.RAGGED_BF16, layer=0)
+    order = np.random.default_rng(2026).permutation(len(inp.kv_len))
+    rows, toks = [], 0
     for b in order:
-        oracle.decode_reconstructed(q_nope[b:b + 1], q_rope[b:b + 1], lat[b:b + 1], rope[b:b + 1], w,
-                                    inp.kv_len[b:b + 1], None, c.softmax_scale, c.qk_nope, c.v_head)
-        rows += 1
-        tokens += int(inp.kv_len[b])
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
-    # the absorbed form (q_lat = W_UK^T q_nope, attention over latent||rope,
-    # W_UV o_lat) on the same rows, fp64
-    ta = time.perf_counter()
-    for b in order[:rows]:
-        oracle.decode_absorbed(q_nope[b:b + 1], q_rope[b:b + 1], lat[b:b + 1], rope[b:b + 1], w,
-                               inp.kv_len[b:b + 1], None, c.softmax_scale, c.qk_nope, c.v_head)
-    dta = time.perf_counter() - ta
+        if toks + int(inp.kv_len[b]) <= 10000:
+            rows.append(int(b))
+            toks += int(inp.kv_len[b])
+    if not rows:
+        rows, toks = [int(np.argmin(inp.kv_len))], int(np.min(inp.kv_len))
+    layer_toks = int(np.sum(inp.kv_len))
+    decode_cfg("ragged_bf16", inp, rows, 1,
+               f"rows {rows} of layer 0 ({toks} of its {layer_toks} cached tokens; rows in a seeded random order, "
+               f"each taken while the sample stays within 10000 tokens)")
+    for form in ("reconstructed", "absorbed"):
+        r = out["ragged_bf16"][form]
+        r["layer_rows_layers_per_s"] = len(inp.kv_len) / (r["s"] * layer_toks / toks)
+    inp = None
+    # prefill: every key expanded, 64 query rows drawn at random (seeded)
+    pc = cf.PREFILL_BF16
+    pin = cf.prefill_inputs(pc)
+    qrows = np.sort(np.random.default_rng(2027).choice(pc.tokens, size=64, replace=False))
+    rr = oracle.rope_partial_interleaved(cf.values(pin.k_rope_raw), 0, pc.qk_rope, pc.theta)
+    args = (cf.values(pin.c_q), cf.values(pin.w_qb), cf.values(pin.latent), rr, cf.values(pin.w_kvb), pin.q_offsets,
+            pc.theta, None, pc.softmax_scale, pc.heads, pc.qk_nope, pc.qk_rope, pc.v_head)
+    dt, _ = timed(lambda: oracle.prefill_reconstructed(*args, query_rows=qrows), 1)
+    h, t, k = pc.heads, len(qrows), pc.keys
+    flops = (2 * t * pc.q_lora_rank * h * (pc.qk_nope + pc.qk_rope) + 2 * k * pc.kv_lora_rank * h * (pc.qk_nope + pc.v_head)
+             + 2 * h * int(np.sum(qrows + 1)) * (pc.qk_nope + pc.qk_rope + pc.v_head))
+    out["prefill_bf16"] = {"sample": f"64 query rows of 4096 drawn at random, all {k} keys expanded", "runs": 1,
+                           "reconstructed": {"s": dt, "GFLOPs": flops / dt / 1e9, "algorithmic_GFLOP": flops / 1e9}}
+    log(f"cpu baseline prefill: {dt:.2f} s")
     threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
+    r = out["ragged_bf16"]
     return {
-        "value": rows / dt, "unit": "rows*layers/s", "cores": int(threads), "kind": "oracle",
-        "sample": f"reconstructed fp64 decode of {rows} row(s) of layer 0 ({tokens} cached tokens) in {dt:.1f}s",
-        "cache_GBps": tokens * TOKEN_BYTES / dt / 1e9,
-        "absorbed_value": rows / dta, "absorbed_cache_GBps": tokens * TOKEN_BYTES / dta / 1e9,
-        "host_cpus": len(os.sched_getaffinity(0)),
+        "value": r["reconstructed"]["layer_rows_layers_per_s"], "unit": "rows*layers/s", "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"ragged_bf16: {r['sample']}; reconstructed fp64 decode in {r['reconstructed']['s']:.1f} s, scaled "
+                  f"to the whole 8-row layer by cached tokens",
+        "cache_GBps": r["reconstructed"]["cache_GBps"],
+        "absorbed_value": r["absorbed"]["layer_rows_layers_per_s"],
+        "cpu_model": cpu_model(), "host_cpus": len(os.sched_getaffinity(0)),
+        "configs": out,
     }
 
 
@@ -364,39 +459,46 @@ def main():
         for ly in layers:
             ly.step(mla)
 
-    ms_step, _ = time_graph(torch, step, args.steps, args.warmup)
+    ms_step, _, step_samples = time_graph(torch, step, args.steps, args.warmup)
     cache_bytes = sum(ly.cache_bytes for ly in layers)
     log(f"step {ms_step:.3f} ms  ({cache_bytes / 1e6:.0f} MB of cache per step)")
+    nl = len(layers)
 
     # dominant kernel: latent attention alone, one launch per layer captured in
     # a graph (back-to-back kernels, no host gaps), events around the replays
-    ms_attn = time_graph(torch, lambda: [ly.attn(mla) for ly in layers], args.steps, args.warmup,
-                         blocks=3)[0] / len(layers)
-    per_launch_bytes = cache_bytes / len(layers)
+    ms_attn, _, attn_samples = time_graph(torch, lambda: [ly.attn(mla) for ly in layers], args.steps, args.warmup,
+                                          blocks=3)
+    ms_attn /= nl
+    per_launch_bytes = cache_bytes / nl
     achieved = per_launch_bytes / (ms_attn * 1e-3) / 1e9
     log(f"attention {ms_attn * 1e3:.1f} us/launch  {achieved:.0f} GB/s")
     # the streaming probe: the same bytes, launch geometry and copy schedule,
     # no arithmetic and no partials
     ms_probe = time_graph(torch, lambda: [mla.mla_decode_stream_probe(ly.latent, ly.rope, ly.kv_len, ly.chunk)
-                                          for ly in layers], args.steps, args.warmup, blocks=3)[0] / len(layers)
+                                          for ly in layers], args.steps, args.warmup, blocks=3)[0] / nl
     probe_gbps = per_launch_bytes / (ms_probe * 1e-3) / 1e9
     log(f"stream probe {ms_probe * 1e3:.1f} us/launch  {probe_gbps:.0f} GB/s")
-    # attention + merge (the merge fused with absorb_v, as in the step)
+    # attention + merge (the merge fused with absorb_v, as in the step): the
+    # pair the latent-cache bandwidth target is judged on
     def attn_merge():
         for ly in layers:
             ly.attn(mla)
             mla.mla_decode_combine_v(ly.part_o, ly.part_lse, ly.n_splits, ly.w, ly.cfg.qk_nope, ly.cfg.v_head,
                                      ctx=ly.ctx)
-    ms_am = time_graph(torch, attn_merge, args.steps, args.warmup)[0] / len(layers)
+    ms_am, _, am_samples = time_graph(torch, attn_merge, args.steps, args.warmup, blocks=3)
+    ms_am /= nl
+    am_gbps = per_launch_bytes / (ms_am * 1e-3) / 1e9
+    log(f"attention + merge {ms_am * 1e3:.1f} us/layer  {am_gbps:.0f} GB/s")
 
     result = {
         "metric": "MLA decode rows*layers/s and achieved latent-cache HBM GB/s (% of peak)",
-        "value": rows * len(layers) / (ms_step * 1e-3),
+        "value": rows * nl / (ms_step * 1e-3),
         "unit": "rows*layers/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "ms_per_step_spread": spread(step_samples),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -405,30 +507,62 @@ def main():
         "config": {
             "workload": "ragged_bf16 decode: B=8, H=64, qk_nope=128, qk_rope=64, v_head=128, kv_lora_rank=512, "
                         "lengths U{1024..32768}, 1 query token, bf16 cache, fp32 accumulate",
-            "layers": len(layers), "rows": rows, "cache_MB_per_step": cache_bytes / 1e6,
+            "layers": nl, "rows": rows, "cache_MB_per_step": cache_bytes / 1e6,
             "step_GBps_cache": cache_bytes / (ms_step * 1e-3) / 1e9,
-            "chain": "decode_query (absorb_q + q RoPE, one launch) -> latent_attn -> combine_v (combine + "
-                     "absorb_v, one launch) per layer, HIP graph",
+            "chain": "decode_query (absorb_q + q RoPE, one launch) -> latent_attn (bf16 split partials) -> "
+                     "combine_v (combine + absorb_v, one launch) per layer, HIP graph",
         },
         "roofline": {
             "kernel": "mla_decode_latent_attn (decode_mfma_kernel)",
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(kernel_sources_digest(ATTN_SOURCES)),
             "per_launch_bytes": per_launch_bytes, "launch_us": ms_attn * 1e3,
+            "launch_us_spread": spread(attn_samples, 1e3 / nl),
             "stream_probe_us": ms_probe * 1e3, "stream_probe_GBps": probe_gbps,
             "frac_of_stream_probe": achieved / probe_gbps,
-            "attn_plus_merge_us": ms_am * 1e3, "attn_plus_merge_GBps": per_launch_bytes / (ms_am * 1e-3) / 1e9,
+            # the attention and the merge (K3 + K4) over the same cache bytes
+            "k3_k4": {"per_layer": {"us": ms_am * 1e3, "us_spread": spread(am_samples, 1e3 / nl),
+                                    "GBps": am_gbps, "frac": am_gbps / HBM_PEAK_GBS,
+                                    "frac_of_stream_probe": am_gbps / probe_gbps}},
             "sources_sha256": kernel_sources_digest(ATTN_SOURCES),
         },
     }
+    k3k4 = result["roofline"]["k3_k4"]
 
     # ------------------------------------------------------------- extras
     if not args.no_extra:
         extra = {}
+
+        def stacked_leg(q_lat, q_rope, latent, rope, lens, w, cfg_, sel_idx=None, sel_count=None):
+            """One launch of the attention over all the rows, then (a second
+            graph) the attention and the merge + projection of those rows."""
+            n_att = [c if sel_count is not None and c > 0 else n
+                     for n, c in zip(lens, sel_count or [-1] * len(lens))]
+            chunk = mla.plan_chunk_len(n_att, slots)
+            ns = [mla.split_count(n, chunk) for n in n_att]
+            po = torch.empty((len(lens), cfg_.heads, max(ns), cfg_.kv_lora_rank), dtype=torch.bfloat16, device=dev)
+            pl = torch.empty((len(lens), cfg_.heads, max(ns)), dtype=torch.float32, device=dev)
+            ctx = torch.empty((len(lens), cfg_.heads * cfg_.v_head), dtype=torch.float32, device=dev)
+            attn = lambda: mla.mla_decode_latent_attn(q_lat, q_rope, latent, rope, lens, cfg_.softmax_scale, chunk,
+                                                      sel_idx=sel_idx, sel_count=sel_count, part_o=po, part_lse=pl,
+                                                      s_max=max(ns))
+            ms_a, _, sa = time_graph(torch, attn, args.steps, args.warmup, blocks=3)
+            def both():
+                attn()
+                mla.mla_decode_combine_v(po, pl, ns, w, cfg_.qk_nope, cfg_.v_head, ctx=ctx)
+            ms_b, _, sb = time_graph(torch, both, args.steps, args.warmup, blocks=3)
+            byts = sum(n_att) * TOKEN_BYTES
+            return {"rows": len(lens), "chunk": chunk, "splits": sum(ns), "cache_MB": byts / 1e6,
+                    "attn_us": ms_a * 1e3, "attn_us_spread": spread(sa, 1e3),
+                    "attn_GBps": byts / (ms_a * 1e-3) / 1e9, "attn_frac_hbm": byts / (ms_a * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "k3_k4_us": ms_b * 1e3, "k3_k4_us_spread": spread(sb, 1e3),
+                    "k3_k4_GBps": byts / (ms_b * 1e-3) / 1e9,
+                    "k3_k4_frac_hbm": byts / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
         # the ragged workload's 8 layer instances as the 64 rows of one launch:
-        # the same kernel with its per-launch costs (dispatch, first tiles,
-        # partial burst, kernel boundary) spread over 1351 MB; a model's
-        # layers run one after the other, so this is not the step's figure
+        # the same kernels with their per-launch costs (dispatch, first tiles,
+        # partial burst, kernel boundary) spread over 1351 MB; a model's layers
+        # run one after the other, so this is kernel throughput, not the step
         wmax = max(ly.cache.shape[1] for ly in layers)
         rows_all = sum(ly.cache.shape[0] for ly in layers)
         rs = torch.empty((rows_all, wmax, cfg.kv_lora_rank + cfg.qk_rope), dtype=torch.bfloat16, device=dev)
@@ -439,18 +573,12 @@ def main():
         r_lens = [n for ly in layers for n in ly.kv_len]
         r_q_lat = torch.cat([ly.q_lat for ly in layers], dim=0)
         r_q_rope = torch.cat([ly.q_rope for ly in layers], dim=0)
-        r_chunk = mla.plan_chunk_len(r_lens, slots)
-        r_ns = [mla.split_count(n, r_chunk) for n in r_lens]
-        r_po = torch.empty((rows_all, cfg.heads, max(r_ns), cfg.kv_lora_rank), dtype=torch.bfloat16, device=dev)
-        r_pl = torch.empty((rows_all, cfg.heads, max(r_ns)), dtype=torch.float32, device=dev)
-        ms_r = time_graph(torch, lambda: mla.mla_decode_latent_attn(
-            r_q_lat, r_q_rope, rs[..., :cfg.kv_lora_rank], rs[..., cfg.kv_lora_rank:], r_lens, cfg.softmax_scale,
-            r_chunk, part_o=r_po, part_lse=r_pl, s_max=max(r_ns)), args.steps, args.warmup, blocks=3)[0]
-        extra["ragged_stacked_attn"] = {"rows": rows_all, "chunk": r_chunk, "splits": sum(r_ns),
-                                        "launch_us": ms_r * 1e3, "cache_MB": cache_bytes / 1e6,
-                                        "cache_GBps": cache_bytes / (ms_r * 1e-3) / 1e9,
-                                        "frac_hbm": cache_bytes / (ms_r * 1e-3) / 1e9 / HBM_PEAK_GBS}
-        del rs, r_q_lat, r_q_rope, r_po, r_pl
+        extra["ragged_stacked"] = stacked_leg(r_q_lat, r_q_rope, rs[..., :cfg.kv_lora_rank], rs[..., cfg.kv_lora_rank:],
+                                              r_lens, layers[0].w, cfg)
+        k3k4["stacked_ragged"] = {k: extra["ragged_stacked"][k] for k in ("k3_k4_us", "k3_k4_GBps", "k3_k4_frac_hbm")}
+        log(f"stacked ragged: attn {extra['ragged_stacked']['attn_us']:.1f} us, attn + merge "
+            f"{extra['ragged_stacked']['k3_k4_us']:.1f} us")
+        del rs, r_q_lat, r_q_rope
         torch.cuda.empty_cache()
         # dense workload, 64 layer instances: chained (one graph) and stacked (one launch, 64 rows)
         dcfg = cf.DENSE_BF16
@@ -459,63 +587,51 @@ def main():
         for ly in dl:
             ly.plan(mla, slots, torch, dev)
         share_partials(dl, torch, dev)
-        ms_d, _ = time_graph(torch, lambda: [ly.step(mla) for ly in dl], args.steps, args.warmup)
+        ms_d, _, _ = time_graph(torch, lambda: [ly.step(mla) for ly in dl], args.steps, args.warmup)
         extra["dense_chained"] = {"layers": n_dense, "ms_per_step": ms_d,
                                   "rows_layers_per_s": n_dense / (ms_d * 1e-3),
                                   "cache_GBps": sum(ly.cache_bytes for ly in dl) / (ms_d * 1e-3) / 1e9}
         stacked = torch.cat([ly.cache for ly in dl], dim=0)          # [64, 4096, 576]
         q_lat = torch.cat([ly.q_lat for ly in dl], dim=0)
         q_rope = torch.cat([ly.q_rope for ly in dl], dim=0)
-        lens = [dcfg.tokens] * n_dense
-        chunk = mla.plan_chunk_len(lens, slots)
-        ns = [mla.split_count(n, chunk) for n in lens]
-        po = torch.empty((n_dense, dcfg.heads, max(ns), dcfg.kv_lora_rank), dtype=torch.bfloat16, device=dev)
-        pl = torch.empty((n_dense, dcfg.heads, max(ns)), dtype=torch.float32, device=dev)
-        ms_s = time_graph(torch, lambda: mla.mla_decode_latent_attn(
-            q_lat, q_rope, stacked[..., :512], stacked[..., 512:], lens, dcfg.softmax_scale, chunk, part_o=po,
-            part_lse=pl, s_max=max(ns)), args.steps, args.warmup)[0]
-        sb = n_dense * dcfg.tokens * TOKEN_BYTES
-        extra["dense_stacked_attn"] = {"rows": n_dense, "chunk": chunk, "launch_us": ms_s * 1e3,
-                                       "cache_GBps": sb / (ms_s * 1e-3) / 1e9,
-                                       "frac_hbm": sb / (ms_s * 1e-3) / 1e9 / HBM_PEAK_GBS}
-        del dl, stacked, q_lat, q_rope, po, pl
+        extra["dense_stacked"] = stacked_leg(q_lat, q_rope, stacked[..., :512], stacked[..., 512:],
+                                             [dcfg.tokens] * n_dense, dl[0].w, dcfg)
+        k3k4["stacked_dense"] = {k: extra["dense_stacked"][k] for k in ("k3_k4_us", "k3_k4_GBps", "k3_k4_frac_hbm")}
+        del dl, stacked, q_lat, q_rope
         torch.cuda.empty_cache()
         # DSA workload, 8 layer instances (each 131072-token cache, 2048 selected)
+        import numpy as np
         scfg = cf.DSA_BF16
         sl = [DecodeLayer(scfg, l, torch, cf, dev) for l in range(args.layers)]
         for ly in sl:
             ly.plan(mla, slots, torch, dev)
         share_partials(sl, torch, dev)
-        ms_dsa, _ = time_graph(torch, lambda: [ly.step(mla) for ly in sl], args.steps, args.warmup)
+        ms_dsa, _, _ = time_graph(torch, lambda: [ly.step(mla) for ly in sl], args.steps, args.warmup)
         ms_dsa_attn = time_graph(torch, lambda: [ly.attn(mla) for ly in sl], args.steps, args.warmup)[0] / len(sl)
         gb = scfg.selected * TOKEN_BYTES
         extra["dsa_chained"] = {"layers": len(sl), "ms_per_step": ms_dsa,
                                 "rows_layers_per_s": len(sl) / (ms_dsa * 1e-3),
                                 "attn_launch_us": ms_dsa_attn * 1e3,
                                 "gathered_GBps": gb / (ms_dsa_attn * 1e-3) / 1e9}
-        # layer-stacked: the layers' selections as rows of one launch
-        st_cache = torch.cat([ly.cache for ly in sl], dim=0)
-        st_q_lat = torch.cat([ly.q_lat for ly in sl], dim=0)
-        st_q_rope = torch.cat([ly.q_rope for ly in sl], dim=0)
-        st_sel = torch.cat([ly.sel for ly in sl], dim=0)
-        st_len = [n for ly in sl for n in ly.kv_len]
-        st_cnt = [c for ly in sl for c in ly.sel_count]
-        st_chunk = mla.plan_chunk_len(st_cnt, slots)
-        st_ns = [mla.split_count(c, st_chunk) for c in st_cnt]
-        st_po = torch.empty((len(st_len), scfg.heads, max(st_ns), scfg.kv_lora_rank), dtype=torch.bfloat16,
-                            device=dev)
-        st_pl = torch.empty((len(st_len), scfg.heads, max(st_ns)), dtype=torch.float32, device=dev)
-        ms_dst = time_graph(torch, lambda: mla.mla_decode_latent_attn(
-            st_q_lat, st_q_rope, st_cache[..., :512], st_cache[..., 512:], st_len, scfg.softmax_scale, st_chunk,
-            sel_idx=st_sel, sel_count=st_cnt, part_o=st_po, part_lse=st_pl, s_max=max(st_ns)),
-            args.steps, args.warmup)[0]
-        extra["dsa_stacked_attn"] = {"rows": len(st_len), "chunk": st_chunk, "launch_us": ms_dst * 1e3,
-                                     "gathered_GBps": len(st_len) * gb / (ms_dst * 1e-3) / 1e9}
-        del sl, st_cache, st_q_lat, st_q_rope, st_sel, st_po, st_pl
+        # layer-stacked: 64 selections of 2048 (fresh sorted indices) as the rows
+        # of one launch, row r over the 131072-token window that starts r/16 of
+        # a cache into the 8 caches laid end to end (rows overlap; the 64 x 2048
+        # gathered tokens, 151 MB, come from 5 caches, beyond the last-level cache)
+        from synth import generators as gen
+        n_sel_rows = 64
+        st_cache = torch.cat([ly.cache for ly in sl], dim=0)            # [8, W, 576]
+        wd = scfg.tokens
+        win = torch.as_strided(st_cache, (n_sel_rows, wd, 576), (wd * 576 // 16, 576, 1))
+        st_q_lat = torch.cat([ly.q_lat for ly in sl] * (n_sel_rows // len(sl)), dim=0)
+        st_q_rope = torch.cat([ly.q_rope for ly in sl] * (n_sel_rows // len(sl)), dim=0)
+        st_sel = torch.from_numpy(np.concatenate([gen.dsa_positions(scfg.config_id, wd, scfg.selected, layer=100 + r)
+                                                  for r in range(n_sel_rows)])).to(dev)
+        extra["dsa_stacked"] = stacked_leg(st_q_lat, st_q_rope, win[..., :512], win[..., 512:], [wd] * n_sel_rows,
+                                           sl[0].w, scfg, sel_idx=st_sel, sel_count=[scfg.selected] * n_sel_rows)
+        k3k4["stacked_dsa"] = {k: extra["dsa_stacked"][k] for k in ("k3_k4_us", "k3_k4_GBps", "k3_k4_frac_hbm")}
+        del sl, st_cache, win, st_q_lat, st_q_rope, st_sel
         torch.cuda.empty_cache()
         # DSA top-k selection over the 131072-token context (synthetic fp32 scores)
-        import numpy as np
-        from synth import generators as gen
         n_ctx, k_sel = scfg.tokens, scfg.selected
         scores = torch.from_numpy(gen.normal_f32(scfg.config_id, gen.T_DSA_SCORES, (args.layers, n_ctx))).to(dev)
         sel_buf = torch.empty(args.layers * k_sel, dtype=torch.int32, device=dev)
@@ -540,7 +656,7 @@ def main():
             ly.plan(mla, slots, torch, dev)
             ly.full_layer_setup(torch, cf, dev, hidden=6144)
         share_partials(fl, torch, dev)
-        ms_full, _ = time_graph(torch, lambda: [ly.full_step(mla) for ly in fl], args.steps, args.warmup)
+        ms_full, _, _ = time_graph(torch, lambda: [ly.full_step(mla) for ly in fl], args.steps, args.warmup)
         ms_oproj = time_graph(torch, lambda: [mla.mla_o_proj(ly.ctx, ly.w_o, out=ly.out) for ly in fl],
                               args.steps, args.warmup)[0] / len(fl)
         extra["decode_full_layer"] = {
@@ -566,7 +682,7 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         log("cpu baseline: oracle")
-        result["cpu_baseline"] = cpu_baseline(cf, oracle, layers[0])
+        result["cpu_baseline"] = cpu_baseline(cf, oracle)
 
     print(json.dumps(result), flush=True)
 
