@@ -446,6 +446,154 @@ __global__ __launch_bounds__(kPairThreads) void combine_v_pair_kernel(CombinePar
   }
 }
 
+// ---- The fused merge + projection for many rows (bf16 weights, r = 512,
+// v_head <= 128): one workgroup of 16 waves per (head, block of 16 rows).
+// The pair kernel fetches a head's value block once per two rows, which at
+// 64 rows and more is 32+ fetches of each block through L2; here each block
+// serves 16 rows.  Wave w merges row b0 + w alone (lane l owns latent
+// features 8 l .. 8 l + 7), batches of 8 splits with all their loads in
+// flight: rows of a many-row launch hold few splits each.  The merged rows go
+// to LDS in fp32; the projection runs on MFMA with the merged row as a bf16
+// high part plus a bf16 residual (~16 significant bits), wave (nt, kh)
+// taking output columns 16 nt .. 16 nt + 15 over latent half kh, its weight
+// fragments requested at entry so that they arrive during the merge.
+constexpr int kRowsBlock = 16;
+constexpr int kRowsThreads = kRowsBlock * kWave;
+constexpr int kRowsBatch = 8;                      // splits per batch of loads
+constexpr int kRowsStride = kPairR * 4 + 32;       // merged row in LDS: an odd number of 32-byte units
+constexpr int kRowsMin = 16;                       // fewest rows that take this kernel
+
+// eight consecutive partial features as fp32
+__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ void load8(const uint16_t* p, float (&x)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+template <typename PT>
+__global__ __launch_bounds__(kRowsThreads) void combine_v_rows_kernel(CombineParams p) {
+  __shared__ __attribute__((aligned(16))) char o_sh[kRowsBlock * kRowsStride];
+  __shared__ float psum[kRowsBlock][kPairMaxDv];
+  const int h = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int m = lane & 15, g = lane >> 4;
+  const int b0 = blockIdx.y * kRowsBlock;
+
+  // this wave's projection tile and its weight fragments (B[k][n] = W_UV[h][16 nt + n][k])
+  const int nt = wave & 7, kh = wave >> 3;
+  const bool proj = 16 * nt < p.dv;
+  bf16x8 bw[8];
+  if (proj) {
+    const int col = min(16 * nt + m, p.dv - 1);   // columns past dv re-read the last one (never stored)
+    const uint16_t* wr = static_cast<const uint16_t*>(p.w) +
+                         (static_cast<int64_t>(h) * (p.dn + p.dv) + p.dn + col) * kPairR + 256 * kh + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) bw[ks] = *reinterpret_cast<const bf16x8*>(wr + 32 * ks);
+  }
+
+  // ---- merge row b0 + wave
+  const int b = b0 + wave;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float M = -INFINITY, L = 0.f;
+  if (b < p.rows) {
+    const int n = p.n_splits[b];
+    const int64_t bh = static_cast<int64_t>(b) * p.heads + h;
+    const float* lse_in = p.part_lse + bh * p.s_max;
+    const PT* po = static_cast<const PT*>(p.part_o) + bh * p.s_max * kPairR + 8 * lane;
+    for (int s0 = 0; s0 < n; s0 += kRowsBatch) {
+      float ls[kRowsBatch], v[kRowsBatch][8];
+#pragma unroll
+      for (int u = 0; u < kRowsBatch; ++u) {
+        const int sc = min(s0 + u, n - 1);   // splits past n re-read the last one, weight 0
+        ls[u] = lse_in[sc];
+        load8(po + static_cast<int64_t>(sc) * kPairR, v[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kRowsBatch; ++u)
+        if (s0 + u >= n) ls[u] = -INFINITY;
+      float bm = ls[0];
+#pragma unroll
+      for (int u = 1; u < kRowsBatch; ++u) bm = fmaxf(bm, ls[u]);
+      const float mn = fmaxf(M, bm);
+      if (mn == -INFINITY) continue;   // no token in these splits yet
+      const float rs = weight_of(M, mn);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] *= rs;
+      L *= rs;
+      M = mn;
+#pragma unroll
+      for (int u = 0; u < kRowsBatch; ++u) {
+        const float w = weight_of(ls[u], M);
+        L += w;
+        if (w != 0.f) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[u][i], acc[i]);
+        }
+      }
+    }
+    float lse = -INFINITY;
+    if (M != -INFINITY) {
+      const float inv = 1.f / L;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] *= inv;
+      lse = M + logf(L);
+    }
+    if (p.o_lat) {
+      float* ol = p.o_lat + bh * kPairR + 8 * lane;
+      *reinterpret_cast<float4*>(ol) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      *reinterpret_cast<float4*>(ol + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+    if (p.lse && lane == 0) p.lse[bh] = lse;
+  }
+  // rows past the launch stay zero: their projections are never stored
+  float* orow = reinterpret_cast<float*>(o_sh + wave * kRowsStride) + 8 * lane;
+  *reinterpret_cast<float4*>(orow) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  *reinterpret_cast<float4*>(orow + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  __syncthreads();
+
+  // ---- projection: ctx[b0 + row][16 nt + n] over latent half kh
+  f32x4 c = {0.f, 0.f, 0.f, 0.f};
+  if (proj) {
+    const float* arow = reinterpret_cast<const float*>(o_sh + m * kRowsStride) + 256 * kh + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const float4 u = *reinterpret_cast<const float4*>(arow + 32 * ks);
+      const float4 v = *reinterpret_cast<const float4*>(arow + 32 * ks + 4);
+      const bf16x8 hi = to_bf16x8(u, v);
+      const float4 ru = make_float4(u.x - static_cast<float>(hi[0]), u.y - static_cast<float>(hi[1]),
+                                    u.z - static_cast<float>(hi[2]), u.w - static_cast<float>(hi[3]));
+      const float4 rv = make_float4(v.x - static_cast<float>(hi[4]), v.y - static_cast<float>(hi[5]),
+                                    v.z - static_cast<float>(hi[6]), v.w - static_cast<float>(hi[7]));
+      c = mfma16x16x32(hi, bw[ks], c);
+      c = mfma16x16x32(to_bf16x8(ru, rv), bw[ks], c);
+    }
+    if (kh == 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) psum[4 * g + i][16 * nt + m] = c[i];
+    }
+  }
+  __syncthreads();
+  if (proj && kh == 0) {
+    const int col = 16 * nt + m;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int bo = b0 + 4 * g + i;
+      if (bo < p.rows && col < p.dv)
+        p.ctx[static_cast<int64_t>(bo) * p.heads * p.dv + static_cast<int64_t>(h) * p.dv + col] =
+            c[i] + psum[4 * g + i][col];
+    }
+  }
+}
+
 template <typename PT>
 hipError_t launch_combine_t(const CombineParams& p, hipStream_t stream) {
   // whole 4-feature partial groups from aligned bases (16 bytes fp32, 8 bf16)
@@ -461,7 +609,11 @@ hipError_t launch_combine_t(const CombineParams& p, hipStream_t stream) {
   }
   // the pair kernel: bf16 weights with r = 512, dv <= 128 (16-byte aligned weight rows)
   if (vec && p.w_dtype == kBF16 && p.r == kPairR && p.dv <= kPairMaxDv && (reinterpret_cast<uintptr_t>(p.w) & 15) == 0) {
-    hipLaunchKernelGGL((combine_v_pair_kernel<PT>), dim3(p.heads, (p.rows + 1) / 2), dim3(kPairThreads), 0, stream, p);
+    if (p.rows >= kRowsMin)
+      hipLaunchKernelGGL((combine_v_rows_kernel<PT>), dim3(p.heads, (p.rows + kRowsBlock - 1) / kRowsBlock),
+                         dim3(kRowsThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((combine_v_pair_kernel<PT>), dim3(p.heads, (p.rows + 1) / 2), dim3(kPairThreads), 0, stream, p);
     return hipGetLastError();
   }
   const bool fast = vec && p.w_dtype == kBF16 && p.r % 64 == 0 && p.r / 64 <= kFastLoads &&

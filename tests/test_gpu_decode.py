@@ -460,6 +460,47 @@ def test_combine_v_direct_partials(wdt, heads, r, dn, dv, n_splits):
     assert_close(got, ctx_ref, cf.F32, "fused ctx", tol=1e-5)
 
 
+@pytest.mark.parametrize("pdt,rows,heads,dv,max_splits", [
+    (cf.F32, 37, 8, 128, 20),    # 16-row blocks with a ragged last block; batches of 8 splits and a tail
+    (cf.BF16, 64, 16, 96, 6),    # bf16 partials, dv < 128 (columns past dv idle in the projection)
+    (cf.BF16, 16, 4, 128, 1),    # one split per row, the fewest rows that take the many-row kernel
+])
+def test_combine_v_many_rows(pdt, rows, heads, dv, max_splits):
+    """The fused merge + projection of a many-row launch (one workgroup per
+    head and 16 rows) against the oracle: empty splits with NaN partials,
+    a (row, head) with no split, split counts spanning several batches."""
+    mla = _mla()
+    r, dn = 512, 128
+    n_splits = [int(v) for v in np.random.default_rng(rows).integers(1, max_splits, size=rows, endpoint=True)]
+    s_max = max(n_splits)
+    say(f"combine_v many rows: {pdt} rows={rows} heads={heads} dv={dv} s_max={s_max}")
+    po = gen.normal_f32(96, 1, (rows, heads, s_max, r))
+    pl = 3.0 * gen.normal_f32(96, 2, (rows, heads, s_max))
+    empty = np.random.default_rng(13).random((rows, heads, s_max)) < 0.2
+    empty[0, 0, :] = True
+    pl[empty] = -np.inf
+    po_store = cf.store(po, pdt)
+    po_gpu = dev(po_store)
+    po_gpu[torch.from_numpy(empty).to(po_gpu.device)] = float("nan")
+    w = cf.store(gen.normal_f32(96, 3, (heads * (dn + dv), r), std=r ** -0.5), cf.BF16)
+    o_lat = torch.empty((rows, heads, r), dtype=torch.float32, device="cuda")
+    lse = torch.empty((rows, heads), dtype=torch.float32, device="cuda")
+    ctx = mla.mla_decode_combine_v(po_gpu, dev(pl), n_splits, dev(w), dn, dv, o_lat=o_lat, lse=lse)
+    o_sep, lse_sep = mla.mla_decode_combine(po_gpu, dev(pl), n_splits)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.combine_partials(np.where(empty[..., None], 0.0, cf.values(po_store)), pl, n_splits)
+    ctx_ref = oracle.absorb_v(o_ref, cf.values(w), dn, dv)
+    got = host_values(ctx)
+    assert not np.isnan(got).any()
+    assert np.array_equal(got[0, :dv], np.zeros(dv))   # row 0, head 0: no split, o = 0
+    assert_close(host_values(o_lat), o_ref, cf.F32, "many-row merge o_lat", tol=1e-5)
+    assert_close(host_values(o_lat), host_values(o_sep), cf.F32, "many-row merge vs combine", tol=1e-6)
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(host_values(lse)), fin)
+    assert np.allclose(host_values(lse)[fin], lse_ref[fin], rtol=0, atol=1e-5)
+    assert_close(got, ctx_ref, cf.F32, "many-row ctx", tol=1e-5)
+
+
 def test_stream_probe_runs_and_writes_nothing():
     """The attention's streaming probe reads the ragged rows' cache and leaves it as it was."""
     mla = _mla()
