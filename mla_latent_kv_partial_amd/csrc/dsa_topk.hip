@@ -26,8 +26,9 @@
 //
 // Two-stage form for rows of 2 to 8 segments of 16384 scores (the 131072-
 // score rows of a long context), in two launches with a caller workspace:
-//   A. one workgroup per (row, segment): the segment's keys go to LDS, the
-//      same radix select finds the segment's top_k under the page's order
+//   A. one workgroup per (row, segment): the segment's keys go to LDS, a
+//      select (by score buckets, below; the radix select when the buckets do
+//      not separate the keys) finds the segment's top_k under the page's order
 //      (key, then position), and an order-keeping compaction writes those
 //      top_k (key, position) pairs to the workspace in ascending position
 //      order.  A position the whole row selects has fewer than top_k
@@ -66,6 +67,53 @@ __device__ __forceinline__ int lanes_below(uint64_t ballot) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(ballot), 0u));
 }
 
+// Cross-lane steps on the VALU (DPP and the gfx950 lane swaps) instead of
+// lane shuffles through ds_bpermute, which wait on LDS latency at every step.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ uint32_t dpp_zero(uint32_t v) {   // lanes without a source read 0
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROWS, 0xf, true));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_self(uint32_t v) {   // every lane has a source in these patterns
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), CTRL, 0xf, 0xf,
+                                                           false));
+}
+
+// Inclusive prefix sum over the wave's 64 lanes: shifts by 1, 2, 4 and 8 lanes
+// inside each row of 16, then row 0's total into row 1 and row 2's into row 3
+// (row_bcast:15), then the first half's total into rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
+  v += dpp_zero<0x111>(v);
+  v += dpp_zero<0x112>(v);
+  v += dpp_zero<0x114>(v);
+  v += dpp_zero<0x118>(v);
+  v += dpp_zero<0x142, 0xa>(v);
+  v += dpp_zero<0x143, 0xc>(v);
+  return v;
+}
+
+// Minimum and maximum over the wave (every lane receives both): lane pairs
+// i ^ 1 and i ^ 2 (quad permutes), then the mirrors inside 8 and 16 lanes,
+// then the 16- and 32-lane swaps.
+__device__ __forceinline__ void wave_min_max(uint32_t& lo, uint32_t& hi) {
+  lo = min(lo, dpp_self<0xB1>(lo));
+  hi = max(hi, dpp_self<0xB1>(hi));
+  lo = min(lo, dpp_self<0x4E>(lo));
+  hi = max(hi, dpp_self<0x4E>(hi));
+  lo = min(lo, dpp_self<0x141>(lo));
+  hi = max(hi, dpp_self<0x141>(hi));
+  lo = min(lo, dpp_self<0x140>(lo));
+  hi = max(hi, dpp_self<0x140>(hi));
+  auto a = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  lo = min(static_cast<uint32_t>(a[0]), static_cast<uint32_t>(a[1]));
+  a = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  hi = max(static_cast<uint32_t>(a[0]), static_cast<uint32_t>(a[1]));
+  a = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  lo = min(static_cast<uint32_t>(a[0]), static_cast<uint32_t>(a[1]));
+  a = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  hi = max(static_cast<uint32_t>(a[0]), static_cast<uint32_t>(a[1]));
+}
+
 // After a histogram pass over `nb` bins: the bin holding the rank-th key
 // (1-based) among those matching the prefix; the thread that finds it writes
 // the extended prefix and the rank within the bin.  Whole-block call: thread t
@@ -79,12 +127,7 @@ __device__ __forceinline__ void locate_digit(const uint32_t* hist, int nb, uint3
   uint32_t sum = 0;
   if (tid < users)
     for (int j = 0; j < per; ++j) sum += hist[tid * per + j];
-  uint32_t incl = sum;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const uint32_t v = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += v;
-  }
+  uint32_t incl = wave_inclusive_sum(sum);
   if (lane == kWave - 1) wtot[wave] = incl;
   __syncthreads();
   for (int w = 0; w < wave; ++w) incl += wtot[w];
@@ -136,6 +179,47 @@ __device__ __forceinline__ void lds_radix_select(const uint32_t* keys, int n, ui
   }
   kstar = prefix;
   m = static_cast<int>(rank);
+}
+
+// ---- select by score buckets (the two-stage kernels' first try).  Keys
+// ascend as scores descend, so the bucket of a score, floor((vmax - score) *
+// scale) with scale = kBuckets / (vmax - vmin), is non-decreasing in the key
+// (fp32 subtraction, product and truncation are monotone) and equal scores
+// share one: every key of a lower bucket is smaller than every key of a
+// higher one.  One histogram pass locates the bucket b holding the k-th
+// smallest key and its rank r inside b; the few keys of b are gathered, and
+// K* is the key of b with fewer than r keys of b below it and at least r at
+// or below it, found by direct comparison; m = r - (keys of b below K*).
+// Normal-like scores spread evenly over the buckets, so the histogram's
+// atomics rarely collide (the radix digits' top bits put a whole octave of
+// scores in one bin).  The result is the (K*, m) the radix select finds.
+// Rows with a non-finite or zero score range, or more than kSmallCap keys in
+// b (long runs of equal scores), take the radix select instead.
+constexpr int kBuckets = 4096;
+constexpr int kSweep = 8;   // LDS keys read together by each lane in the passes
+constexpr int kSmallCap = 1024;
+
+__device__ __forceinline__ int score_bucket(uint32_t key, float vmax, float scale) {
+  const float f = (vmax - key_score(key)) * scale;
+  return f >= static_cast<float>(kBuckets - 1) ? kBuckets - 1 : (f >= 0.f ? static_cast<int>(f) : 0);
+}
+
+// Whole-block minimum and maximum (every thread receives both).
+__device__ __forceinline__ void block_minmax(uint32_t lo, uint32_t hi, uint32_t* s_mm, uint32_t& kmin, uint32_t& kmax) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  wave_min_max(lo, hi);
+  if (lane == 0) {
+    s_mm[wave] = lo;
+    s_mm[kTW + wave] = hi;
+  }
+  __syncthreads();
+  kmin = s_mm[0];
+  kmax = s_mm[kTW];
+#pragma unroll
+  for (int w = 1; w < kTW; ++w) {
+    kmin = min(kmin, s_mm[w]);
+    kmax = max(kmax, s_mm[kTW + w]);
+  }
 }
 
 __global__ __launch_bounds__(kTT) void dsa_topk_kernel(TopkParams p) {
@@ -290,6 +374,88 @@ __device__ __forceinline__ int32_t* ws_cnt(const TopkParams& p, int i) {
   return reinterpret_cast<int32_t*>(p.ws + static_cast<size_t>(i) * kTopkRowWsBytes + kTopkMaxCand * 8);
 }
 
+// The bucket select of the two-stage kernels, fused with the per-wave counts
+// of the order-keeping sweep that follows it.  Wave w owns the run
+// [w_lo, w_hi) of the n keys.  On success: K* and m, and for every wave the
+// number of its keys in buckets below K*'s (their scores exceed the
+// threshold) in s_below[wave]; the keys of K*'s bucket are in small[0..c)
+// with their index in small_at, for the caller to classify.  Returns false
+// (nothing written but the histogram) when the radix select has to run.
+__device__ __forceinline__ bool bucket_select_runs(const uint32_t* keys, int n, uint32_t k, uint32_t kmin,
+                                                   uint32_t kmax, int w_lo, int w_hi, uint32_t* hist, uint32_t* small,
+                                                   uint16_t* small_at, uint32_t* s_prefix, uint32_t* s_rank,
+                                                   uint32_t* wtot, uint32_t* s_cnt, int* s_below, uint32_t& kstar,
+                                                   int& m, int& c) {
+  const float vmax = key_score(kmin), vmin = key_score(kmax);
+  const float range = vmax - vmin;
+  const float scale = static_cast<float>(kBuckets) / range;
+  // uniform: every thread holds the same kmin and kmax
+  if (!__builtin_isfinite(vmax) || !__builtin_isfinite(vmin) || !(range > 0.f) || !__builtin_isfinite(range) ||
+      !__builtin_isfinite(scale))
+    return false;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  // a batch of keys read before its atomics (the compiler would otherwise wait
+  // for each read behind the previous atomic)
+  for (int i0 = tid; i0 < n; i0 += kSweep * kTT) {
+    uint32_t kk[kSweep];
+#pragma unroll
+    for (int u = 0; u < kSweep; ++u) {
+      const int i = i0 + u * kTT;
+      kk[u] = i < n ? keys[i] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kSweep; ++u)   // past n: add 0 to some bin, no branch
+      atomicAdd(&hist[score_bucket(kk[u], vmax, scale)], i0 + u * kTT < n ? 1u : 0u);
+  }
+  __syncthreads();
+  locate_digit(hist, kBuckets, k, 0u, 0, s_prefix, s_rank, wtot);
+  __syncthreads();
+  const int b = static_cast<int>(*s_prefix);
+  const uint32_t r = *s_rank;
+  c = static_cast<int>(hist[b]);
+  if (c > kSmallCap) return false;   // uniform
+  // the wave's run: keys of lower buckets counted, K*'s bucket gathered
+  uint32_t below = 0;
+  for (int i0 = w_lo; i0 < w_hi; i0 += kSweep * kWave) {
+    uint32_t kk[kSweep];
+#pragma unroll
+    for (int u = 0; u < kSweep; ++u) {
+      const int i = i0 + u * kWave + lane;
+      kk[u] = i < w_hi ? keys[i] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kSweep; ++u) {
+      const int i = i0 + u * kWave + lane;
+      const int bk = i < w_hi ? score_bucket(kk[u], vmax, scale) : kBuckets;
+      below += __popcll(__ballot(bk < b));
+      if (bk == b) {
+        const uint32_t at = atomicAdd(s_cnt, 1u);
+        small[at] = kk[u];
+        small_at[at] = static_cast<uint16_t>(i);
+      }
+    }
+  }
+  if (lane == 0) s_below[wave] = static_cast<int>(below);
+  __syncthreads();
+  for (int t = tid; t < c; t += kTT) {
+    const uint32_t kt = small[t];
+    uint32_t less = 0, le = 0;
+    for (int j = 0; j < c; ++j) {
+      const uint32_t kj = small[j];
+      less += kj < kt;
+      le += kj <= kt;
+    }
+    if (less < r && r <= le) {   // every thread holding K* writes the same values
+      *s_prefix = kt;
+      *s_rank = r - less;
+    }
+  }
+  __syncthreads();
+  kstar = *s_prefix;
+  m = static_cast<int>(*s_rank);
+  return true;
+}
+
 // A: the top_k of one segment, written in ascending position order.
 __global__ __launch_bounds__(kTT) void dsa_topk_segment_kernel(TopkParams p) {
   const int seg = blockIdx.x, i_row = blockIdx.y;
@@ -303,13 +469,34 @@ __global__ __launch_bounds__(kTT) void dsa_topk_segment_kernel(TopkParams p) {
   uint32_t* out_key = ws_keys(p, i_row) + static_cast<int64_t>(seg) * p.top_k;
   int32_t* out_pos = ws_pos(p, i_row) + static_cast<int64_t>(seg) * p.top_k;
 
-  __shared__ uint32_t keys[kTopkSeg];
-  __shared__ uint32_t hist[4096];
-  __shared__ uint32_t s_prefix, s_rank;
+  __shared__ __attribute__((aligned(16))) uint32_t keys[kTopkSeg];
+  __shared__ uint32_t hist[kBuckets];   // the histogram, then the staged output
+  __shared__ uint32_t small[kSmallCap];
+  __shared__ uint16_t small_at[kSmallCap];
+  __shared__ uint32_t s_prefix, s_rank, s_cnt;
   __shared__ uint32_t s_wtot[kTW];
-  __shared__ int s_tot[2][kTW];
-  {
-    // every load of the thread in flight before the first LDS store
+  __shared__ uint32_t s_mm[2 * kTW];
+  __shared__ int s_tot[2][kTW];   // per wave: keys below K*, keys equal to K*
+  uint32_t klo = 0xffffffffu, khi = 0u;
+  if ((reinterpret_cast<uintptr_t>(sc) & 15) == 0 && (len & 3) == 0) {
+    // 16-byte loads, all in flight before the first LDS store
+    float4 v[kTopkSeg / (4 * kTT)];
+#pragma unroll
+    for (int u = 0; u < kTopkSeg / (4 * kTT); ++u) {
+      const int i = 4 * (u * kTT + tid);
+      v[u] = i < len ? *reinterpret_cast<const float4*>(sc + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < kTopkSeg / (4 * kTT); ++u) {
+      const int i = 4 * (u * kTT + tid);
+      if (i < len) {
+        const uint4 q = make_uint4(rank_key(v[u].x), rank_key(v[u].y), rank_key(v[u].z), rank_key(v[u].w));
+        *reinterpret_cast<uint4*>(&keys[i]) = q;
+        klo = min(klo, min(min(q.x, q.y), min(q.z, q.w)));
+        khi = max(khi, max(max(q.x, q.y), max(q.z, q.w)));
+      }
+    }
+  } else {
     float v[kTopkSeg / kTT];
 #pragma unroll
     for (int u = 0; u < kTopkSeg / kTT; ++u) {
@@ -319,11 +506,19 @@ __global__ __launch_bounds__(kTT) void dsa_topk_segment_kernel(TopkParams p) {
 #pragma unroll
     for (int u = 0; u < kTopkSeg / kTT; ++u) {
       const int i = u * kTT + tid;
-      if (i < len) keys[i] = rank_key(v[u]);
+      if (i < len) {
+        const uint32_t key = rank_key(v[u]);
+        keys[i] = key;
+        klo = min(klo, key);
+        khi = max(khi, key);
+      }
     }
   }
-  __syncthreads();
-  if (static_cast<uint32_t>(len) <= k) {   // the whole segment is a candidate
+  for (int i = tid; i < kBuckets; i += kTT) hist[i] = 0;
+  if (tid == 0) s_cnt = 0;
+  if (tid < kTW) s_tot[1][tid] = 0;
+  if (static_cast<uint32_t>(len) <= k) {   // the whole segment is a candidate (uniform)
+    __syncthreads();
     for (int i = tid; i < len; i += kTT) {
       out_key[i] = keys[i];
       out_pos[i] = lo + i;
@@ -331,23 +526,43 @@ __global__ __launch_bounds__(kTT) void dsa_topk_segment_kernel(TopkParams p) {
     if (tid == 0) ws_cnt(p, i_row)[seg] = len;
     return;
   }
-  uint32_t kstar;
-  int m;
-  lds_radix_select(keys, len, k, hist, &s_prefix, &s_rank, s_wtot, kstar, m);
-  // order-keeping compaction: wave w owns a run of positions; a selected
-  // position lands at (keys below K* before it) + min(ties before it, m)
+  uint32_t kmin, kmax, kstar = 0;
+  int m = 0, c = 0;
+  block_minmax(klo, khi, s_mm, kmin, kmax);   // its barrier publishes the keys and the zeroed counters
   const int per_wave = ((len + kTW - 1) / kTW + kWave - 1) / kWave * kWave;
   const int w_lo = min(len, wave * per_wave), w_hi = min(len, w_lo + per_wave);
-  int cb = 0, ct = 0;
-  for (int i0 = w_lo; i0 < w_hi; i0 += kWave) {
-    const int i = i0 + lane;
-    const uint32_t key = i < w_hi ? keys[i] : 0xffffffffu;
-    cb += __popcll(__ballot(i < w_hi && key < kstar));
-    ct += __popcll(__ballot(i < w_hi && key == kstar));
-  }
-  if (lane == 0) {
-    s_tot[0][wave] = cb;
-    s_tot[1][wave] = ct;
+  if (bucket_select_runs(keys, len, k, kmin, kmax, w_lo, w_hi, hist, small, small_at, &s_prefix, &s_rank, s_wtot,
+                         &s_cnt, s_tot[0], kstar, m, c)) {
+    // K*'s bucket: its keys below K* and equal to K*, counted for their waves
+    for (int t = tid; t < c; t += kTT) {
+      const uint32_t kt = small[t];
+      const int w = small_at[t] / per_wave;
+      if (kt < kstar)
+        atomicAdd(&s_tot[0][w], 1);
+      else if (kt == kstar)
+        atomicAdd(&s_tot[1][w], 1);
+    }
+  } else {
+    lds_radix_select(keys, len, k, hist, &s_prefix, &s_rank, s_wtot, kstar, m);
+    int cb = 0, ct = 0;
+    for (int i0 = w_lo; i0 < w_hi; i0 += kSweep * kWave) {
+      uint32_t kk[kSweep];
+#pragma unroll
+      for (int u = 0; u < kSweep; ++u) {
+        const int i = i0 + u * kWave + lane;
+        kk[u] = i < w_hi ? keys[i] : 0xffffffffu;
+      }
+#pragma unroll
+      for (int u = 0; u < kSweep; ++u) {
+        const bool ok = i0 + u * kWave + lane < w_hi;
+        cb += __popcll(__ballot(ok && kk[u] < kstar));
+        ct += __popcll(__ballot(ok && kk[u] == kstar));
+      }
+    }
+    if (lane == 0) {
+      s_tot[0][wave] = cb;
+      s_tot[1][wave] = ct;
+    }
   }
   __syncthreads();
   int rb = 0, rt = 0;
@@ -355,22 +570,49 @@ __global__ __launch_bounds__(kTT) void dsa_topk_segment_kernel(TopkParams p) {
     rb += s_tot[0][w];
     rt += s_tot[1][w];
   }
-  for (int i0 = w_lo; i0 < w_hi; i0 += kWave) {
-    const int i = i0 + lane;
-    const bool ok = i < w_hi;
-    const uint32_t key = ok ? keys[i] : 0xffffffffu;
-    const bool fb = ok && key < kstar, ft = ok && key == kstar;
-    const uint64_t bb = __ballot(fb), bt = __ballot(ft);
-    const int b_before = rb + lanes_below(bb), t_before = rt + lanes_below(bt);
-    int dst = -1;
-    if (fb) dst = b_before + min(t_before, m);
-    if (ft && t_before < m) dst = b_before + t_before;
-    if (dst >= 0) {
-      out_key[dst] = key;
-      out_pos[dst] = lo + i;
+  // order-keeping compaction: a selected position lands at (keys below K*
+  // before it) + min(ties before it, m); staged in LDS (the histogram's
+  // space) when it holds top_k pairs, so the stores leave as whole rows
+  const bool stage = 2 * k <= static_cast<uint32_t>(kBuckets);
+  uint32_t* st_key = hist;
+  uint32_t* st_pos = hist + k;
+  for (int i0 = w_lo; i0 < w_hi; i0 += kSweep * kWave) {
+    uint32_t kk[kSweep];
+#pragma unroll
+    for (int u = 0; u < kSweep; ++u) {
+      const int i = i0 + u * kWave + lane;
+      kk[u] = i < w_hi ? keys[i] : 0xffffffffu;
     }
-    rb += __popcll(bb);
-    rt += __popcll(bt);
+#pragma unroll
+    for (int u = 0; u < kSweep; ++u) {
+      const int i = i0 + u * kWave + lane;
+      const bool ok = i < w_hi;
+      const uint32_t key = kk[u];
+      const bool fb = ok && key < kstar, ft = ok && key == kstar;
+      const uint64_t bb = __ballot(fb), bt = __ballot(ft);
+      const int b_before = rb + lanes_below(bb), t_before = rt + lanes_below(bt);
+      int dst = -1;
+      if (fb) dst = b_before + min(t_before, m);
+      if (ft && t_before < m) dst = b_before + t_before;
+      if (dst >= 0 && dst < static_cast<int>(k)) {
+        if (stage) {
+          st_key[dst] = key;
+          st_pos[dst] = static_cast<uint32_t>(lo + i);
+        } else {
+          out_key[dst] = key;
+          out_pos[dst] = lo + i;
+        }
+      }
+      rb += __popcll(bb);
+      rt += __popcll(bt);
+    }
+  }
+  if (stage) {
+    __syncthreads();
+    for (int e = tid; e < static_cast<int>(k); e += kTT) {
+      out_key[e] = st_key[e];
+      out_pos[e] = static_cast<int32_t>(st_pos[e]);
+    }
   }
   if (tid == 0) ws_cnt(p, i_row)[seg] = p.top_k;
 }
@@ -386,14 +628,18 @@ __global__ __launch_bounds__(kTT) void dsa_topk_merge_kernel(TopkParams p) {
 
   __shared__ uint32_t ckey[kTopkMaxCand];
   __shared__ int32_t cpos[kTopkMaxCand];
-  __shared__ uint32_t hist[4096];
-  __shared__ uint32_t s_prefix, s_rank;
+  __shared__ uint32_t hist[kBuckets];   // the histogram, then the staged output
+  __shared__ uint32_t small[kSmallCap];
+  __shared__ uint16_t small_at[kSmallCap];
+  __shared__ uint32_t s_prefix, s_rank, s_cnt;
   __shared__ uint32_t s_wtot[kTW];
-  __shared__ int s_tot[3][kTW];
+  __shared__ uint32_t s_mm[2 * kTW];
+  __shared__ int s_tot[3][kTW];   // per wave: class 0, other keys below K*, keys equal to K*
   // Every segment but the last is longer than top_k (16384 > 8192 >= top_k)
   // and wrote exactly top_k candidates from s * top_k, so the candidates are
   // one contiguous run of (segs - 1) * top_k + the last segment's count.
   const int c_total = (segs - 1) * p.top_k + ws_cnt(p, i_row)[segs - 1];
+  uint32_t klo = 0xffffffffu, khi = 0u;
   {
     const uint32_t* ks = ws_keys(p, i_row);
     const int32_t* ps = ws_pos(p, i_row);
@@ -411,34 +657,62 @@ __global__ __launch_bounds__(kTT) void dsa_topk_merge_kernel(TopkParams p) {
       if (i < c_total) {
         ckey[i] = kv[u];
         cpos[i] = pv[u];
+        klo = min(klo, kv[u]);
+        khi = max(khi, kv[u]);
       }
     }
   }
-  __syncthreads();
-  uint32_t kstar;
-  int m;
-  lds_radix_select(ckey, c_total, k, hist, &s_prefix, &s_rank, s_wtot, kstar, m);
-  const float thr = key_score(kstar);
-
-  // the sweeps of the one-workgroup form over the candidates (ascending
-  // positions): class 0 (key < K*, score > threshold), class 1 (other keys
-  // below K*) and ties (key == K*, the first m selected)
+  for (int i = tid; i < kBuckets; i += kTT) hist[i] = 0;
+  if (tid == 0) s_cnt = 0;
+  if (tid < kTW) {
+    s_tot[1][tid] = 0;
+    s_tot[2][tid] = 0;
+  }
+  uint32_t kmin, kmax, kstar = 0;
+  int m = 0, c = 0;
+  block_minmax(klo, khi, s_mm, kmin, kmax);   // its barrier publishes the candidates and the zeroed counters
   const int per_wave = ((c_total + kTW - 1) / kTW + kWave - 1) / kWave * kWave;
   const int w_lo = min(c_total, wave * per_wave), w_hi = min(c_total, w_lo + per_wave);
-  int c0 = 0, c1 = 0, ct = 0;
-  for (int i0 = w_lo; i0 < w_hi; i0 += kWave) {
-    const int i = i0 + lane;
-    const bool ok = i < w_hi;
-    const uint32_t key = ok ? ckey[i] : 0xffffffffu;
-    const float v = key_score(key);
-    c0 += __popcll(__ballot(ok && key < kstar && v > thr));
-    c1 += __popcll(__ballot(ok && key < kstar && !(v > thr)));
-    ct += __popcll(__ballot(ok && key == kstar));
-  }
-  if (lane == 0) {
-    s_tot[0][wave] = c0;
-    s_tot[1][wave] = c1;
-    s_tot[2][wave] = ct;
+  float thr;
+  if (bucket_select_runs(ckey, c_total, k, kmin, kmax, w_lo, w_hi, hist, small, small_at, &s_prefix, &s_rank, s_wtot,
+                         &s_cnt, s_tot[0], kstar, m, c)) {
+    // keys of lower buckets score above the threshold (class 0, counted);
+    // K*'s bucket is classified key by key
+    thr = key_score(kstar);
+    for (int t = tid; t < c; t += kTT) {
+      const uint32_t kt = small[t];
+      const int w = small_at[t] / per_wave;
+      if (kt < kstar)
+        atomicAdd(&s_tot[key_score(kt) > thr ? 0 : 1][w], 1);
+      else if (kt == kstar)
+        atomicAdd(&s_tot[2][w], 1);
+    }
+  } else {
+    lds_radix_select(ckey, c_total, k, hist, &s_prefix, &s_rank, s_wtot, kstar, m);
+    thr = key_score(kstar);
+    int c0 = 0, c1 = 0, ct = 0;
+    for (int i0 = w_lo; i0 < w_hi; i0 += kSweep * kWave) {
+      uint32_t kk[kSweep];
+#pragma unroll
+      for (int u = 0; u < kSweep; ++u) {
+        const int i = i0 + u * kWave + lane;
+        kk[u] = i < w_hi ? ckey[i] : 0xffffffffu;
+      }
+#pragma unroll
+      for (int u = 0; u < kSweep; ++u) {
+        const bool ok = i0 + u * kWave + lane < w_hi;
+        const uint32_t key = kk[u];
+        const float v = key_score(key);
+        c0 += __popcll(__ballot(ok && key < kstar && v > thr));
+        c1 += __popcll(__ballot(ok && key < kstar && !(v > thr)));
+        ct += __popcll(__ballot(ok && key == kstar));
+      }
+    }
+    if (lane == 0) {
+      s_tot[0][wave] = c0;
+      s_tot[1][wave] = c1;
+      s_tot[2][wave] = ct;
+    }
   }
   __syncthreads();
   int r0 = 0, r1 = 0, rt = 0, n0 = 0;
@@ -450,23 +724,46 @@ __global__ __launch_bounds__(kTT) void dsa_topk_merge_kernel(TopkParams p) {
     }
     n0 += s_tot[0][w];
   }
-  for (int i0 = w_lo; i0 < w_hi; i0 += kWave) {
-    const int i = i0 + lane;
-    const bool ok = i < w_hi;
-    const uint32_t key = ok ? ckey[i] : 0xffffffffu;
-    const float v = key_score(key);
-    const bool f0 = ok && key < kstar && v > thr;
-    const bool f1 = ok && key < kstar && !(v > thr);
-    const bool ft = ok && key == kstar;
-    const uint64_t b0 = __ballot(f0), b1 = __ballot(f1), bt = __ballot(ft);
-    const int t_before = rt + lanes_below(bt);
-    const int pos = ok ? cpos[i] : 0;
-    if (f0) out[r0 + lanes_below(b0)] = pos;
-    if (f1) out[n0 + r1 + lanes_below(b1) + min(t_before, m)] = pos;
-    if (ft && t_before < m) out[n0 + r1 + lanes_below(b1) + t_before] = pos;
-    r0 += __popcll(b0);
-    r1 += __popcll(b1);
-    rt += __popcll(bt);
+  // the sweeps of the one-workgroup form over the candidates (ascending
+  // positions): class 0 (key < K*, score > threshold), class 1 (other keys
+  // below K*) and ties (key == K*, the first m selected); staged in LDS (the
+  // histogram's space) when it holds top_k positions
+  const bool stage = k <= static_cast<uint32_t>(kBuckets);
+  int32_t* st = reinterpret_cast<int32_t*>(hist);
+  int32_t* dst_base = stage ? st : out;
+  for (int i0 = w_lo; i0 < w_hi; i0 += kSweep * kWave) {
+    uint32_t kk[kSweep];
+    int32_t pp[kSweep];
+#pragma unroll
+    for (int u = 0; u < kSweep; ++u) {
+      const int i = i0 + u * kWave + lane;
+      kk[u] = i < w_hi ? ckey[i] : 0xffffffffu;
+      pp[u] = i < w_hi ? cpos[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kSweep; ++u) {
+      const int i = i0 + u * kWave + lane;
+      const bool ok = i < w_hi;
+      const uint32_t key = kk[u];
+      const float v = key_score(key);
+      const bool f0 = ok && key < kstar && v > thr;
+      const bool f1 = ok && key < kstar && !(v > thr);
+      const bool ft = ok && key == kstar;
+      const uint64_t b0 = __ballot(f0), b1 = __ballot(f1), bt = __ballot(ft);
+      const int t_before = rt + lanes_below(bt);
+      int d = -1;
+      if (f0) d = r0 + lanes_below(b0);
+      if (f1) d = n0 + r1 + lanes_below(b1) + min(t_before, m);
+      if (ft && t_before < m) d = n0 + r1 + lanes_below(b1) + t_before;
+      if (d >= 0 && d < static_cast<int>(k)) dst_base[d] = pp[u];
+      r0 += __popcll(b0);
+      r1 += __popcll(b1);
+      rt += __popcll(bt);
+    }
+  }
+  if (stage) {
+    __syncthreads();
+    for (int e = tid; e < static_cast<int>(k); e += kTT) out[e] = st[e];
   }
 }
 

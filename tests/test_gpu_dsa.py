@@ -28,6 +28,13 @@ def _scores(n, layer, kind="normal"):
         s = np.where(s > 0.5, np.float32(0.0), np.where(s > -0.5, np.float32(-0.0), s)).astype(np.float32)
     elif kind == "negative":
         s = -np.abs(s) - np.float32(1.0)
+    elif kind == "fine":        # a 1/1024 grid: short tie runs inside one score bucket
+        s = np.round(s * 1024.0).astype(np.float32) / np.float32(1024.0)
+    elif kind == "signed_zero_mix":   # normal scores with +0 / -0 pairs near the threshold of a 2048-of-131072 row
+        s = s.copy()
+        s[::97] = np.float32(2.0)
+        s[1::97] = np.float32(0.0)
+        s[2::97] = np.float32(-0.0)
     return np.ascontiguousarray(s, dtype=np.float32)
 
 
@@ -40,6 +47,8 @@ def _scores(n, layer, kind="normal"):
     # candidates, all ties, zeros and long tie runs across segment ends
     (16385, 64, "normal"), (40000, 5000, "coarse"), (131072, 2048, "equal"), (131072, 2048, "zeros"),
     (65543, 2048, "coarse"), (131072, 2048, "negative"),
+    # the score-bucket select: ties inside the bucket, +-0 and a tie run at the threshold
+    (131072, 2048, "fine"), (50000, 3000, "fine"), (131072, 2048, "signed_zero_mix"), (20000, 9000, "normal"),
 ])
 def test_topk_matches_oracle_bitwise(n, k, kind, two_stage):
     say(f"dsa topk n={n} k={k} {kind} two_stage={two_stage}")
