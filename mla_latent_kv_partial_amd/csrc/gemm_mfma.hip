@@ -48,15 +48,24 @@ __device__ __forceinline__ void store_cols4(const GemmNT& p, int m, int n, const
   }
 }
 
+// One rope pair (a, b) of a q row rotated by the table's (cos, sin) in fp32
+// (two products and one fused add each), rounded once to bf16; the 128 x 128
+// and the 256 x 256 tiles share it, so both give the same bits.
+__device__ __forceinline__ void rope_pair_bf16(float a, float b, float2 cs, uint16_t& re, uint16_t& im) {
+  re = f32_to_bf16(fmaf(a, cs.x, -(b * cs.y)));
+  im = f32_to_bf16(fmaf(b, cs.x, a * cs.y));
+}
+
 // A wave's output blocks: block (bm, bn) lane (i16, g) holds row
 // m_base + 16 bm + i16, columns n_base + 16 bn + 4 g .. +3.  n_base is a
 // multiple of 64 and the wave spans at most 64 columns, so with ROPE (the q
 // projection, 192 columns per head: 128 no-PE, then 64 rope) its columns are
 // either all no-PE or all the rope part of one head.  Rope columns are
 // rotated at the row's position and written as split halves: columns
-// (v0, v1) and (v2, v3) are rope pairs q0 and q0 + 1 of the head, cos and sin
-// come from the row's table in double.  The table entries of row block bm + 1
-// are requested before block bm is rotated, so their latency overlaps.
+// (v0, v1) and (v2, v3) are rope pairs q0 and q0 + 1 of the head, rotated by
+// the row's cos and sin from the table (rope_pair_bf16).  A rope wave requests the table entries of four row blocks at a time
+// (2 BN float2 per block, in the registers the fragments held) before it
+// rotates them, so their latency is paid twice per tile, not once per block.
 template <bool ROPE, bool OUT_F32, int BM, int BN>
 __device__ __forceinline__ void store_tile(const GemmNT& p, const f32x4 (&acc)[BM][BN], int m_base, int n_base,
                                            int i16, int g) {
@@ -64,22 +73,24 @@ __device__ __forceinline__ void store_tile(const GemmNT& p, const f32x4 (&acc)[B
   if (ROPE && n_base % kQk >= kDn) {
     const int head_col = n_base - n_base % kQk;           // first column of the head
     const int q_lane = (n_base % kQk - kDn) / 2 + 2 * g;  // pair of column n_base + 4 g
-    double2 cur[BN][2], nxt[BN][2];
-    auto load = [&](double2 (&t)[BN][2], int bm) {
-      const int m = min(m_base + 16 * bm + i16, p.m - 1);
-      const double2* cs = p.cs + static_cast<int64_t>(m) * 32 + q_lane;
+    constexpr int kChunk = BM < 4 ? BM : 4;   // row blocks whose table entries fly together
 #pragma unroll
-      for (int bn = 0; bn < BN; ++bn) {
-        t[bn][0] = cs[8 * bn];
-        t[bn][1] = cs[8 * bn + 1];
+    for (int b0 = 0; b0 < BM; b0 += kChunk) {
+      float2 t[kChunk][BN][2];
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) {
+        const int m = min(m_base + 16 * (b0 + u) + i16, p.m - 1);
+        const float2* cs = p.cs + static_cast<int64_t>(m) * 32 + q_lane;
+#pragma unroll
+        for (int bn = 0; bn < BN; ++bn) {
+          t[u][bn][0] = cs[8 * bn];
+          t[u][bn][1] = cs[8 * bn + 1];
+        }
       }
-    };
-    load(cur, 0);
 #pragma unroll
-    for (int bm = 0; bm < BM; ++bm) {
-      if (bm + 1 < BM) load(nxt, bm + 1);
-      const int m = m_base + 16 * bm + i16;
-      if (m < p.m) {
+      for (int u = 0; u < kChunk; ++u) {
+        const int m = m_base + 16 * (b0 + u) + i16;
+        if (m >= p.m) continue;
         uint16_t* head = static_cast<uint16_t*>(p.c) + static_cast<int64_t>(m) * p.ldc + head_col + kDn;
 #pragma unroll
         for (int bn = 0; bn < BN; ++bn) {
@@ -87,21 +98,10 @@ __device__ __forceinline__ void store_tile(const GemmNT& p, const f32x4 (&acc)[B
           const int q0 = q_lane + 8 * bn;
           uint16_t re[2], im[2];
 #pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const double2 t = cur[bn][e];
-            const double a = acc[bm][bn][2 * e], b = acc[bm][bn][2 * e + 1];
-            re[e] = f64_to_bf16(a * t.x - b * t.y);
-            im[e] = f64_to_bf16(b * t.x + a * t.y);
-          }
+          for (int e = 0; e < 2; ++e)
+            rope_pair_bf16(acc[b0 + u][bn][2 * e], acc[b0 + u][bn][2 * e + 1], t[u][bn][e], re[e], im[e]);
           *reinterpret_cast<uint32_t*>(head + q0) = re[0] | (static_cast<uint32_t>(re[1]) << 16);
           *reinterpret_cast<uint32_t*>(head + kDr / 2 + q0) = im[0] | (static_cast<uint32_t>(im[1]) << 16);
-        }
-      }
-      if (bm + 1 < BM) {
-#pragma unroll
-        for (int bn = 0; bn < BN; ++bn) {
-          cur[bn][0] = nxt[bn][0];
-          cur[bn][1] = nxt[bn][1];
         }
       }
     }
@@ -207,27 +207,124 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(GemmNT p) {
 
 // ------------------------------------------------------------------ 256 x 256 NT GEMM
 // Same contract, workgroup tile 256 x 256 for long GEMMs: 8 waves of 128 x 64
-// (8 x 4 MFMA blocks), K step 32 through a 4-stage LDS ring, three steps in
-// flight.  A 16-row block of an operand tile is 1 KB: row r (64 bytes, four
-// 16-byte chunks) at 64 r, chunk c stored at position c ^ ((r >> 2) & 3).
-// Each copy instruction fills one block with four lanes per row, so the
-// global reads coalesce into whole 64-byte row segments; the XOR spreads the
-// fragment reads (16 rows, one chunk each) over the banks.  Relative to the
-// 128 x 128 tile this halves the operand bytes per FLOP that reach the CU.
-// (Measured: chunk-major blocks read by single lanes per row, which need no
-// swizzle, were 12 % slower from the uncoalesced copies; a deeper 5-stage
-// ring and register-staged copies were no faster.)
+// (8 x 4 MFMA blocks).  The operands stream through LDS in K steps of 64 as
+// half stages: the A or the B slice of one step (256 rows of 128 bytes, 32
+// KB), in a ring of five slots (160 KB), so that up to three half stages fly
+// while a step computes.  A row's 16-byte chunk c sits at position
+// c ^ (r & 7) of its 128-byte line: each 1 KB copy instruction fills 8 whole
+// rows (every request covers whole 128-byte row segments; measured on the
+// copy path alone, 23 % faster than the 64-byte segments of 32-wide K steps),
+// and the fragment reads (16 rows, one chunk each) hit 32 distinct banks per
+// 8 lanes.
+// Per K step a wave runs its MFMAs in two halves of K = 32; the fragments of
+// each half are read from LDS while the MFMAs of the half before run, and
+// the step's one barrier sits between the halves: after it, step i + 1 has
+// landed (every wave waited for its own copies) and every wave has finished
+// reading step i, whose two slots then take the copies of the next two half
+// stages.
 constexpr int kBT = 256;
-constexpr int kBK = 32;
-constexpr int kBOpBytes = kBT * kBK * 2;            // 16 KB per operand tile
-constexpr int kBStageBytes = 2 * kBOpBytes;         // A tile then B tile
-constexpr int kBStages = 4;
-constexpr int kBCopies = kBStageBytes / 1024 / 8;   // 1 KB copies per wave per stage (4)
+constexpr int kBK = 64;
+constexpr int kBRowBytes = kBK * 2;                 // 128
+constexpr int kBHalfBytes = kBT * kBRowBytes;       // 32 KB: one operand's slice of a step
+constexpr int kBSlots = 5;
+constexpr int kBCopies = kBHalfBytes / 1024 / 8;    // 1 KB copies per wave per half stage (4)
 
-__shared__ __attribute__((aligned(1024))) char g_gemm256[kBStages * kBStageBytes];
+__shared__ __attribute__((aligned(1024))) char g_gemm256[kBSlots * kBHalfBytes];
 
-// chunk swizzle of row r of a 16-row block
-__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+// Epilogue of the 256 x 256 tile through LDS (free once the K loop is done):
+// the waves write their accumulators in their fragment layout (bf16 rounded
+// to nearest even, or fp32), then the tile leaves in whole rows, every store
+// instruction covering full 128-byte lines, where the fragment layout stores
+// 32-byte pieces of 16 rows (measured: the epilogue took as long as a third
+// of the MFMA work).  fp32 tiles go in two passes of 128 rows.
+template <bool ROPE, bool OUT_F32>
+__device__ __forceinline__ void store_tile_staged(const GemmNT& p, const f32x4 (&acc)[8][4], int m0, int n0, int wm,
+                                                  int wn, int i16, int g) {
+  static_assert(!(ROPE && OUT_F32), "the q projection writes bf16");
+  constexpr int kEs = OUT_F32 ? 4 : 2;              // bytes per element
+  constexpr int kRowB = 256 * kEs + 16;             // LDS row stride
+  constexpr int kPassRows = OUT_F32 ? 128 : 256;
+  constexpr int kChunks = 256 * kEs / 16;           // 16-byte chunks per row
+  static_assert(kPassRows * kRowB <= kBSlots * kBHalfBytes, "a pass fits the LDS ring");
+  const int tid = threadIdx.x;
+  const bool al16 = (p.ldc * kEs) % 16 == 0;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  lds_barrier();   // every wave is past its last fragment reads
+#pragma unroll
+  for (int pass = 0; pass < 256 / kPassRows; ++pass) {
+    const int n_base = n0 + 64 * wn;
+    if (ROPE && n_base % kQk >= kDn) {
+      // rope columns: rotated here, written as split halves (pair q at column
+      // q, its imaginary part at 32 + q of the head's rope part), with the
+      // table entries of four row blocks requested at a time
+      const int q_lane = (n_base % kQk - kDn) / 2 + 2 * g;   // pair of column n_base + 4 g
+      const int rope_col = 64 * wn - (n_base % kQk - kDn);    // tile column of the head's rope part
+#pragma unroll
+      for (int b0 = 0; b0 < 8; b0 += 4) {
+        float2 t[4][4][2];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int m = min(m0 + 128 * wm + 16 * (b0 + u) + i16, p.m - 1);
+          const float2* cs = p.cs + static_cast<int64_t>(m) * 32 + q_lane;
+#pragma unroll
+          for (int bn = 0; bn < 4; ++bn) {
+            t[u][bn][0] = cs[8 * bn];
+            t[u][bn][1] = cs[8 * bn + 1];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int bn = 0; bn < 4; ++bn) {
+            uint16_t re[2], im[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+              rope_pair_bf16(acc[b0 + u][bn][2 * e], acc[b0 + u][bn][2 * e + 1], t[u][bn][e], re[e], im[e]);
+            char* d = g_gemm256 + (128 * wm + 16 * (b0 + u) + i16) * kRowB + (rope_col + q_lane + 8 * bn) * kEs;
+            *reinterpret_cast<uint32_t*>(d) = re[0] | (static_cast<uint32_t>(re[1]) << 16);
+            *reinterpret_cast<uint32_t*>(d + (kDr / 2) * kEs) = im[0] | (static_cast<uint32_t>(im[1]) << 16);
+          }
+      }
+    } else if (!OUT_F32 || wm == pass) {
+      const int rbase = OUT_F32 ? 0 : 128 * wm;
+#pragma unroll
+      for (int bm = 0; bm < 8; ++bm)
+#pragma unroll
+        for (int bn = 0; bn < 4; ++bn) {
+          char* d = g_gemm256 + (rbase + 16 * bm + i16) * kRowB + (64 * wn + 16 * bn + 4 * g) * kEs;
+          const f32x4& v = acc[bm][bn];
+          if (OUT_F32) {
+            *reinterpret_cast<float4*>(d) = make_float4(v[0], v[1], v[2], v[3]);
+          } else {
+            const uint32_t lo = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+            const uint32_t hi = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+            *reinterpret_cast<uint2*>(d) = make_uint2(lo, hi);
+          }
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    lds_barrier();
+    for (int e = tid; e < kPassRows * kChunks; e += 512) {
+      const int r = e / kChunks, ch = e % kChunks;
+      const int m = m0 + pass * kPassRows + r;
+      const int n = n0 + ch * (16 / kEs);
+      if (m < p.m && n < p.n) {
+        const uint4 v = *reinterpret_cast<const uint4*>(g_gemm256 + r * kRowB + ch * 16);
+        char* crow = static_cast<char*>(p.c) + (static_cast<int64_t>(m) * p.ldc + n) * kEs;
+        if (al16 && n + 16 / kEs <= p.n) {
+          *reinterpret_cast<uint4*>(crow) = v;
+        } else {   // 8-byte pieces (the row is 8-byte aligned; n + 4 elements of bf16 or 2 of fp32 may end it)
+          *reinterpret_cast<uint2*>(crow) = make_uint2(v.x, v.y);
+          if (n + 8 / kEs < p.n) *reinterpret_cast<uint2*>(crow + 8) = make_uint2(v.z, v.w);
+        }
+      }
+    }
+    if (pass + 1 < 256 / kPassRows) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      lds_barrier();   // the pass's rows are read before the next pass overwrites them
+    }
+  }
+}
 
 template <bool ROPE, bool OUT_F32>
 __global__ __launch_bounds__(512) void gemm256_nt_kernel(GemmNT p) {
@@ -237,68 +334,96 @@ __global__ __launch_bounds__(512) void gemm256_nt_kernel(GemmNT p) {
   const int m0 = (tile % p.m_tiles) * kBT;
   const int n0 = (tile / p.m_tiles) * kBT;
 
-  // copy plan: copy j of this wave fills 16-row block q = wave + 8 j of the
-  // stage (blocks 0..15 of A, 16..31 of B); lane l lands at position l of the
-  // block: row l / 4, chunk (l % 4) ^ swz(l / 4).  Rows past the matrix edge
+  // copy plan: copy j of this wave fills 8-row block q = wave + 8 j of a
+  // half stage; lane l lands at position l of the block: row l / 8, position
+  // l % 8, which holds chunk (l % 8) ^ (l / 8).  Rows past the matrix edge
   // re-read its last row.
-  const uint16_t* src[kBCopies];
+  const uint16_t* srca[kBCopies];
+  const uint16_t* srcb[kBCopies];
 #pragma unroll
   for (int j = 0; j < kBCopies; ++j) {
-    const int q = wave + 8 * j;
-    const int r16 = lane >> 2;
-    const int row = 16 * (q & 15) + r16;
-    const int c = (lane & 3) ^ swz(r16);
-    src[j] = q < 16 ? p.a + static_cast<int64_t>(min(m0 + row, p.m - 1)) * p.lda + 8 * c
-                    : p.b + static_cast<int64_t>(min(n0 + row, p.n - 1)) * p.ldb + 8 * c;
+    const int r8 = lane >> 3;
+    const int row = 8 * (wave + 8 * j) + r8;
+    const int c = (lane & 7) ^ r8;
+    srca[j] = p.a + static_cast<int64_t>(min(m0 + row, p.m - 1)) * p.lda + 8 * c;
+    srcb[j] = p.b + static_cast<int64_t>(min(n0 + row, p.n - 1)) * p.ldb + 8 * c;
   }
-  auto issue = [&](int s, int k0) {
-    const uint32_t dst = lds_addr(g_gemm256 + s * kBStageBytes);
+  // half stage h: the A slice (h even) or the B slice (h odd) of step h / 2, in slot h % 5
+  const int nh = 2 * (p.k / kBK);
+  auto issue = [&](int h) {
+    if (h >= nh) return;
+    const uint32_t dst = lds_addr(g_gemm256 + (h % kBSlots) * kBHalfBytes) + wave * 1024;
+    const int k0 = (h >> 1) * kBK;
+    if (h & 1) {
 #pragma unroll
-    for (int j = 0; j < kBCopies; ++j) dma16(src[j] + k0, dst + (wave + 8 * j) * 1024);
+      for (int j = 0; j < kBCopies; ++j) dma16(srcb[j] + k0, dst + j * 8192);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kBCopies; ++j) dma16(srca[j] + k0, dst + j * 8192);
+    }
   };
 
   const int wm = wave >> 2, wn = wave & 3;   // rows 128 wm .., columns 64 wn ..
   const int i16 = lane & 15, g = lane >> 4;
-  // fragment of lane l: row l % 16, chunk l / 16 of a block
-  const uint32_t lpos = 64 * i16 + 16 * (g ^ swz(i16));
-  const uint32_t a_frag = (8 * wm) * 1024 + lpos;
-  const uint32_t b_frag = kBOpBytes + (4 * wn) * 1024 + lpos;
+  // fragment of lane l in half q: row l % 16 of a 16-row block, chunk
+  // 4 q + l / 16 at its swizzled position
+  const uint32_t a_row = (128 * wm + i16) * kBRowBytes;
+  const uint32_t b_row = (64 * wn + i16) * kBRowBytes;
+  const uint32_t pos0 = 16 * (g ^ (i16 & 7)), pos1 = 16 * ((4 + g) ^ (i16 & 7));
 
-  const int nk = p.k / kBK;
-  for (int t = 0; t < kBStages - 1 && t < nk; ++t) issue(t, t * kBK);
+  const int nk = nh / 2;
+  for (int h = 0; h < kBSlots; ++h) issue(h);
   f32x4 acc[8][4];
 #pragma unroll
   for (int bm = 0; bm < 8; ++bm)
 #pragma unroll
     for (int bn = 0; bn < 4; ++bn) acc[bm][bn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int i = 0; i < nk; ++i) {
-    // step i's copies done; those of the (up to two) following steps may fly
-    const int later = min(nk - 1 - i, kBStages - 2);
-    wait_vm_upto<kBCopies * (kBStages - 2)>(kBCopies * later);
-    lds_barrier();
-    if (i + kBStages - 1 < nk) issue((i + kBStages - 1) % kBStages, (i + kBStages - 1) * kBK);
-    const char* st = g_gemm256 + (i % kBStages) * kBStageBytes;
-    bf16x8 af[8], bfr[4];
+  auto read_half = [&](int step, uint32_t pos, bf16x8 (&a)[8], bf16x8 (&b)[4]) {
+    const char* sa = g_gemm256 + ((2 * step) % kBSlots) * kBHalfBytes + pos;
+    const char* sb = g_gemm256 + ((2 * step + 1) % kBSlots) * kBHalfBytes + pos;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) bfr[t] = *reinterpret_cast<const bf16x8*>(st + b_frag + t * 1024);
+    for (int t = 0; t < 4; ++t) b[t] = *reinterpret_cast<const bf16x8*>(sb + b_row + t * 16 * kBRowBytes);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) af[t] = *reinterpret_cast<const bf16x8*>(st + a_frag + t * 1024);
-    // D^T blocks: lane (row m = i16, group g) receives C[m][n + 4g + (0..3)]
+    for (int t = 0; t < 8; ++t) a[t] = *reinterpret_cast<const bf16x8*>(sa + a_row + t * 16 * kBRowBytes);
+  };
+  // D^T blocks: lane (row m = i16, group g) receives C[m][n + 4g + (0..3)]
+  auto mfmas = [&](const bf16x8 (&a)[8], const bf16x8 (&b)[4]) {
 #pragma unroll
     for (int bm = 0; bm < 8; ++bm)
 #pragma unroll
-      for (int bn = 0; bn < 4; ++bn) acc[bm][bn] = mfma16x16x32(bfr[bn], af[bm], acc[bm][bn]);
+      for (int bn = 0; bn < 4; ++bn) acc[bm][bn] = mfma16x16x32(b[bn], a[bm], acc[bm][bn]);
+  };
+  // step 0 landed; half stages 2 .. 4 may fly
+  wait_vm_upto<kBCopies * (kBSlots - 2)>(kBCopies * (min(kBSlots, nh) - 2));
+  lds_barrier();
+  bf16x8 a0[8], b0[4], a1[8], b1[4];
+  read_half(0, pos0, a0, b0);
+  for (int i = 0; i < nk; ++i) {
+    read_half(i, pos1, a1, b1);
+    mfmas(a0, b0);
+    if (i + 1 < nk) {
+      // step i + 1 landed (half stage 2 i + 4 may fly); every wave is past
+      // its reads of step i, whose slots take half stages 2 i + 5 and 2 i + 6
+      wait_vm_upto<kBCopies>(2 * i + 4 < nh ? kBCopies : 0);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      lds_barrier();
+      issue(2 * i + 5);
+      issue(2 * i + 6);
+      read_half(i + 1, pos0, a0, b0);
+    }
+    mfmas(a1, b1);
   }
 
-  store_tile<ROPE, OUT_F32>(p, acc, m0 + 128 * wm, n0 + 64 * wn, i16, g);
+  store_tile_staged<ROPE, OUT_F32>(p, acc, m0, n0, wm, wn, i16, g);
 }
 
 // cos / sin of the q RoPE angles, one thread per (row, pair): the angle is
 // the f32 product of the position and the pair's inverse frequency, its
 // cos and sin are taken in double (the accurate device routine: positions
-// reach 2^17 and beyond, where a hardware approximation loses the angle).
-__global__ __launch_bounds__(256) void rope_table_kernel(GemmNT p, double2* __restrict__ cs) {
+// reach 2^17 and beyond, where a hardware approximation loses the angle) and
+// rounded to f32.
+__global__ __launch_bounds__(256) void rope_table_kernel(GemmNT p, float2* __restrict__ cs) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= static_cast<int64_t>(p.m) * 32) return;
   const int m = static_cast<int>(i >> 5), q = static_cast<int>(i & 31);
@@ -307,12 +432,12 @@ __global__ __launch_bounds__(256) void rope_table_kernel(GemmNT p, double2* __re
   const float ang = static_cast<float>(pos * static_cast<double>(p.inv[q]));
   double sn, c;
   sincos(static_cast<double>(ang), &sn, &c);
-  cs[i] = make_double2(c, sn);
+  cs[i] = make_float2(static_cast<float>(c), static_cast<float>(sn));
 }
 
 }  // namespace
 
-hipError_t launch_rope_table(const GemmNT& p, double2* cs, hipStream_t stream) {
+hipError_t launch_rope_table(const GemmNT& p, float2* cs, hipStream_t stream) {
   const int64_t n = static_cast<int64_t>(p.m) * 32;
   hipLaunchKernelGGL(rope_table_kernel, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, stream, p, cs);
   return hipGetLastError();

@@ -170,11 +170,12 @@ struct GemmNT {
   float inv[32];
   // RoPE epilogue: {cos, sin} of the angle of GEMM row m and pair q at
   // cs[32 m + q], written by launch_rope_table for the same rows
-  const double2* cs;
+  const float2* cs;
 };
-// cs[32 m + q] for m < p.m, q < 32 (the 64-wide rope part): cos and sin, in
-// double, of the f32 angle (position of row m) * inv[q].
-hipError_t launch_rope_table(const GemmNT& p, double2* cs, hipStream_t stream);
+// cs[32 m + q] for m < p.m, q < 32 (the 64-wide rope part): cos and sin of
+// the f32 angle (position of row m) * inv[q], taken in double and rounded to
+// f32.
+hipError_t launch_rope_table(const GemmNT& p, float2* cs, hipStream_t stream);
 bool gemm_nt_mfma_ok(const void* a, int64_t lda, const void* b, int64_t ldb, const void* c, int64_t ldc, int64_t m,
                      int64_t n, int64_t k);
 hipError_t launch_gemm_nt_mfma(const GemmNT& p, bool rope, bool out_f32, hipStream_t stream);

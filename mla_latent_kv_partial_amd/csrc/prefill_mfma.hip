@@ -305,9 +305,9 @@ bool prefill_mfma_supported(const PrefillParams& p) {
          al(p.ctx);
 }
 
-// q RoPE table of one launch: {cos, sin} (double) per query row and pair
+// q RoPE table of one launch: {cos, sin} (f32) per query row and pair
 size_t rope_table_bytes(const PrefillParams& p) {
-  return static_cast<size_t>(min(p.batch, kBatchPerLaunch)) * p.tokens * 32 * sizeof(double2);
+  return static_cast<size_t>(min(p.batch, kBatchPerLaunch)) * p.tokens * 32 * sizeof(float2);
 }
 
 size_t prefill_mfma_workspace_bytes(const PrefillParams& p) {
@@ -321,7 +321,7 @@ hipError_t launch_prefill_mfma(const PrefillParams& p, hipStream_t stream) {
   const size_t q_bytes = static_cast<size_t>(p.batch) * p.tokens * p.heads * kQk * 2;
   const size_t kv_bytes = static_cast<size_t>(p.batch) * p.keys * p.heads * kKvw * 2;
   uint16_t* kv = reinterpret_cast<uint16_t*>(static_cast<char*>(p.workspace) + up256(q_bytes));
-  double2* cs = reinterpret_cast<double2*>(static_cast<char*>(p.workspace) + up256(q_bytes) + up256(kv_bytes));
+  float2* cs = reinterpret_cast<float2*>(static_cast<char*>(p.workspace) + up256(q_bytes) + up256(kv_bytes));
   const uint16_t* q_c = static_cast<const uint16_t*>(p.q_c);
   const uint16_t* latent = static_cast<const uint16_t*>(p.latent);
   const uint16_t* rope = static_cast<const uint16_t*>(p.rope);
