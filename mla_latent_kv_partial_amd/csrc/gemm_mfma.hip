@@ -334,32 +334,39 @@ __global__ __launch_bounds__(512) void gemm256_nt_kernel(GemmNT p) {
   const int m0 = (tile % p.m_tiles) * kBT;
   const int n0 = (tile / p.m_tiles) * kBT;
 
-  // copy plan: copy j of this wave fills 8-row block q = wave + 8 j of a
-  // half stage; lane l lands at position l of the block: row l / 8, position
-  // l % 8, which holds chunk (l % 8) ^ (l / 8).  Rows past the matrix edge
-  // re-read its last row.
-  const uint16_t* srca[kBCopies];
-  const uint16_t* srcb[kBCopies];
+  // copy plan: waves 0..3 issue every copy (8 per half stage each), so the
+  // waves sharing their SIMDs (4..7) keep issuing MFMAs while a copy holds
+  // its wave at the address path (q_b 184 -> 174 us).  Copy j of issuing wave
+  // w fills 8-row block q = w + 4 j of a half stage; lane l lands at
+  // position l of the block: row l / 8, position l % 8, which holds chunk
+  // (l % 8) ^ (l / 8).  Each copy is an SGPR base (the operand at the step's
+  // K offset) plus a 32-bit lane offset (the launcher takes this kernel only
+  // for operands under 4 GB).  Rows past the matrix edge re-read its last row.
+  constexpr int kIss = 2 * kBCopies;
+  uint32_t offa[kIss], offb[kIss];
+  const bool issuer = wave < 4;
 #pragma unroll
-  for (int j = 0; j < kBCopies; ++j) {
+  for (int j = 0; j < kIss; ++j) {
     const int r8 = lane >> 3;
-    const int row = 8 * (wave + 8 * j) + r8;
+    const int row = 8 * ((wave & 3) + 4 * j) + r8;
     const int c = (lane & 7) ^ r8;
-    srca[j] = p.a + static_cast<int64_t>(min(m0 + row, p.m - 1)) * p.lda + 8 * c;
-    srcb[j] = p.b + static_cast<int64_t>(min(n0 + row, p.n - 1)) * p.ldb + 8 * c;
+    offa[j] = static_cast<uint32_t>((static_cast<int64_t>(min(m0 + row, p.m - 1)) * p.lda + 8 * c) * 2);
+    offb[j] = static_cast<uint32_t>((static_cast<int64_t>(min(n0 + row, p.n - 1)) * p.ldb + 8 * c) * 2);
   }
   // half stage h: the A slice (h even) or the B slice (h odd) of step h / 2, in slot h % 5
   const int nh = 2 * (p.k / kBK);
   auto issue = [&](int h) {
-    if (h >= nh) return;
-    const uint32_t dst = lds_addr(g_gemm256 + (h % kBSlots) * kBHalfBytes) + wave * 1024;
+    if (h >= nh || !issuer) return;
+    const uint32_t dst = lds_addr(g_gemm256 + (h % kBSlots) * kBHalfBytes) + (wave & 3) * 1024;
     const int k0 = (h >> 1) * kBK;
     if (h & 1) {
+      const char* base = reinterpret_cast<const char*>(p.b + k0);
 #pragma unroll
-      for (int j = 0; j < kBCopies; ++j) dma16(srcb[j] + k0, dst + j * 8192);
+      for (int j = 0; j < kIss; ++j) dma16_off(base, offb[j], dst + j * 4096);
     } else {
+      const char* base = reinterpret_cast<const char*>(p.a + k0);
 #pragma unroll
-      for (int j = 0; j < kBCopies; ++j) dma16(srca[j] + k0, dst + j * 8192);
+      for (int j = 0; j < kIss; ++j) dma16_off(base, offa[j], dst + j * 4096);
     }
   };
 
@@ -395,7 +402,7 @@ __global__ __launch_bounds__(512) void gemm256_nt_kernel(GemmNT p) {
       for (int bn = 0; bn < 4; ++bn) acc[bm][bn] = mfma16x16x32(b[bn], a[bm], acc[bm][bn]);
   };
   // step 0 landed; half stages 2 .. 4 may fly
-  wait_vm_upto<kBCopies * (kBSlots - 2)>(kBCopies * (min(kBSlots, nh) - 2));
+  wait_vm_upto<2 * kBCopies * (kBSlots - 2)>(issuer ? 2 * kBCopies * (min(kBSlots, nh) - 2) : 0);
   lds_barrier();
   bf16x8 a0[8], b0[4], a1[8], b1[4];
   read_half(0, pos0, a0, b0);
@@ -405,7 +412,7 @@ __global__ __launch_bounds__(512) void gemm256_nt_kernel(GemmNT p) {
     if (i + 1 < nk) {
       // step i + 1 landed (half stage 2 i + 4 may fly); every wave is past
       // its reads of step i, whose slots take half stages 2 i + 5 and 2 i + 6
-      wait_vm_upto<kBCopies>(2 * i + 4 < nh ? kBCopies : 0);
+      wait_vm_upto<2 * kBCopies>(issuer && 2 * i + 4 < nh ? 2 * kBCopies : 0);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       lds_barrier();
       issue(2 * i + 5);
@@ -459,7 +466,10 @@ hipError_t launch_gemm_nt_mfma(const GemmNT& p0, bool rope, bool out_f32, hipStr
   const int64_t big = ((p.m + kBT - 1) / kBT) * static_cast<int64_t>((p.n + kBT - 1) / kBT);
   const int64_t small = ((p.m + kGT - 1) / kGT) * static_cast<int64_t>((p.n + kGT - 1) / kGT);
   const int64_t cost_big = (big + 255) / 256 * 4, cost_small = (small + 511) / 512 * 2;
-  if (p.k % kBK == 0 && big >= 256 && cost_big <= cost_small) {
+  // the 256 x 256 kernel addresses its copies with 32-bit offsets
+  const bool spans32 = static_cast<int64_t>(p.m) * p.lda * 2 < (int64_t{1} << 32) &&
+                       static_cast<int64_t>(p.n) * p.ldb * 2 < (int64_t{1} << 32);
+  if (p.k % kBK == 0 && big >= 256 && cost_big <= cost_small && spans32) {
     p.m_tiles = (p.m + kBT - 1) / kBT;
     p.n_tiles = (p.n + kBT - 1) / kBT;
     const dim3 grid(p.m_tiles * p.n_tiles);
