@@ -87,15 +87,29 @@ struct AttnMfma {
   int32_t pad[kBatchPerLaunch];
 };
 
+// Maxima of values that are never NaN (finite scores or -inf), as single
+// v_max3_f32 / v_max_f32: fmaxf would first quiet every operand the compiler
+// cannot prove canonical (lane swaps, selects), one extra VALU op each.
+__device__ __forceinline__ float max3_nn(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max_nn(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // Max over lanes i, i ^ 16, i ^ 32 and i ^ 48 by v_permlane16_swap and
 // v_permlane32_swap (VALU; a lane shuffle through ds_bpermute waits on LDS).
 // With both operands x, the 16-lane-row swap returns rows (0, 0, 2, 2) and
 // (1, 1, 3, 3) of x, the 32-lane swap the halves (lo, lo) and (hi, hi).
 __device__ __forceinline__ float max_lanes_xor16_32(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = max_nn(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return max_nn(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ int sigma(int m) {
@@ -217,30 +231,38 @@ __global__ __launch_bounds__(64 * kAWaves, kAWavesPerEu) void flash_attn_kernel(
           s[qb][tb] = mfma16x16x32(kf, __builtin_bit_cast(bf16x8, qreg[qb][ks]), s[qb][tb]);
       }
     }
+    // scaled scores; masked entries -inf.  One wave-uniform branch per tile
+    // for both query blocks: a tile every key of which every query of the
+    // wave sees takes no mask arithmetic at all.
+    float x[2][8];
+    if (k0 + kAK - 1 <= P + t_lo && k0 >= pad) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[qb][4 * tb + e] = s[qb][tb][e] * p.scale_log2;
+    } else {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = k0 + 16 * tb + sigma(4 * g + e);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            const bool vis = key >= pad && key <= P + t_q[qb];
+            x[qb][4 * tb + e] = vis ? s[qb][tb][e] * p.scale_log2 : -INFINITY;
+          }
+        }
+    }
     bf16x8 pb[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      float x[8];
-      if (k0 + kAK - 1 <= P + t_lo && k0 >= pad) {
-        // every key of the tile is visible to every query of the wave (a
-        // wave-uniform branch): no mask
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[4 * tb + e] = s[qb][tb][e] * p.scale_log2;
-      } else {
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int key = k0 + 16 * tb + sigma(4 * g + e);
-            const bool vis = key >= pad && key <= P + t_q[qb];
-            x[4 * tb + e] = vis ? s[qb][tb][e] * p.scale_log2 : -INFINITY;
-          }
-      }
-      float mt = x[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) mt = fmaxf(mt, x[e]);
+      // no score is NaN, so the maxima need no quieting of their operands
+      float mt = max3_nn(x[qb][0], x[qb][1], x[qb][2]);
+      mt = max3_nn(mt, x[qb][3], x[qb][4]);
+      mt = max3_nn(mt, x[qb][5], x[qb][6]);
+      mt = max_nn(mt, x[qb][7]);
       mt = max_lanes_xor16_32(mt);
       const bool move = mt > m_run[qb] + kSlack;
       if (__any(move)) {
@@ -254,7 +276,7 @@ __global__ __launch_bounds__(64 * kAWaves, kAWavesPerEu) void flash_attn_kernel(
       const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float pr = __builtin_amdgcn_exp2f(x[e] - m_use);
+        const float pr = __builtin_amdgcn_exp2f(x[qb][e] - m_use);
         l_run[qb] += pr;
         pb[qb][e] = static_cast<__bf16>(pr);
       }
