@@ -191,6 +191,24 @@ __global__ __launch_bounds__(64 * kAWaves, kAWavesPerEu) void flash_attn_kernel(
     for (int ks = 0; ks < kQk / 32; ++ks) qreg[qb][ks] = *reinterpret_cast<const f32x4*>(qrow + 32 * ks);
   }
   for (int t = 0; t < kAStages - 1 && t < nt; ++t) issue(t, t);
+  // Probabilities are exp2(fma(score, cs, -max)) with cs > 0 (the tile max
+  // of the raw scores times cs is the max of the scaled scores, rounding
+  // being monotonic).  A negative scale flips the sign of the queries instead
+  // (exact in bf16); a zero scale becomes the least normal float, whose
+  // products stay below 2^-24 in magnitude, so every visible key still gets
+  // weight exactly 1 while masked scores stay -inf.
+  float cs = p.scale_log2;
+  if (cs < 0.f) {
+    cs = -cs;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int ks = 0; ks < kQk / 32; ++ks)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          qreg[qb][ks][e] = __uint_as_float(__float_as_uint(qreg[qb][ks][e]) ^ 0x80008000u);
+  }
+  cs = fmaxf(cs, 1.17549435e-38f);
 
   const uint32_t k_frag = sigma(m) * kAKvRowBytes + g * 16;
   const uint32_t r_frag = kARopeOffset + sigma(m) * kARopeRowBytes + g * 16;
@@ -231,7 +249,7 @@ __global__ __launch_bounds__(64 * kAWaves, kAWavesPerEu) void flash_attn_kernel(
           s[qb][tb] = mfma16x16x32(kf, __builtin_bit_cast(bf16x8, qreg[qb][ks]), s[qb][tb]);
       }
     }
-    // scaled scores; masked entries -inf.  One wave-uniform branch per tile
+    // raw scores; masked entries -inf.  One wave-uniform branch per tile
     // for both query blocks: a tile every key of which every query of the
     // wave sees takes no mask arithmetic at all.
     float x[2][8];
@@ -241,7 +259,7 @@ __global__ __launch_bounds__(64 * kAWaves, kAWavesPerEu) void flash_attn_kernel(
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) x[qb][4 * tb + e] = s[qb][tb][e] * p.scale_log2;
+          for (int e = 0; e < 4; ++e) x[qb][4 * tb + e] = s[qb][tb][e];
     } else {
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
@@ -251,7 +269,7 @@ __global__ __launch_bounds__(64 * kAWaves, kAWavesPerEu) void flash_attn_kernel(
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb) {
             const bool vis = key >= pad && key <= P + t_q[qb];
-            x[qb][4 * tb + e] = vis ? s[qb][tb][e] * p.scale_log2 : -INFINITY;
+            x[qb][4 * tb + e] = vis ? s[qb][tb][e] : -INFINITY;
           }
         }
     }
@@ -263,7 +281,7 @@ __global__ __launch_bounds__(64 * kAWaves, kAWavesPerEu) void flash_attn_kernel(
       mt = max3_nn(mt, x[qb][3], x[qb][4]);
       mt = max3_nn(mt, x[qb][5], x[qb][6]);
       mt = max_nn(mt, x[qb][7]);
-      mt = max_lanes_xor16_32(mt);
+      mt = max_lanes_xor16_32(mt) * cs;
       const bool move = mt > m_run[qb] + kSlack;
       if (__any(move)) {
         const float alpha = move ? __builtin_amdgcn_exp2f(m_run[qb] - mt) : 1.f;
@@ -276,7 +294,7 @@ __global__ __launch_bounds__(64 * kAWaves, kAWavesPerEu) void flash_attn_kernel(
       const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float pr = __builtin_amdgcn_exp2f(x[qb][e] - m_use);
+        const float pr = __builtin_amdgcn_exp2f(fmaf(x[qb][e], cs, -m_use));
         l_run[qb] += pr;
         pb[qb][e] = static_cast<__bf16>(pr);
       }
