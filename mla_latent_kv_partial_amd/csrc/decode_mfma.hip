@@ -67,7 +67,7 @@ __shared__ __attribute__((aligned(1024))) char g_stage[kStages * kStageBytes];
 __shared__ __attribute__((aligned(16))) char g_p[2][kMaxHeadGroups][kWave * 16];   // P operands, by tile parity
 __shared__ float g_alpha[2][kMaxHeadGroups][16];                                     // rescale factor per head
 __shared__ int g_moved[2][kMaxHeadGroups];                                           // any rescale in the wave
-__shared__ float g_l[kMaxHeadGroups][16];                                            // softmax denominators
+__shared__ float g_inv[kMaxHeadGroups][16];                                          // 1 / softmax denominator
 
 // Max over lanes i, i ^ 16, i ^ 32 and i ^ 48 by v_permlane16_swap and
 // v_permlane32_swap (VALU; a lane shuffle through ds_bpermute waits on LDS).
@@ -490,7 +490,7 @@ struct Decode {
       l_tot += __shfl_xor(l_tot, 32, kWave);
       if (g == 0) {
         const int64_t ps = (static_cast<int64_t>(b) * p.heads + head) * p.s_max + s;
-        g_l[hw][h] = l_tot;
+        g_inv[hw][h] = l_tot > 0.f ? 1.f / l_tot : 0.f;
         p.part_lse[ps] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
       }
     }
@@ -501,13 +501,19 @@ struct Decode {
     wait_vm<0>();
     lds_barrier();   // every wave's copies have landed: the stages are free
     if (!SC) {
-      // O^T leaves through LDS so that every store instruction writes two
-      // whole 512-byte partial rows: the wave's region holds its dims of every
-      // head, one row per head padded to an odd number of 32-byte units.  The
-      // stores are non-temporal.
+      // O^T leaves through LDS so that every store instruction writes whole
+      // partial rows: the wave's region holds its dims of every head, one row
+      // per head padded to an odd number of 32-byte units.  Each lane then
+      // normalises 8 consecutive dims (one 16-byte store of bf16, two of
+      // fp32); the per-head reciprocal comes from the score waves, the row
+      // addresses advance by a fixed stride, and bf16 rounding is the
+      // hardware's round-to-nearest-even conversion.  The stores are
+      // non-temporal: the burst at the end of the launch does not wait on the
+      // caches (3-4 us less per 169 MB launch, measured).
       constexpr int kEpiDims = kR / NW;
       constexpr int kEpiRow = kEpiDims * 4 + 32;
-      constexpr int kChunksPerRow = kEpiDims / 4;
+      constexpr int kLanesPerRow = kEpiDims / 8;
+      constexpr int kRowsPerIter = kWave / kLanesPerRow;
       char* region = g_stage + hw * (16 * NW * kEpiRow);
 #pragma unroll
       for (int hb = 0; hb < NW; ++hb)
@@ -515,24 +521,28 @@ struct Decode {
         for (int db = 0; db < kCtxBlocks; ++db)
           *reinterpret_cast<f32x4*>(region + (16 * hb + h) * kEpiRow + (16 * db + 4 * g) * 4) = reg[db * NW + hb];
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave reads back its own writes
+      const int r0 = lane / kLanesPerRow, c8 = lane % kLanesPerRow;
+      const int64_t row_step = static_cast<int64_t>(kRowsPerIter) * p.s_max * kR;   // elements
+      int64_t e = ((static_cast<int64_t>(b) * p.heads + head0 + r0) * p.s_max + s) * kR + kEpiDims * hw + 8 * c8;
 #pragma unroll 4
-      for (int k = 0; k < 16 * NW * kChunksPerRow / kWave; ++k) {
-        const int q = k * kWave + lane;
-        const int row = q / kChunksPerRow, c = q - row * kChunksPerRow;
-        const float l_tot = g_l[row >> 4][row & 15];
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(region + row * kEpiRow + c * 16) * inv;
-        const int64_t ps = (static_cast<int64_t>(b) * p.heads + head0 + row) * p.s_max + s;
-        // non-temporal: the burst at the end of the launch does not wait on
-        // the caches (3-4 us less per 169 MB launch, measured)
-        const int64_t e = ps * kR + kEpiDims * hw + 4 * c;
+      for (int k = 0; k < 16 * NW / kRowsPerIter; ++k, e += row_step) {
+        const int row = k * kRowsPerIter + r0;
+        const float inv = g_inv[row >> 4][row & 15];
+        const char* src = region + row * kEpiRow + c8 * 32;
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(src) * inv;
+        const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + 16) * inv;
         if (p.part_bf16) {
-          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-          const u32x2 pk = {static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16),
-                            static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16)};
-          __builtin_nontemporal_store(pk, reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.part_o) + e));
+          bf16x8 o;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            o[j] = static_cast<__bf16>(v0[j]);
+            o[4 + j] = static_cast<__bf16>(v1[j]);
+          }
+          __builtin_nontemporal_store(__builtin_bit_cast(f32x4, o),
+                                      reinterpret_cast<f32x4*>(static_cast<uint16_t*>(p.part_o) + e));
         } else {
-          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(static_cast<float*>(p.part_o) + e));
+          __builtin_nontemporal_store(v0, reinterpret_cast<f32x4*>(static_cast<float*>(p.part_o) + e));
+          __builtin_nontemporal_store(v1, reinterpret_cast<f32x4*>(static_cast<float*>(p.part_o) + e + 4));
         }
       }
     }
