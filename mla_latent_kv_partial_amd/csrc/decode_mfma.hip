@@ -503,44 +503,59 @@ struct Decode {
     if (!SC) {
       // O^T leaves through LDS so that every store instruction writes whole
       // partial rows: the wave's region holds its dims of every head, one row
-      // per head padded to an odd number of 32-byte units.  Each lane then
-      // normalises 8 consecutive dims (one 16-byte store of bf16, two of
-      // fp32); the per-head reciprocal comes from the score waves, the row
-      // addresses advance by a fixed stride, and bf16 rounding is the
-      // hardware's round-to-nearest-even conversion.  The stores are
+      // per head padded to an odd number of 32-byte units, and each lane
+      // stores 8 consecutive dims (one 16-byte store of bf16, two of fp32).
+      // The per-head reciprocal comes from the score waves, the row addresses
+      // advance by a fixed stride, and bf16 rounding is the hardware's
+      // round-to-nearest-even conversion.  The stores are
       // non-temporal: the burst at the end of the launch does not wait on the
       // caches (3-4 us less per 169 MB launch, measured).
       constexpr int kEpiDims = kR / NW;
-      constexpr int kEpiRow = kEpiDims * 4 + 32;
       constexpr int kLanesPerRow = kEpiDims / 8;
       constexpr int kRowsPerIter = kWave / kLanesPerRow;
-      char* region = g_stage + hw * (16 * NW * kEpiRow);
-#pragma unroll
-      for (int hb = 0; hb < NW; ++hb)
-#pragma unroll
-        for (int db = 0; db < kCtxBlocks; ++db)
-          *reinterpret_cast<f32x4*>(region + (16 * hb + h) * kEpiRow + (16 * db + 4 * g) * 4) = reg[db * NW + hb];
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave reads back its own writes
       const int r0 = lane / kLanesPerRow, c8 = lane % kLanesPerRow;
       const int64_t row_step = static_cast<int64_t>(kRowsPerIter) * p.s_max * kR;   // elements
       int64_t e = ((static_cast<int64_t>(b) * p.heads + head0 + r0) * p.s_max + s) * kR + kEpiDims * hw + 8 * c8;
-#pragma unroll 4
-      for (int k = 0; k < 16 * NW / kRowsPerIter; ++k, e += row_step) {
-        const int row = k * kRowsPerIter + r0;
-        const float inv = g_inv[row >> 4][row & 15];
-        const char* src = region + row * kEpiRow + c8 * 32;
-        const f32x4 v0 = *reinterpret_cast<const f32x4*>(src) * inv;
-        const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + 16) * inv;
-        if (p.part_bf16) {
-          bf16x8 o;
+      if (p.part_bf16) {
+        // bf16 partials: normalise and round in registers, so the LDS round
+        // trip carries half the bytes
+        constexpr int kEpiRow = kEpiDims * 2 + 32;
+        char* region = g_stage + hw * (16 * NW * kEpiRow);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            o[j] = static_cast<__bf16>(v0[j]);
-            o[4 + j] = static_cast<__bf16>(v1[j]);
+        for (int hb = 0; hb < NW; ++hb) {
+          const float inv = g_inv[hb][h];
+#pragma unroll
+          for (int db = 0; db < kCtxBlocks; ++db) {
+            const f32x4 v = reg[db * NW + hb] * inv;
+            bf16x4 o;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[j] = static_cast<__bf16>(v[j]);
+            *reinterpret_cast<bf16x4*>(region + (16 * hb + h) * kEpiRow + (16 * db + 4 * g) * 2) = o;
           }
-          __builtin_nontemporal_store(__builtin_bit_cast(f32x4, o),
-                                      reinterpret_cast<f32x4*>(static_cast<uint16_t*>(p.part_o) + e));
-        } else {
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave reads back its own writes
+#pragma unroll 4
+        for (int k = 0; k < 16 * NW / kRowsPerIter; ++k, e += row_step) {
+          const int row = k * kRowsPerIter + r0;
+          const f32x4 v = *reinterpret_cast<const f32x4*>(region + row * kEpiRow + c8 * 16);
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(static_cast<uint16_t*>(p.part_o) + e));
+        }
+      } else {
+        constexpr int kEpiRow = kEpiDims * 4 + 32;
+        char* region = g_stage + hw * (16 * NW * kEpiRow);
+#pragma unroll
+        for (int hb = 0; hb < NW; ++hb)
+#pragma unroll
+          for (int db = 0; db < kCtxBlocks; ++db)
+            *reinterpret_cast<f32x4*>(region + (16 * hb + h) * kEpiRow + (16 * db + 4 * g) * 4) = reg[db * NW + hb];
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave reads back its own writes
+#pragma unroll 4
+        for (int k = 0; k < 16 * NW / kRowsPerIter; ++k, e += row_step) {
+          const int row = k * kRowsPerIter + r0;
+          const float inv = g_inv[row >> 4][row & 15];
+          const char* src = region + row * kEpiRow + c8 * 32;
+          const f32x4 v0 = *reinterpret_cast<const f32x4*>(src) * inv;
+          const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + 16) * inv;
           __builtin_nontemporal_store(v0, reinterpret_cast<f32x4*>(static_cast<float*>(p.part_o) + e));
           __builtin_nontemporal_store(v1, reinterpret_cast<f32x4*>(static_cast<float*>(p.part_o) + e + 4));
         }
