@@ -222,22 +222,17 @@ __device__ __forceinline__ void block_minmax(uint32_t lo, uint32_t hi, uint32_t*
   }
 }
 
-__global__ __launch_bounds__(kTT) void dsa_topk_kernel(TopkParams p) {
+// The one-workgroup selection of a whole row of n scores at sc into out
+// (whole-block call).  LDS: hist (4096 bins), two scalars, kTW wave totals and
+// three rows of kTW wave counts.
+__device__ __forceinline__ void select_row(const float* sc, int n, uint32_t k, int32_t* out, uint32_t* hist,
+                                           uint32_t* s_prefix, uint32_t* s_rank, uint32_t* s_wtot,
+                                           int (*s_tot)[kTW]) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const int row = p.row[blockIdx.x];
-  const int n = p.len[blockIdx.x];
-  const float* sc = p.scores + static_cast<int64_t>(row) * p.stride;
-  int32_t* out = p.sel_idx + p.out_off[blockIdx.x];
-  const uint32_t k = static_cast<uint32_t>(p.top_k);
   // whole 16-byte groups: an aligned row whose length is a multiple of 4
   const bool vec4 = (reinterpret_cast<uintptr_t>(sc) & 15) == 0 && (n & 3) == 0;
-
-  __shared__ uint32_t hist[4096];
-  __shared__ uint32_t s_prefix, s_rank;
-  __shared__ uint32_t s_wtot[kTW];
-  __shared__ int s_tot[3][kTW];
 
   // ---- 1. radix select of the k-th smallest key: digits of 12, 12 and 8 bits
   // from the top (12-bit digits spread the sign-and-exponent-heavy top bits
@@ -287,10 +282,10 @@ __global__ __launch_bounds__(kTT) void dsa_topk_kernel(TopkParams p) {
       }
     }
     __syncthreads();
-    locate_digit(hist, nb, rank, prefix, shift, &s_prefix, &s_rank, s_wtot);
+    locate_digit(hist, nb, rank, prefix, shift, s_prefix, s_rank, s_wtot);
     __syncthreads();
-    prefix = s_prefix;
-    rank = s_rank;
+    prefix = *s_prefix;
+    rank = *s_rank;
     mask |= digit << shift;
     __syncthreads();
   }
@@ -360,10 +355,40 @@ __global__ __launch_bounds__(kTT) void dsa_topk_kernel(TopkParams p) {
   }
 }
 
-// ---- two-stage form.  Workspace of launch row i (kTopkRowWsBytes): keys of
-// the candidates [kTopkMaxCand] uint32, their positions [kTopkMaxCand] int32,
-// then the candidate count of each segment [kTopkMaxSegs] int32.  Segment s
-// writes its candidates from s * top_k.
+__global__ __launch_bounds__(kTT) void dsa_topk_kernel(TopkParams p) {
+  __shared__ uint32_t hist[4096];
+  __shared__ uint32_t s_prefix, s_rank;
+  __shared__ uint32_t s_wtot[kTW];
+  __shared__ int s_tot[3][kTW];
+  select_row(p.scores + static_cast<int64_t>(p.row[blockIdx.x]) * p.stride, p.len[blockIdx.x],
+             static_cast<uint32_t>(p.top_k), p.sel_idx + p.out_off[blockIdx.x], hist, &s_prefix, &s_rank, s_wtot,
+             s_tot);
+}
+
+// ---- multi-workgroup form, three launches.  Segments of kPrSeg scores.
+//   1. bound: segment i of a row of n scores finds t_i, its r_i-th smallest
+//      key, r_i = ceil(top_k len_i / n).  Every segment holds r_i keys <= t_i
+//      and the r_i add up to at least top_k, so at least top_k keys of the row
+//      are <= T = max_i t_i: K* <= T, and no key above T is selected.
+//   2. prune: segment i writes its keys <= T (the survivors, typically a few
+//      percent of the row) with their positions, in ascending position order,
+//      and their count.
+//   3. final: one workgroup per row gathers the survivors of its segments
+//      (ascending positions) into LDS and runs the select and the two sweeps
+//      of the one-workgroup form over them: every key <= K* survives, so K*,
+//      m and the output are the row's.  A segment with more survivors than
+//      its area holds (long runs of equal scores) sends its row through the
+//      one-workgroup form instead, in the same launch.
+// Workspace of launch row i (kTopkRowWsBytes): survivor keys [kTopkMaxCand]
+// uint32, their positions [kTopkMaxCand] int32 (segment s from s * kPrCap),
+// then per segment its survivor count [kPrMaxSegs] int32 and t_s
+// [kPrMaxSegs] uint32.
+constexpr int kPrSeg = 8192;
+constexpr int kPrMaxSegs = 16;
+constexpr int kPrCap = kTopkMaxCand / kPrMaxSegs;   // survivors a segment's area holds
+static_assert(kPrSeg * kPrMaxSegs >= kTopkSeg * kTopkMaxSegs, "the segments cover the rows of this form");
+static_assert(kTopkMaxCand * 8 + 8 * kPrMaxSegs <= static_cast<int>(kTopkRowWsBytes), "workspace of a row");
+
 __device__ __forceinline__ uint32_t* ws_keys(const TopkParams& p, int i) {
   return reinterpret_cast<uint32_t*>(p.ws + static_cast<size_t>(i) * kTopkRowWsBytes);
 }
@@ -373,8 +398,12 @@ __device__ __forceinline__ int32_t* ws_pos(const TopkParams& p, int i) {
 __device__ __forceinline__ int32_t* ws_cnt(const TopkParams& p, int i) {
   return reinterpret_cast<int32_t*>(p.ws + static_cast<size_t>(i) * kTopkRowWsBytes + kTopkMaxCand * 8);
 }
+__device__ __forceinline__ uint32_t* ws_bound(const TopkParams& p, int i) {
+  return reinterpret_cast<uint32_t*>(p.ws + static_cast<size_t>(i) * kTopkRowWsBytes + kTopkMaxCand * 8 +
+                                     4 * kPrMaxSegs);
+}
 
-// The bucket select of the two-stage kernels, fused with the per-wave counts
+// The bucket select of the multi-workgroup kernels, fused with the per-wave counts
 // of the order-keeping sweep that follows it.  Wave w owns the run
 // [w_lo, w_hi) of the n keys.  On success: K* and m, and for every wave the
 // number of its keys in buckets below K*'s (their scores exceed the
@@ -403,9 +432,11 @@ __device__ __forceinline__ bool bucket_select_runs(const uint32_t* keys, int n, 
       const int i = i0 + u * kTT;
       kk[u] = i < n ? keys[i] : 0u;
     }
+    // past n: no atomic (a short candidate list would otherwise pile its idle
+    // lanes' atomics onto one bin)
 #pragma unroll
-    for (int u = 0; u < kSweep; ++u)   // past n: add 0 to some bin, no branch
-      atomicAdd(&hist[score_bucket(kk[u], vmax, scale)], i0 + u * kTT < n ? 1u : 0u);
+    for (int u = 0; u < kSweep; ++u)
+      if (i0 + u * kTT < n) atomicAdd(&hist[score_bucket(kk[u], vmax, scale)], 1u);
   }
   __syncthreads();
   locate_digit(hist, kBuckets, k, 0u, 0, s_prefix, s_rank, wtot);
@@ -456,38 +487,22 @@ __device__ __forceinline__ bool bucket_select_runs(const uint32_t* keys, int n, 
   return true;
 }
 
-// A: the top_k of one segment, written in ascending position order.
-__global__ __launch_bounds__(kTT) void dsa_topk_segment_kernel(TopkParams p) {
-  const int seg = blockIdx.x, i_row = blockIdx.y;
-  const int n = p.len[i_row];
-  const int lo = seg * kTopkSeg;
-  if (lo >= n) return;   // the row has fewer segments (uniform)
-  const int len = min(kTopkSeg, n - lo);
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const float* sc = p.scores + static_cast<int64_t>(p.row[i_row]) * p.stride + lo;
-  const uint32_t k = static_cast<uint32_t>(p.top_k);
-  uint32_t* out_key = ws_keys(p, i_row) + static_cast<int64_t>(seg) * p.top_k;
-  int32_t* out_pos = ws_pos(p, i_row) + static_cast<int64_t>(seg) * p.top_k;
-
-  __shared__ __attribute__((aligned(16))) uint32_t keys[kTopkSeg];
-  __shared__ uint32_t hist[kBuckets];   // the histogram, then the staged output
-  __shared__ uint32_t small[kSmallCap];
-  __shared__ uint16_t small_at[kSmallCap];
-  __shared__ uint32_t s_prefix, s_rank, s_cnt;
-  __shared__ uint32_t s_wtot[kTW];
-  __shared__ uint32_t s_mm[2 * kTW];
-  __shared__ int s_tot[2][kTW];   // per wave: keys below K*, keys equal to K*
-  uint32_t klo = 0xffffffffu, khi = 0u;
+// The keys of a segment's len scores at sc into keys[] (LDS); klo / khi: this
+// thread's minimum and maximum.
+__device__ __forceinline__ void load_segment_keys(const float* sc, int len, uint32_t* keys, uint32_t& klo,
+                                                  uint32_t& khi) {
+  const int tid = threadIdx.x;
+  klo = 0xffffffffu;
+  khi = 0u;
   if ((reinterpret_cast<uintptr_t>(sc) & 15) == 0 && (len & 3) == 0) {
-    // 16-byte loads, all in flight before the first LDS store
-    float4 v[kTopkSeg / (4 * kTT)];
+    float4 v[kPrSeg / (4 * kTT)];
 #pragma unroll
-    for (int u = 0; u < kTopkSeg / (4 * kTT); ++u) {
+    for (int u = 0; u < kPrSeg / (4 * kTT); ++u) {
       const int i = 4 * (u * kTT + tid);
       v[u] = i < len ? *reinterpret_cast<const float4*>(sc + i) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
-    for (int u = 0; u < kTopkSeg / (4 * kTT); ++u) {
+    for (int u = 0; u < kPrSeg / (4 * kTT); ++u) {
       const int i = 4 * (u * kTT + tid);
       if (i < len) {
         const uint4 q = make_uint4(rank_key(v[u].x), rank_key(v[u].y), rank_key(v[u].z), rank_key(v[u].w));
@@ -497,14 +512,14 @@ __global__ __launch_bounds__(kTT) void dsa_topk_segment_kernel(TopkParams p) {
       }
     }
   } else {
-    float v[kTopkSeg / kTT];
+    float v[kPrSeg / kTT];
 #pragma unroll
-    for (int u = 0; u < kTopkSeg / kTT; ++u) {
+    for (int u = 0; u < kPrSeg / kTT; ++u) {
       const int i = u * kTT + tid;
       v[u] = i < len ? sc[i] : 0.f;
     }
 #pragma unroll
-    for (int u = 0; u < kTopkSeg / kTT; ++u) {
+    for (int u = 0; u < kPrSeg / kTT; ++u) {
       const int i = u * kTT + tid;
       if (i < len) {
         const uint32_t key = rank_key(v[u]);
@@ -514,114 +529,106 @@ __global__ __launch_bounds__(kTT) void dsa_topk_segment_kernel(TopkParams p) {
       }
     }
   }
+}
+
+// 1. bound
+__global__ __launch_bounds__(kTT) void dsa_topk_bound_kernel(TopkParams p) {
+  const int seg = blockIdx.x, i_row = blockIdx.y;
+  const int n = p.len[i_row];
+  const int lo = seg * kPrSeg;
+  if (lo >= n) return;   // the row has fewer segments (uniform)
+  const int len = min(kPrSeg, n - lo);
+  const int tid = threadIdx.x, wave = tid / kWave;
+  const float* sc = p.scores + static_cast<int64_t>(p.row[i_row]) * p.stride + lo;
+  // 1 <= r <= len, as top_k < n
+  const uint32_t r = static_cast<uint32_t>((static_cast<int64_t>(p.top_k) * len + n - 1) / n);
+
+  __shared__ __attribute__((aligned(16))) uint32_t keys[kPrSeg];
+  __shared__ uint32_t hist[kBuckets];
+  __shared__ uint32_t small[kSmallCap];
+  __shared__ uint16_t small_at[kSmallCap];
+  __shared__ uint32_t s_prefix, s_rank, s_cnt;
+  __shared__ uint32_t s_wtot[kTW];
+  __shared__ uint32_t s_mm[2 * kTW];
+  __shared__ int s_below[kTW];
+  uint32_t klo, khi;
+  load_segment_keys(sc, len, keys, klo, khi);
   for (int i = tid; i < kBuckets; i += kTT) hist[i] = 0;
   if (tid == 0) s_cnt = 0;
-  if (tid < kTW) s_tot[1][tid] = 0;
-  if (static_cast<uint32_t>(len) <= k) {   // the whole segment is a candidate (uniform)
-    __syncthreads();
-    for (int i = tid; i < len; i += kTT) {
-      out_key[i] = keys[i];
-      out_pos[i] = lo + i;
-    }
-    if (tid == 0) ws_cnt(p, i_row)[seg] = len;
-    return;
-  }
-  uint32_t kmin, kmax, kstar = 0;
+  uint32_t kmin, kmax, t = 0;
   int m = 0, c = 0;
   block_minmax(klo, khi, s_mm, kmin, kmax);   // its barrier publishes the keys and the zeroed counters
   const int per_wave = ((len + kTW - 1) / kTW + kWave - 1) / kWave * kWave;
   const int w_lo = min(len, wave * per_wave), w_hi = min(len, w_lo + per_wave);
-  if (bucket_select_runs(keys, len, k, kmin, kmax, w_lo, w_hi, hist, small, small_at, &s_prefix, &s_rank, s_wtot,
-                         &s_cnt, s_tot[0], kstar, m, c)) {
-    // K*'s bucket: its keys below K* and equal to K*, counted for their waves
-    for (int t = tid; t < c; t += kTT) {
-      const uint32_t kt = small[t];
-      const int w = small_at[t] / per_wave;
-      if (kt < kstar)
-        atomicAdd(&s_tot[0][w], 1);
-      else if (kt == kstar)
-        atomicAdd(&s_tot[1][w], 1);
-    }
-  } else {
-    lds_radix_select(keys, len, k, hist, &s_prefix, &s_rank, s_wtot, kstar, m);
-    int cb = 0, ct = 0;
-    for (int i0 = w_lo; i0 < w_hi; i0 += kSweep * kWave) {
-      uint32_t kk[kSweep];
-#pragma unroll
-      for (int u = 0; u < kSweep; ++u) {
-        const int i = i0 + u * kWave + lane;
-        kk[u] = i < w_hi ? keys[i] : 0xffffffffu;
-      }
-#pragma unroll
-      for (int u = 0; u < kSweep; ++u) {
-        const bool ok = i0 + u * kWave + lane < w_hi;
-        cb += __popcll(__ballot(ok && kk[u] < kstar));
-        ct += __popcll(__ballot(ok && kk[u] == kstar));
-      }
-    }
-    if (lane == 0) {
-      s_tot[0][wave] = cb;
-      s_tot[1][wave] = ct;
-    }
-  }
-  __syncthreads();
-  int rb = 0, rt = 0;
-  for (int w = 0; w < wave; ++w) {
-    rb += s_tot[0][w];
-    rt += s_tot[1][w];
-  }
-  // order-keeping compaction: a selected position lands at (keys below K*
-  // before it) + min(ties before it, m); staged in LDS (the histogram's
-  // space) when it holds top_k pairs, so the stores leave as whole rows
-  const bool stage = 2 * k <= static_cast<uint32_t>(kBuckets);
-  uint32_t* st_key = hist;
-  uint32_t* st_pos = hist + k;
-  for (int i0 = w_lo; i0 < w_hi; i0 += kSweep * kWave) {
-    uint32_t kk[kSweep];
-#pragma unroll
-    for (int u = 0; u < kSweep; ++u) {
-      const int i = i0 + u * kWave + lane;
-      kk[u] = i < w_hi ? keys[i] : 0xffffffffu;
-    }
-#pragma unroll
-    for (int u = 0; u < kSweep; ++u) {
-      const int i = i0 + u * kWave + lane;
-      const bool ok = i < w_hi;
-      const uint32_t key = kk[u];
-      const bool fb = ok && key < kstar, ft = ok && key == kstar;
-      const uint64_t bb = __ballot(fb), bt = __ballot(ft);
-      const int b_before = rb + lanes_below(bb), t_before = rt + lanes_below(bt);
-      int dst = -1;
-      if (fb) dst = b_before + min(t_before, m);
-      if (ft && t_before < m) dst = b_before + t_before;
-      if (dst >= 0 && dst < static_cast<int>(k)) {
-        if (stage) {
-          st_key[dst] = key;
-          st_pos[dst] = static_cast<uint32_t>(lo + i);
-        } else {
-          out_key[dst] = key;
-          out_pos[dst] = lo + i;
-        }
-      }
-      rb += __popcll(bb);
-      rt += __popcll(bt);
-    }
-  }
-  if (stage) {
-    __syncthreads();
-    for (int e = tid; e < static_cast<int>(k); e += kTT) {
-      out_key[e] = st_key[e];
-      out_pos[e] = static_cast<int32_t>(st_pos[e]);
-    }
-  }
-  if (tid == 0) ws_cnt(p, i_row)[seg] = p.top_k;
+  if (!bucket_select_runs(keys, len, r, kmin, kmax, w_lo, w_hi, hist, small, small_at, &s_prefix, &s_rank, s_wtot,
+                          &s_cnt, s_below, t, m, c))
+    lds_radix_select(keys, len, r, hist, &s_prefix, &s_rank, s_wtot, t, m);
+  if (tid == 0) ws_bound(p, i_row)[seg] = t;
 }
 
-// B: the row's selection among the segments' candidates, in the page's order.
-__global__ __launch_bounds__(kTT) void dsa_topk_merge_kernel(TopkParams p) {
+// 2. prune.  Wave w owns positions [512 w, 512 w + 512) of the segment; a
+// survivor's slot is the survivors of the lower waves plus those before it
+// in its wave.
+__global__ __launch_bounds__(kTT) void dsa_topk_prune_kernel(TopkParams p) {
+  constexpr int kPer = kPrSeg / kTT;   // 8 scores per lane
+  const int seg = blockIdx.x, i_row = blockIdx.y;
+  const int n = p.len[i_row];
+  const int lo = seg * kPrSeg;
+  if (lo >= n) return;   // uniform
+  const int len = min(kPrSeg, n - lo);
+  const int segs = (n + kPrSeg - 1) / kPrSeg;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const float* sc = p.scores + static_cast<int64_t>(p.row[i_row]) * p.stride + lo;
+  __shared__ int s_cnt[kTW];
+  // all bounds requested at once (a fixed trip count: one batch of loads, not
+  // one round trip per segment)
+  const uint32_t* bound = ws_bound(p, i_row);
+  uint32_t tmax = 0u;
+#pragma unroll
+  for (int s = 0; s < kPrMaxSegs; ++s) tmax = max(tmax, s < segs ? bound[s] : 0u);
+  uint32_t key[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = wave * (kPer * kWave) + u * kWave + lane;
+    key[u] = i < len ? rank_key(sc[i]) : 0xffffffffu;
+  }
+  int cnt = 0;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = wave * (kPer * kWave) + u * kWave + lane;
+    cnt += __popcll(__ballot(i < len && key[u] <= tmax));
+  }
+  if (lane == 0) s_cnt[wave] = cnt;
+  __syncthreads();
+  int at = 0, total = 0;
+  for (int w = 0; w < kTW; ++w) {
+    if (w < wave) at += s_cnt[w];
+    total += s_cnt[w];
+  }
+  uint32_t* out_key = ws_keys(p, i_row) + seg * kPrCap;
+  int32_t* out_pos = ws_pos(p, i_row) + seg * kPrCap;
+  if (total <= kPrCap) {   // uniform
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = wave * (kPer * kWave) + u * kWave + lane;
+      const bool keep = i < len && key[u] <= tmax;
+      const uint64_t b = __ballot(keep);
+      if (keep) {
+        const int d = at + lanes_below(b);
+        out_key[d] = key[u];
+        out_pos[d] = lo + i;
+      }
+      at += __popcll(b);
+    }
+  }
+  if (tid == 0) ws_cnt(p, i_row)[seg] = total;
+}
+
+// 3. final: the row's selection among the survivors, in the page's order.
+__global__ __launch_bounds__(kTT) void dsa_topk_final_kernel(TopkParams p) {
   const int i_row = blockIdx.x;
   const int n = p.len[i_row];
-  const int segs = (n + kTopkSeg - 1) / kTopkSeg;
+  const int segs = (n + kPrSeg - 1) / kPrSeg;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const uint32_t k = static_cast<uint32_t>(p.top_k);
   int32_t* out = p.sel_idx + p.out_off[i_row];
@@ -635,31 +642,47 @@ __global__ __launch_bounds__(kTT) void dsa_topk_merge_kernel(TopkParams p) {
   __shared__ uint32_t s_wtot[kTW];
   __shared__ uint32_t s_mm[2 * kTW];
   __shared__ int s_tot[3][kTW];   // per wave: class 0, other keys below K*, keys equal to K*
-  // Every segment but the last is longer than top_k (16384 > 8192 >= top_k)
-  // and wrote exactly top_k candidates from s * top_k, so the candidates are
-  // one contiguous run of (segs - 1) * top_k + the last segment's count.
-  const int c_total = (segs - 1) * p.top_k + ws_cnt(p, i_row)[segs - 1];
+  // survivors per segment (uniform: every thread reads the same counts; all
+  // requested at once)
+  const int32_t* cnt = ws_cnt(p, i_row);
+  int cs[kPrMaxSegs];
+  int c_total = 0;
+  bool overflow = false;
+#pragma unroll
+  for (int s = 0; s < kPrMaxSegs; ++s) {
+    cs[s] = s < segs ? cnt[s] : 0;
+    overflow |= cs[s] > kPrCap;
+    c_total += cs[s];
+  }
+  if (overflow) {
+    select_row(p.scores + static_cast<int64_t>(p.row[i_row]) * p.stride, n, k, out, hist, &s_prefix, &s_rank, s_wtot,
+               s_tot);
+    return;
+  }
+  // thread t takes survivor t of every segment (at most kPrCap = kTT each):
+  // every load in flight before the first LDS store
+  static_assert(kPrCap <= kTT, "one survivor per thread and segment");
   uint32_t klo = 0xffffffffu, khi = 0u;
   {
     const uint32_t* ks = ws_keys(p, i_row);
     const int32_t* ps = ws_pos(p, i_row);
-    uint32_t kv[kTopkMaxCand / kTT];
-    int32_t pv[kTopkMaxCand / kTT];
+    uint32_t kv[kPrMaxSegs];
+    int32_t pv[kPrMaxSegs];
 #pragma unroll
-    for (int u = 0; u < kTopkMaxCand / kTT; ++u) {
-      const int i = u * kTT + tid;
-      kv[u] = i < c_total ? ks[i] : 0u;
-      pv[u] = i < c_total ? ps[i] : 0;
+    for (int s = 0; s < kPrMaxSegs; ++s) {
+      kv[s] = tid < cs[s] ? ks[s * kPrCap + tid] : 0u;
+      pv[s] = tid < cs[s] ? ps[s * kPrCap + tid] : 0;
     }
+    int base = 0;
 #pragma unroll
-    for (int u = 0; u < kTopkMaxCand / kTT; ++u) {
-      const int i = u * kTT + tid;
-      if (i < c_total) {
-        ckey[i] = kv[u];
-        cpos[i] = pv[u];
-        klo = min(klo, kv[u]);
-        khi = max(khi, kv[u]);
+    for (int s = 0; s < kPrMaxSegs; ++s) {
+      if (tid < cs[s]) {
+        ckey[base + tid] = kv[s];
+        cpos[base + tid] = pv[s];
+        klo = min(klo, kv[s]);
+        khi = max(khi, kv[s]);
       }
+      base += cs[s];
     }
   }
   for (int i = tid; i < kBuckets; i += kTT) hist[i] = 0;
@@ -776,10 +799,13 @@ bool dsa_topk_two_stage(int64_t n, int32_t top_k) {
 
 hipError_t launch_dsa_topk_two_stage(const TopkParams& p, hipStream_t stream) {
   if (p.rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(dsa_topk_segment_kernel, dim3(kTopkMaxSegs, p.rows), dim3(kTT), 0, stream, p);
+  hipLaunchKernelGGL(dsa_topk_bound_kernel, dim3(kPrMaxSegs, p.rows), dim3(kTT), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(dsa_topk_merge_kernel, dim3(p.rows), dim3(kTT), 0, stream, p);
+  hipLaunchKernelGGL(dsa_topk_prune_kernel, dim3(kPrMaxSegs, p.rows), dim3(kTT), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(dsa_topk_final_kernel, dim3(p.rows), dim3(kTT), 0, stream, p);
   return hipGetLastError();
 }
 
