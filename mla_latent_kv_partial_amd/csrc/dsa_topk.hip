@@ -433,10 +433,13 @@ __device__ __forceinline__ bool bucket_select_runs(const uint32_t* keys, int n, 
       kk[u] = i < n ? keys[i] : 0u;
     }
     // past n: no atomic (a short candidate list would otherwise pile its idle
-    // lanes' atomics onto one bin)
+    // lanes' atomics onto one bin), and no work at all once the whole wave is
+    // past n (wave-uniform)
 #pragma unroll
-    for (int u = 0; u < kSweep; ++u)
+    for (int u = 0; u < kSweep; ++u) {
+      if (i0 - lane + u * kTT >= n) break;
       if (i0 + u * kTT < n) atomicAdd(&hist[score_bucket(kk[u], vmax, scale)], 1u);
+    }
   }
   __syncthreads();
   locate_digit(hist, kBuckets, k, 0u, 0, s_prefix, s_rank, wtot);
@@ -456,6 +459,7 @@ __device__ __forceinline__ bool bucket_select_runs(const uint32_t* keys, int n, 
     }
 #pragma unroll
     for (int u = 0; u < kSweep; ++u) {
+      if (i0 + u * kWave >= w_hi) break;   // the rest of the batch lies past the run (uniform)
       const int i = i0 + u * kWave + lane;
       const int bk = i < w_hi ? score_bucket(kk[u], vmax, scale) : kBuckets;
       below += __popcll(__ballot(bk < b));
@@ -642,6 +646,21 @@ __global__ __launch_bounds__(kTT) void dsa_topk_final_kernel(TopkParams p) {
   __shared__ uint32_t s_wtot[kTW];
   __shared__ uint32_t s_mm[2 * kTW];
   __shared__ int s_tot[3][kTW];   // per wave: class 0, other keys below K*, keys equal to K*
+  // thread t takes survivor t of every segment (at most kPrCap = kTT each),
+  // requested together with the counts: one round trip for both (slots past a
+  // segment's count hold stale values and are never used)
+  static_assert(kPrCap <= kTT, "one survivor per thread and segment");
+  uint32_t kv[kPrMaxSegs];
+  int32_t pv[kPrMaxSegs];
+  {
+    const uint32_t* ks = ws_keys(p, i_row);
+    const int32_t* ps = ws_pos(p, i_row);
+#pragma unroll
+    for (int s = 0; s < kPrMaxSegs; ++s) {
+      kv[s] = ks[s * kPrCap + tid];
+      pv[s] = ps[s * kPrCap + tid];
+    }
+  }
   // survivors per segment (uniform: every thread reads the same counts; all
   // requested at once)
   const int32_t* cnt = ws_cnt(p, i_row);
@@ -659,20 +678,8 @@ __global__ __launch_bounds__(kTT) void dsa_topk_final_kernel(TopkParams p) {
                s_tot);
     return;
   }
-  // thread t takes survivor t of every segment (at most kPrCap = kTT each):
-  // every load in flight before the first LDS store
-  static_assert(kPrCap <= kTT, "one survivor per thread and segment");
   uint32_t klo = 0xffffffffu, khi = 0u;
   {
-    const uint32_t* ks = ws_keys(p, i_row);
-    const int32_t* ps = ws_pos(p, i_row);
-    uint32_t kv[kPrMaxSegs];
-    int32_t pv[kPrMaxSegs];
-#pragma unroll
-    for (int s = 0; s < kPrMaxSegs; ++s) {
-      kv[s] = tid < cs[s] ? ks[s * kPrCap + tid] : 0u;
-      pv[s] = tid < cs[s] ? ps[s * kPrCap + tid] : 0;
-    }
     int base = 0;
 #pragma unroll
     for (int s = 0; s < kPrMaxSegs; ++s) {
@@ -723,6 +730,7 @@ __global__ __launch_bounds__(kTT) void dsa_topk_final_kernel(TopkParams p) {
       }
 #pragma unroll
       for (int u = 0; u < kSweep; ++u) {
+        if (i0 + u * kWave >= w_hi) break;   // uniform
         const bool ok = i0 + u * kWave + lane < w_hi;
         const uint32_t key = kk[u];
         const float v = key_score(key);
@@ -765,6 +773,7 @@ __global__ __launch_bounds__(kTT) void dsa_topk_final_kernel(TopkParams p) {
     }
 #pragma unroll
     for (int u = 0; u < kSweep; ++u) {
+      if (i0 + u * kWave >= w_hi) break;   // uniform
       const int i = i0 + u * kWave + lane;
       const bool ok = i < w_hi;
       const uint32_t key = kk[u];
