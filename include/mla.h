@@ -331,9 +331,10 @@ int mla_o_proj(int32_t dtype, const float* ctx, int64_t rows, int32_t in_feature
  *         dense row (row_len[b] <= top_k), as mla_decode_latent_attn takes it.
  * sel_idx: device int32, written with top_k entries per selected row,
  *         concatenated in row order; may be NULL only if no row is selected.
- * workspace / workspace_bytes: a row of 2 to 8 segments of 16384 scores
- *         whose segments' candidates (segments x top_k) fit 16384 runs on one
- *         workgroup per segment and then one for the row, in caller memory of
+ * workspace / workspace_bytes: a row of 16385 to 131072 scores with
+ *         top_k <= 16384 / ceil(row_len / 16384) (the multi-workgroup,
+ *         "two-stage" rows) runs on one workgroup per 8192-score segment and
+ *         then one for the row, in three launches, in caller memory of
  *         131328 bytes per such row (256-byte aligned).  workspace == NULL with
  *         workspace_bytes != NULL writes the size needed (0 when no row
  *         qualifies) and returns MLA_OK without launching.  workspace_bytes

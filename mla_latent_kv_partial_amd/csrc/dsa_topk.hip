@@ -24,20 +24,12 @@
 //      selected ties are the first m.  Ranks inside 64 positions come from
 //      ballots.
 //
-// Two-stage form for rows of 2 to 8 segments of 16384 scores (the 131072-
-// score rows of a long context), in two launches with a caller workspace:
-//   A. one workgroup per (row, segment): the segment's keys go to LDS, a
-//      select (by score buckets, below; the radix select when the buckets do
-//      not separate the keys) finds the segment's top_k under the page's order
-//      (key, then position), and an order-keeping compaction writes those
-//      top_k (key, position) pairs to the workspace in ascending position
-//      order.  A position the whole row selects has fewer than top_k
-//      predecessors in the row, so fewer in its segment: the segments'
-//      candidates contain the row's selection.
-//   B. one workgroup per row: the candidates of the segments (one contiguous
-//      run, ascending positions) go to LDS, and the select and the two sweeps of
-//      the one-workgroup form run over them (the score of a candidate is its
-//      key mapped back, bit for bit).
+// Multi-workgroup form for the long rows of a 131072-token context (16385 to
+// 131072 scores), in three launches with a caller workspace: per segment of
+// 8192 scores a bound on K*, then each segment's keys at or below the
+// largest bound (the survivors, in position order), then one workgroup per
+// row runs the select and the two sweeps over the survivors (see the
+// kernels below).
 // Both forms give the same integers.
 #include <mutex>
 

@@ -130,13 +130,14 @@ struct TopkParams {
   int32_t row[kTopkRowsPerLaunch];
   int32_t len[kTopkRowsPerLaunch];
   int32_t out_off[kTopkRowsPerLaunch];
-  // two-stage rows: candidate area of launch row i at ws + i * kTopkRowWsBytes
+  // two-stage rows: survivor area of launch row i at ws + i * kTopkRowWsBytes
   char* ws;
 };
 // Rows of at most kTopkSeg scores, or longer than kTopkSeg * kTopkMaxSegs, or
-// whose segments' candidates exceed kTopkMaxCand, run on one workgroup
-// (launch_dsa_topk); the others on kTopkMaxSegs workgroups per row, then one
-// (launch_dsa_topk_two_stage), with kTopkRowWsBytes of workspace each.
+// with top_k above kTopkMaxCand / (their kTopkSeg segments), run on one
+// workgroup (launch_dsa_topk); the others ("two-stage" rows) in three
+// launches over 8192-score segments (launch_dsa_topk_two_stage), with
+// kTopkRowWsBytes of workspace each.
 constexpr int kTopkSeg = 16384;
 constexpr int kTopkMaxSegs = 8;
 constexpr int kTopkMaxCand = 16384;
