@@ -332,17 +332,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 // per (head, pair of rows).  Each half of the workgroup merges one row as
 // combine_kernel does, while the head's value block (v_head weight rows of
 // 1 KB) streams into LDS by global_load_lds copies issued right behind the
-// merge's first loads.  The projection then reads every weight element from
-// LDS once for both rows.  Against one workgroup per (head, row) this fetches
-// each value block once per row pair rather than per row, and the weights no
-// longer wait for the merge.  Workgroup ids run head fastest: the row pairs
-// of a head share an XCD and its L2.
+// merge's first loads: wave v < 8 copies rows 16 v .. 16 v + 15 and then
+// projects exactly those 16 output columns for both rows on MFMA, as soon as
+// its own copies have landed (no wait for the whole block).  Against one
+// workgroup per (head, row) this fetches each value block once per row pair
+// rather than per row.  Workgroup ids run head fastest: the row pairs of a
+// head share an XCD and its L2.
 constexpr int kPairThreads = 2 * kThreads;
 constexpr int kPairR = 512;
 constexpr int kWRowBytes = kPairR * 2 + 32;    // weight row in LDS: an odd number of 32-byte units
 constexpr int kPairMaxDv = 128;
-constexpr int kEighths = kPairThreads / kPairMaxDv;   // projection: the latent axis in 8 parts of 64
-static_assert(kEighths * 64 == kPairR, "the projection splits the latent axis in eighths of 64");
 
 __shared__ __attribute__((aligned(1024))) char g_w[kPairMaxDv * kWRowBytes];
 
@@ -362,7 +361,9 @@ __global__ __launch_bounds__(kPairThreads) void combine_v_pair_kernel(CombinePar
   const PT* po = static_cast<const PT*>(p.part_o) + bh * p.s_max * kPairR;
   __shared__ float gm_s[2][kGroups], gl_s[2][kGroups];
   __shared__ float4 grp_all[2][kGroups - 1][kGroupThreads];   // group sums, then the projection's partial sums
-  __shared__ __attribute__((aligned(16))) float o_sh[2][kPairR];
+  // the merged rows as MFMA operands: bf16 high part and bf16 residual
+  __shared__ __attribute__((aligned(16))) __bf16 o_hi[2][kPairR];
+  __shared__ __attribute__((aligned(16))) __bf16 o_lo[2][kPairR];
 
   const int grp = __builtin_amdgcn_readfirstlane(tid / kGroupThreads);
   const int gt = tid % kGroupThreads;
@@ -377,11 +378,16 @@ __global__ __launch_bounds__(kPairThreads) void combine_v_pair_kernel(CombinePar
   float ls[kU];
   float4 v[kU];
   first_batch(po, lse_in, n, kPairR, c, grp, ls, v);
-  {
-    const int wgw = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wgw = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  if (wgw < kPairMaxDv / 16) {
+    // wave v < 8 copies weight rows 16 v .. 16 v + 15 (below dv), which only
+    // it reads in the projection
     const uint16_t* wb = static_cast<const uint16_t*>(p.w) + (static_cast<int64_t>(h) * (p.dn + p.dv) + p.dn) * kPairR;
-    for (int j = wgw; j < p.dv; j += kPairThreads / kWave)
+    for (int i = 0; i < 16; ++i) {
+      const int j = 16 * wgw + i;
+      if (j >= p.dv) break;
       dma16(wb + static_cast<int64_t>(j) * kPairR + 8 * lane, lds_addr(g_w) + j * kWRowBytes);
+    }
   }
   float mg, lg;
   float4 acc;
@@ -398,50 +404,48 @@ __global__ __launch_bounds__(kPairThreads) void combine_v_pair_kernel(CombinePar
     meet_groups(gm_s[half], gl_s[half], &grp_all[half][0][gt], &grp_all[half][1][gt], &grp_all[half][2][gt], acc, o,
                 lse);
     if (p.o_lat && real) *reinterpret_cast<float4*>(p.o_lat + bh * kPairR + c) = o;
-    *reinterpret_cast<float4*>(&o_sh[half][c]) = o;
+    const float e[4] = {o.x, o.y, o.z, o.w};
+    bf16x4 hi, lo;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      hi[q] = static_cast<__bf16>(e[q]);
+      lo[q] = static_cast<__bf16>(e[q] - static_cast<float>(hi[q]));
+    }
+    *reinterpret_cast<bf16x4*>(&o_hi[half][c]) = hi;
+    *reinterpret_cast<bf16x4*>(&o_lo[half][c]) = lo;
     if (p.lse && real && gt == 0) p.lse[bh] = lse;
   }
-  wait_vm<0>();      // this wave's weight copies (and every load) have landed
-  __syncthreads();   // o_sh of both rows and the whole value block are in LDS
+  __syncthreads();   // the merged rows are in LDS
 
-  // ---- projection: thread (e, j) sums latent features 64 e .. 64 e + 63 of
-  // output column j for both rows; a wave covers 64 consecutive weight rows
-  // at one feature offset (conflict-free at the 1056-byte row stride)
-  const int T = threadIdx.x;
-  const int e = T / kPairMaxDv, j = T % kPairMaxDv;
-  float a0 = 0.f, a1 = 0.f;
-  if (j < p.dv) {
-    const char* wr = g_w + j * kWRowBytes + e * 128;
-    const float* o0 = &o_sh[0][64 * e];
-    const float* o1 = &o_sh[1][64 * e];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const f32x4 wb = *reinterpret_cast<const f32x4*>(wr + 16 * k);   // 8 bf16
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint32_t wu = __float_as_uint(wb[t]);
-        const float wl = __uint_as_float(wu << 16), wh = __uint_as_float(wu & 0xffff0000u);
-        const int cc = 8 * k + 2 * t;
-        a0 = fmaf(o0[cc], wl, a0);
-        a0 = fmaf(o0[cc + 1], wh, a0);
-        a1 = fmaf(o1[cc], wl, a1);
-        a1 = fmaf(o1[cc + 1], wh, a1);
+  // ---- projection on MFMA, one 16-column block per wave (waves 0..7): the
+  // wave waits for its own 16 weight rows only, so each block starts as soon
+  // as its rows land.  A = the weight rows (16 columns x 32 latent features
+  // per k-step), B = the two merged rows as a bf16 high part plus a bf16
+  // residual (~16 significant bits), the other 14 columns of B zero.
+  if (wgw < kPairMaxDv / 16 && 16 * wgw < p.dv) {
+    wait_vm<0>();
+    const int m = lane & 15, g = lane >> 4;
+    const char* wrow = g_w + (16 * wgw + m) * kWRowBytes + 16 * g;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int ks = 0; ks < kPairR / 32; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(wrow + 64 * ks);
+      bf16x8 hi = {}, lo = {};
+      if (m < 2) {
+        hi = *reinterpret_cast<const bf16x8*>(&o_hi[m][32 * ks + 8 * g]);
+        lo = *reinterpret_cast<const bf16x8*>(&o_lo[m][32 * ks + 8 * g]);
       }
+      acc = mfma16x16x32(a, hi, acc);
+      acc = mfma16x16x32(a, lo, acc);
     }
-  }
-  float* psum = reinterpret_cast<float*>(grp_all);   // [kEighths][2][kPairMaxDv] (8 KB of the 12 KB)
-  __syncthreads();   // every half is past its reads of grp_all
-  psum[(e * 2 + 0) * kPairMaxDv + j] = a0;
-  psum[(e * 2 + 1) * kPairMaxDv + j] = a1;
-  __syncthreads();
-  if (T < 2 * kPairMaxDv) {
-    const int row = T / kPairMaxDv, jj = T % kPairMaxDv;
-    const int bo = 2 * blockIdx.y + row;
-    if (jj < p.dv && bo < p.rows) {
-      float sum = 0.f;
+    // lane (m, g) holds columns 16 wgw + 4 g + (0..3) of pair row m
+    const int bo = 2 * blockIdx.y + m;
+    if (m < 2 && bo < p.rows) {
+      float* dst = p.ctx + static_cast<int64_t>(bo) * p.heads * p.dv + static_cast<int64_t>(h) * p.dv;
+      const int col = 16 * wgw + 4 * g;
 #pragma unroll
-      for (int q = 0; q < kEighths; ++q) sum += psum[(q * 2 + row) * kPairMaxDv + jj];
-      p.ctx[static_cast<int64_t>(bo) * p.heads * p.dv + static_cast<int64_t>(h) * p.dv + jj] = sum;
+      for (int ii = 0; ii < 4; ++ii)
+        if (col + ii < p.dv) dst[col + ii] = acc[ii];
     }
   }
 }
