@@ -190,6 +190,14 @@ __global__ __launch_bounds__(64 * kAWaves, kAWavesPerEu) void flash_attn_kernel(
 #pragma unroll
     for (int ks = 0; ks < kQk / 32; ++ks) qreg[qb][ks] = *reinterpret_cast<const f32x4*>(qrow + 32 * ks);
   }
+  // Take the queries as landed here: the compiler waits for their loads once,
+  // before the loop.  (Otherwise it keeps a wait for them at their first uses
+  // inside the loop, where the hardware counter also holds the next tile's
+  // copies: every tile's scores would wait for the next tile to land.)
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int ks = 0; ks < kQk / 32; ++ks) asm volatile("" : "+v"(qreg[qb][ks]));
   for (int t = 0; t < kAStages - 1 && t < nt; ++t) issue(t, t);
   // Probabilities are exp2(fma(score, cs, -max)) with cs > 0 (the tile max
   // of the raw scores times cs is the max of the scaled scores, rounding
