@@ -12,7 +12,10 @@ cache).  Per layer the step runs the whole chain through the C ABI:
   attention (split-T partials) -> combine and absorb_v (one launch).  The split partials are
   one workspace shared by the layers, as an engine keeps them.
 The step is captured once in a HIP graph and replayed; W warmup replays, then
-K timed replays between synchronisations.
+K timed replays between synchronisations.  The default W = 50: the chip's
+clocks take ~10-15 ms of continuous work to settle, and with 5 warmup replays
+the first timed steps ran up to 20 % slower (every timed measurement here
+replays its graph W times first).
 
 Printed: one JSON line.  value = rows*layers/s of the step (ms_per_step_spread:
 p10/p50/p90 of the per-step event timings).  roofline = the latent attention
@@ -60,7 +63,7 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
@@ -397,7 +400,7 @@ def prefill_leg(torch, mla, cf, dev, tokens=None, left_pad=0):
     run = lambda: mla.mla_prefill_reconstructed(c_q, w_qb, latent, rope, w_kvb, pcfg.heads, pcfg.qk_nope,
                                                 pcfg.qk_rope, pcfg.v_head, offs, pcfg.theta, workspace=ws,
                                                 ctx=ctx, left_pad=[left_pad] if left_pad else None)
-    ms_p = time_graph(torch, run, 10, 5)[0]   # steady clocks: the first calls run slower
+    ms_p = time_graph(torch, run, 10, 20)[0]   # 20 warmup calls (~14 ms): clocks settle first
     prefix = kk - tt
     visible = sum(max(0, prefix + t + 1 - left_pad) for t in range(tt))   # causal pairs past the pad
     flops = (2 * tt * pcfg.q_lora_rank * h * (pcfg.qk_nope + pcfg.qk_rope)
@@ -421,7 +424,7 @@ def o_proj_prefill_leg(torch, mla, cf, dev, rows=4096, hidden=6144):
                                   cf.BF16).view(np.int16)).to(dev).view(torch.bfloat16)
     out = torch.empty((rows, hidden), dtype=torch.float32, device=dev)
     ws = torch.empty(rows * width * 2, dtype=torch.uint8, device=dev)
-    ms = time_graph(torch, lambda: mla.mla_o_proj(ctx, w, out=out, workspace=ws), 10, 5)[0]
+    ms = time_graph(torch, lambda: mla.mla_o_proj(ctx, w, out=out, workspace=ws), 10, 20)[0]
     flops = 2 * rows * width * hidden
     return {"rows": rows, "in": width, "hidden": hidden, "ms": ms, "TFLOPs": flops / (ms * 1e-3) / 1e12,
             "frac_bf16_mfma": flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
