@@ -33,8 +33,9 @@ layer instances and 64 DSA selections stacked as the rows of one launch each.
 cpu_baseline = the CPU oracle (reconstructed and absorbed forms) on every
 workload, each on the sample it names (median of 3; one run for the ragged
 rows and the prefill), with the CPU model and thread count.  extra = the
-stacked legs, the dense and DSA chains, the top-k selection, the full layer
-and the prefill legs.
+step launched eagerly (no graph: the host's launch work in the timed
+region), the stacked legs, the dense and DSA chains, the top-k selection,
+the full layer and the prefill legs.
 """
 
 from __future__ import annotations
@@ -535,6 +536,21 @@ def main():
     # ------------------------------------------------------------- extras
     if not args.no_extra:
         extra = {}
+
+        # the same step launched eagerly (no graph): the host's launch work
+        # for the 24 kernels is then inside the timed region
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(args.steps):
+            step()
+        ev1.record()
+        torch.cuda.synchronize()
+        ms_eager = ev0.elapsed_time(ev1) / args.steps
+        extra["step_eager"] = {"ms_per_step": ms_eager, "rows_layers_per_s": rows * nl / (ms_eager * 1e-3)}
+        log(f"eager step {ms_eager:.3f} ms")
 
         def stacked_leg(q_lat, q_rope, latent, rope, lens, w, cfg_, sel_idx=None, sel_count=None):
             """One launch of the attention over all the rows, then (a second
