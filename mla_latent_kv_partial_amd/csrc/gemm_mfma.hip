@@ -238,14 +238,16 @@ __shared__ __attribute__((aligned(1024))) char g_gemm256[kBSlots * kBHalfBytes];
 // instruction covering full 128-byte lines, where the fragment layout stores
 // 32-byte pieces of 16 rows (measured: the epilogue took as long as a third
 // of the MFMA work).  fp32 tiles go in two passes of 128 rows.
-template <bool ROPE, bool OUT_F32>
-__device__ __forceinline__ void store_tile_staged(const GemmNT& p, const f32x4 (&acc)[8][4], int m0, int n0, int wm,
-                                                  int wn, int i16, int g) {
+template <bool ROPE, bool OUT_F32, int BN>
+__device__ __forceinline__ void store_tile_staged(const GemmNT& p, const f32x4 (&acc)[8][BN / 64], int m0, int n0,
+                                                  int wm, int wn, int i16, int g) {
   static_assert(!(ROPE && OUT_F32), "the q projection writes bf16");
+  static_assert(!ROPE || BN == 256, "the RoPE epilogue takes 64-column wave spans");
+  constexpr int kNb = BN / 64;                      // 16-column blocks per wave
   constexpr int kEs = OUT_F32 ? 4 : 2;              // bytes per element
-  constexpr int kRowB = 256 * kEs + 16;             // LDS row stride
+  constexpr int kRowB = BN * kEs + 16;              // LDS row stride
   constexpr int kPassRows = OUT_F32 ? 128 : 256;
-  constexpr int kChunks = 256 * kEs / 16;           // 16-byte chunks per row
+  constexpr int kChunks = BN * kEs / 16;            // 16-byte chunks per row
   static_assert(kPassRows * kRowB <= kBSlots * kBHalfBytes, "a pass fits the LDS ring");
   const int tid = threadIdx.x;
   const bool al16 = (p.ldc * kEs) % 16 == 0;
@@ -262,13 +264,13 @@ __device__ __forceinline__ void store_tile_staged(const GemmNT& p, const f32x4 (
       const int rope_col = 64 * wn - (n_base % kQk - kDn);    // tile column of the head's rope part
 #pragma unroll
       for (int b0 = 0; b0 < 8; b0 += 4) {
-        float2 t[4][4][2];
+        float2 t[4][kNb][2];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int m = min(m0 + 128 * wm + 16 * (b0 + u) + i16, p.m - 1);
           const float2* cs = p.cs + static_cast<int64_t>(m) * 32 + q_lane;
 #pragma unroll
-          for (int bn = 0; bn < 4; ++bn) {
+          for (int bn = 0; bn < kNb; ++bn) {
             t[u][bn][0] = cs[8 * bn];
             t[u][bn][1] = cs[8 * bn + 1];
           }
@@ -276,7 +278,7 @@ __device__ __forceinline__ void store_tile_staged(const GemmNT& p, const f32x4 (
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int bn = 0; bn < 4; ++bn) {
+          for (int bn = 0; bn < kNb; ++bn) {
             uint16_t re[2], im[2];
 #pragma unroll
             for (int e = 0; e < 2; ++e)
@@ -291,8 +293,8 @@ __device__ __forceinline__ void store_tile_staged(const GemmNT& p, const f32x4 (
 #pragma unroll
       for (int bm = 0; bm < 8; ++bm)
 #pragma unroll
-        for (int bn = 0; bn < 4; ++bn) {
-          char* d = g_gemm256 + (rbase + 16 * bm + i16) * kRowB + (64 * wn + 16 * bn + 4 * g) * kEs;
+        for (int bn = 0; bn < kNb; ++bn) {
+          char* d = g_gemm256 + (rbase + 16 * bm + i16) * kRowB + (16 * kNb * wn + 16 * bn + 4 * g) * kEs;
           const f32x4& v = acc[bm][bn];
           if (OUT_F32) {
             *reinterpret_cast<float4*>(d) = make_float4(v[0], v[1], v[2], v[3]);
@@ -327,13 +329,17 @@ __device__ __forceinline__ void store_tile_staged(const GemmNT& p, const f32x4 (
   }
 }
 
-template <bool ROPE, bool OUT_F32>
+// BN = 256, or 192 (waves of 128 x 48, B slices of 192 rows) where that
+// tiles the output into whole rounds of the CUs and 256 does not.
+template <bool ROPE, bool OUT_F32, int BN>
 __global__ __launch_bounds__(512) void gemm256_nt_kernel(GemmNT p) {
+  static_assert(BN == 256 || BN == 192, "column tile");
+  constexpr int kNb = BN / 64;   // 16-column blocks per wave
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tile = xcd_tile(blockIdx.x, p.m_tiles * p.n_tiles);
   const int m0 = (tile % p.m_tiles) * kBT;
-  const int n0 = (tile / p.m_tiles) * kBT;
+  const int n0 = (tile / p.m_tiles) * BN;
 
   // copy plan: waves 0..3 issue every copy (8 per half stage each), so the
   // waves sharing their SIMDs (4..7) keep issuing MFMAs while a copy holds
@@ -343,8 +349,9 @@ __global__ __launch_bounds__(512) void gemm256_nt_kernel(GemmNT p) {
   // (l % 8) ^ (l / 8).  Each copy is an SGPR base (the operand at the step's
   // K offset) plus a 32-bit lane offset (the launcher takes this kernel only
   // for operands under 4 GB).  Rows past the matrix edge re-read its last row.
-  constexpr int kIss = 2 * kBCopies;
-  uint32_t offa[kIss], offb[kIss];
+  constexpr int kIss = 2 * kBCopies;     // A copies per issuing wave and half stage (8)
+  constexpr int kIssB = BN / 32;         // B copies (8, or 6)
+  uint32_t offa[kIss], offb[kIssB];
   const bool issuer = wave < 4;
 #pragma unroll
   for (int j = 0; j < kIss; ++j) {
@@ -352,7 +359,8 @@ __global__ __launch_bounds__(512) void gemm256_nt_kernel(GemmNT p) {
     const int row = 8 * ((wave & 3) + 4 * j) + r8;
     const int c = (lane & 7) ^ r8;
     offa[j] = static_cast<uint32_t>((static_cast<int64_t>(min(m0 + row, p.m - 1)) * p.lda + 8 * c) * 2);
-    offb[j] = static_cast<uint32_t>((static_cast<int64_t>(min(n0 + row, p.n - 1)) * p.ldb + 8 * c) * 2);
+    if (j < kIssB)
+      offb[j] = static_cast<uint32_t>((static_cast<int64_t>(min(n0 + row, p.n - 1)) * p.ldb + 8 * c) * 2);
   }
   // half stage h: the A slice (h even) or the B slice (h odd) of step h / 2, in slot h % 5
   const int nh = 2 * (p.k / kBK);
@@ -363,7 +371,7 @@ __global__ __launch_bounds__(512) void gemm256_nt_kernel(GemmNT p) {
     if (h & 1) {
       const char* base = reinterpret_cast<const char*>(p.b + k0);
 #pragma unroll
-      for (int j = 0; j < kIss; ++j) dma16_off(base, offb[j], dst + j * 4096);
+      for (int j = 0; j < kIssB; ++j) dma16_off(base, offb[j], dst + j * 4096);
     } else {
       const char* base = reinterpret_cast<const char*>(p.a + k0);
 #pragma unroll
@@ -371,58 +379,64 @@ __global__ __launch_bounds__(512) void gemm256_nt_kernel(GemmNT p) {
     }
   };
 
-  // Copies 4 part .. 4 part + 3 of half stage h, for the issue spread over
+  // Half of the copies of half stage h (the first for even c, the second for
+  // odd; h is the B slice 2 i + 5 for c < 2, the A slice 2 i + 6 for c >= 2), for the issue spread over
   // the MFMAs below.  They fill only the two slots freed at this step's
   // barrier, which no wave reads before a later barrier, so they carry no
   // memory clobber: the compiler may keep this step's fragment reads of the
   // other slots where it schedules them (with the clobber it had to finish
   // all of them first and spilled).  The barriers and waits keep theirs.
-  auto issue_part = [&](int h, const int part) {
+  auto issue_part = [&](int h, auto cc) {
+    constexpr int c = decltype(cc)::value;   // half stage h is a B slice for c < 2
+    constexpr bool is_b = c < 2;
+    constexpr int per = is_b ? kIssB / 2 : kIss / 2;   // copies per part
+    constexpr int part = c & 1;
     if (h >= nh || !issuer) return;
-    const uint32_t dst = lds_addr(g_gemm256 + (h % kBSlots) * kBHalfBytes) + (wave & 3) * 1024 + part * 4 * 4096;
-    const char* base = reinterpret_cast<const char*>((h & 1) ? p.b + (h >> 1) * kBK : p.a + (h >> 1) * kBK);
+    const uint32_t dst = lds_addr(g_gemm256 + (h % kBSlots) * kBHalfBytes) + (wave & 3) * 1024 + part * per * 4096;
+    const char* base = reinterpret_cast<const char*>(is_b ? p.b + (h >> 1) * kBK : p.a + (h >> 1) * kBK);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t off = (h & 1) ? offb[4 * part + j] : offa[4 * part + j];
+    for (int j = 0; j < per; ++j) {
+      const uint32_t off = is_b ? offb[per * part + j] : offa[per * part + j];
       asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(sgpr(dst + j * 4096))
                    : "m0");
     }
   };
-  const int wm = wave >> 2, wn = wave & 3;   // rows 128 wm .., columns 64 wn ..
+  const int wm = wave >> 2, wn = wave & 3;   // rows 128 wm .., columns 16 kNb wn ..
   const int i16 = lane & 15, g = lane >> 4;
   // fragment of lane l in half q: row l % 16 of a 16-row block, chunk
   // 4 q + l / 16 at its swizzled position
   const uint32_t a_row = (128 * wm + i16) * kBRowBytes;
-  const uint32_t b_row = (64 * wn + i16) * kBRowBytes;
+  const uint32_t b_row = (16 * kNb * wn + i16) * kBRowBytes;
   const uint32_t pos0 = 16 * (g ^ (i16 & 7)), pos1 = 16 * ((4 + g) ^ (i16 & 7));
 
   const int nk = nh / 2;
   for (int h = 0; h < kBSlots; ++h) issue(h);
-  f32x4 acc[8][4];
+  f32x4 acc[8][kNb];
 #pragma unroll
   for (int bm = 0; bm < 8; ++bm)
 #pragma unroll
-    for (int bn = 0; bn < 4; ++bn) acc[bm][bn] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int bn = 0; bn < kNb; ++bn) acc[bm][bn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto read_half = [&](int step, uint32_t pos, bf16x8 (&a)[8], bf16x8 (&b)[4]) {
+  auto read_half = [&](int step, uint32_t pos, bf16x8 (&a)[8], bf16x8 (&b)[kNb]) {
     const char* sa = g_gemm256 + ((2 * step) % kBSlots) * kBHalfBytes + pos;
     const char* sb = g_gemm256 + ((2 * step + 1) % kBSlots) * kBHalfBytes + pos;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) b[t] = *reinterpret_cast<const bf16x8*>(sb + b_row + t * 16 * kBRowBytes);
+    for (int t = 0; t < kNb; ++t) b[t] = *reinterpret_cast<const bf16x8*>(sb + b_row + t * 16 * kBRowBytes);
 #pragma unroll
     for (int t = 0; t < 8; ++t) a[t] = *reinterpret_cast<const bf16x8*>(sa + a_row + t * 16 * kBRowBytes);
   };
   // D^T blocks: lane (row m = i16, group g) receives C[m][n + 4g + (0..3)]
-  auto mfmas = [&](const bf16x8 (&a)[8], const bf16x8 (&b)[4]) {
+  auto mfmas = [&](const bf16x8 (&a)[8], const bf16x8 (&b)[kNb]) {
 #pragma unroll
     for (int bm = 0; bm < 8; ++bm)
 #pragma unroll
-      for (int bn = 0; bn < 4; ++bn) acc[bm][bn] = mfma16x16x32(b[bn], a[bm], acc[bm][bn]);
+      for (int bn = 0; bn < kNb; ++bn) acc[bm][bn] = mfma16x16x32(b[bn], a[bm], acc[bm][bn]);
   };
-  // step 0 landed; half stages 2 .. 4 may fly
-  wait_vm_upto<2 * kBCopies * (kBSlots - 2)>(issuer ? 2 * kBCopies * (min(kBSlots, nh) - 2) : 0);
+  // step 0 landed; half stages 2 .. 4 (A, B, A) may fly
+  constexpr int kFly3 = 2 * kIss + kIssB;
+  wait_vm_upto<kFly3>(!issuer ? 0 : nh >= 5 ? kFly3 : nh == 4 ? kIss + kIssB : 0);
   lds_barrier();
-  bf16x8 a0[8], b0[4], a1[8], b1[4];
+  bf16x8 a0[8], b0[kNb], a1[8], b1[kNb];
   read_half(0, pos0, a0, b0);
   for (int i = 0; i < nk; ++i) {
     read_half(i, pos1, a1, b1);
@@ -430,7 +444,7 @@ __global__ __launch_bounds__(512) void gemm256_nt_kernel(GemmNT p) {
     if (i + 1 < nk) {
       // step i + 1 landed (half stage 2 i + 4 may fly); every wave is past
       // its reads of step i, whose slots take half stages 2 i + 5 and 2 i + 6
-      wait_vm_upto<2 * kBCopies>(issuer && 2 * i + 4 < nh ? 2 * kBCopies : 0);
+      wait_vm_upto<kIss>(issuer && 2 * i + 4 < nh ? kIss : 0);   // half stage 2 i + 4 is an A slice
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       lds_barrier();
       read_half(i + 1, pos0, a0, b0);
@@ -442,11 +456,11 @@ __global__ __launch_bounds__(512) void gemm256_nt_kernel(GemmNT p) {
     // 158 us in the kernel trace, bit-identical).
     auto group = [&](auto cc) {
       constexpr int c = decltype(cc)::value;
-      issue_part(2 * i + 5 + (c >> 1), c & 1);
+      issue_part(2 * i + 5 + (c >> 1), cc);
 #pragma unroll
       for (int bm = 2 * c; bm < 2 * c + 2; ++bm)
 #pragma unroll
-        for (int bn = 0; bn < 4; ++bn) acc[bm][bn] = mfma16x16x32(b1[bn], a1[bm], acc[bm][bn]);
+        for (int bn = 0; bn < kNb; ++bn) acc[bm][bn] = mfma16x16x32(b1[bn], a1[bm], acc[bm][bn]);
     };
     group(std::integral_constant<int, 0>{});
     group(std::integral_constant<int, 1>{});
@@ -454,7 +468,7 @@ __global__ __launch_bounds__(512) void gemm256_nt_kernel(GemmNT p) {
     group(std::integral_constant<int, 3>{});
   }
 
-  store_tile_staged<ROPE, OUT_F32>(p, acc, m0, n0, wm, wn, i16, g);
+  store_tile_staged<ROPE, OUT_F32, BN>(p, acc, m0, n0, wm, wn, i16, g);
 }
 
 // cos / sin of the q RoPE angles, one thread per (row, pair): the angle is
@@ -501,16 +515,29 @@ hipError_t launch_gemm_nt_mfma(const GemmNT& p0, bool rope, bool out_f32, hipStr
   // the 256 x 256 kernel addresses its copies with 32-bit offsets
   const bool spans32 = static_cast<int64_t>(p.m) * p.lda * 2 < (int64_t{1} << 32) &&
                        static_cast<int64_t>(p.n) * p.ldb * 2 < (int64_t{1} << 32);
+  // 256 x 192 tiles (3 units) for the fp32 product (o_proj) where they need
+  // fewer rounds than 256 x 256 and no more than 128 x 128 (o_proj at
+  // 4096 x 6144: 512 tiles, two whole rounds, against 1.5 rounds of
+  // 256 x 256).
+  const int64_t mid = ((p.m + kBT - 1) / kBT) * static_cast<int64_t>((p.n + 191) / 192);
+  const int64_t cost_mid = (mid + 255) / 256 * 3;
+  const bool use_mid = out_f32 && !rope && mid >= 256 && cost_mid < cost_big && cost_mid <= cost_small;
+  if (p.k % kBK == 0 && spans32 && use_mid) {
+    p.m_tiles = (p.m + kBT - 1) / kBT;
+    p.n_tiles = (p.n + 191) / 192;
+    hipLaunchKernelGGL((gemm256_nt_kernel<false, true, 192>), dim3(p.m_tiles * p.n_tiles), dim3(512), 0, stream, p);
+    return hipGetLastError();
+  }
   if (p.k % kBK == 0 && big >= 256 && cost_big <= cost_small && spans32) {
     p.m_tiles = (p.m + kBT - 1) / kBT;
     p.n_tiles = (p.n + kBT - 1) / kBT;
     const dim3 grid(p.m_tiles * p.n_tiles);
     if (rope)
-      hipLaunchKernelGGL((gemm256_nt_kernel<true, false>), grid, dim3(512), 0, stream, p);
+      hipLaunchKernelGGL((gemm256_nt_kernel<true, false, 256>), grid, dim3(512), 0, stream, p);
     else if (out_f32)
-      hipLaunchKernelGGL((gemm256_nt_kernel<false, true>), grid, dim3(512), 0, stream, p);
+      hipLaunchKernelGGL((gemm256_nt_kernel<false, true, 256>), grid, dim3(512), 0, stream, p);
     else
-      hipLaunchKernelGGL((gemm256_nt_kernel<false, false>), grid, dim3(512), 0, stream, p);
+      hipLaunchKernelGGL((gemm256_nt_kernel<false, false, 256>), grid, dim3(512), 0, stream, p);
     return hipGetLastError();
   }
   p.m_tiles = (p.m + kGT - 1) / kGT;

@@ -45,12 +45,18 @@ def test_o_proj_prefill_size_sampled_rows():
     assert_close(got[sample], oracle.o_proj(ctx[sample], cf.values(w)), cf.BF16, "o_proj sampled rows")
 
 
-def test_o_proj_long_gemm_partial_tiles_sampled_rows():
-    """Enough rows and columns for the 256 x 256 GEMM tiles, with a partial
-    tile at both edges (4000 = 15 x 256 + 160 rows, 4100 = 16 x 256 + 4 columns)."""
-    rows, width, hidden = 4000, 512, 4100
+@pytest.mark.parametrize("hidden", [
+    4100,   # 256 x 192 tiles: 16 x 22 = 352 tiles (2 rounds of 3 units) beat 16 x 17 (2 rounds of 4);
+            # 4100 = 21 x 192 + 68 columns
+    4000,   # 256 x 256 tiles: 16 x 16 = 256, one round; 4000 = 15 x 256 + 160 columns
+])
+def test_o_proj_long_gemm_partial_tiles_sampled_rows(hidden):
+    """Enough rows and columns for the 256-row GEMM tiles, with a partial
+    tile at both edges (4000 = 15 x 256 + 160 rows)."""
+    rows, width = 4000, 512
+    say(f"o_proj rows={rows} in={width} hidden={hidden}")
     ctx = gen.normal_f32(32, gen.T_MISC, (rows, width))
     w = cf.store(gen.normal_f32(32, gen.T_MISC, (hidden, width), std=width ** -0.5, layer=1), cf.BF16)
     got = host_values(_mla().mla_o_proj(dev(ctx), dev(w)))
-    sample = [0, 1, 255, 256, 3839, 3840, 3999]
+    sample = [0, 1, 127, 128, 255, 256, 3839, 3840, 3967, 3999]
     assert_close(got[sample], oracle.o_proj(ctx[sample], cf.values(w)), cf.BF16, "o_proj sampled rows")
