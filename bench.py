@@ -416,7 +416,8 @@ def prefill_leg(torch, mla, cf, dev, tokens=None, left_pad=0):
 
 
 def o_proj_prefill_leg(torch, mla, cf, dev, rows=4096, hidden=6144):
-    """o_proj after a 4096-token prefill (hidden size synthetic): TFLOP/s."""
+    """o_proj after a 4096-token prefill (hidden size synthetic): TFLOP/s, after
+    100 untimed replays (~40 ms) so that the clocks have settled."""
     import numpy as np
     from synth import generators as gen
     width = 64 * 128
@@ -425,7 +426,7 @@ def o_proj_prefill_leg(torch, mla, cf, dev, rows=4096, hidden=6144):
                                   cf.BF16).view(np.int16)).to(dev).view(torch.bfloat16)
     out = torch.empty((rows, hidden), dtype=torch.float32, device=dev)
     ws = torch.empty(rows * width * 2, dtype=torch.uint8, device=dev)
-    ms = time_graph(torch, lambda: mla.mla_o_proj(ctx, w, out=out, workspace=ws), 10, 20)[0]
+    ms = time_graph(torch, lambda: mla.mla_o_proj(ctx, w, out=out, workspace=ws), 10, 100)[0]
     flops = 2 * rows * width * hidden
     return {"rows": rows, "in": width, "hidden": hidden, "ms": ms, "TFLOPs": flops / (ms * 1e-3) / 1e12,
             "frac_bf16_mfma": flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
