@@ -3,7 +3,7 @@
 // of a packed bf16 [B, W, 576] cache, with the same launch geometry and the
 // same copy schedule: one workgroup of 512 threads per (row, split) in the
 // same compact order; 32-token tiles of 1184-byte LDS rows copied by
-// global_load_lds_dwordx4 (37 copies of 1 KB per tile, the same lane plan)
+// non-temporal global_load_lds_dwordx4 (37 copies of 1 KB per tile, the same lane plan)
 // into a 4-stage ring of the same size, two tiles ahead, with the same waits
 // and barriers.  It computes nothing and writes no partials, so its time is
 // the floor of the attention's copy path at that shape; the attention's time
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kPWaves * kWave) void stream_probe_kernel(DecodePar
     for (int i = 0; i < kPMaxDma; ++i) {
       if (i == kPMaxDma - 1 && n_dma != kPMaxDma) break;
       const int slot = first + c_row[i] < n_tok ? pad + j0 + first + c_row[i] : p.width - 1;
-      dma16_off(lat_base, static_cast<uint32_t>(slot) * lat_st + c_off[i], dst + (wave + kPWaves * i) * 1024);
+      dma16_off_nt(lat_base, static_cast<uint32_t>(slot) * lat_st + c_off[i], dst + (wave + kPWaves * i) * 1024);
     }
   };
   issue(0, 0);
