@@ -225,6 +225,7 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(GemmNT p) {
 // stages.
 constexpr int kBT = 256;
 constexpr int kBK = 64;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // operand of the non-temporal store builtin
 constexpr int kBRowBytes = kBK * 2;                 // 128
 constexpr int kBHalfBytes = kBT * kBRowBytes;       // 32 KB: one operand's slice of a step
 constexpr int kBSlots = 5;
@@ -315,7 +316,18 @@ __device__ __forceinline__ void store_tile_staged(const GemmNT& p, const f32x4 (
         const uint4 v = *reinterpret_cast<const uint4*>(g_gemm256 + r * kRowB + ch * 16);
         char* crow = static_cast<char*>(p.c) + (static_cast<int64_t>(m) * p.ldc + n) * kEs;
         if (al16 && n + 16 / kEs <= p.n) {
-          *reinterpret_cast<uint4*>(crow) = v;
+          if constexpr (ROPE) {
+            // q rows are read once, by the attention: stored non-temporally
+            // they leave the last-level cache to the operands still being
+            // re-read (4096-token prefill: q_b 165 -> 161.5, kv_b 102.9 ->
+            // 101.3, flash 387.5 -> 382.1 us; on kv_b's own output the hint
+            // cost 10 us)
+            u32x4 nv;
+            nv.x = v.x; nv.y = v.y; nv.z = v.z; nv.w = v.w;
+            __builtin_nontemporal_store(nv, reinterpret_cast<u32x4*>(crow));
+          } else {
+            *reinterpret_cast<uint4*>(crow) = v;
+          }
         } else {   // 8-byte pieces (the row is 8-byte aligned; n + 4 elements of bf16 or 2 of fp32 may end it)
           *reinterpret_cast<uint2*>(crow) = make_uint2(v.x, v.y);
           if (n + 8 / kEs < p.n) *reinterpret_cast<uint2*>(crow + 8) = make_uint2(v.z, v.w);
